@@ -1,0 +1,316 @@
+// C ABI of libqmoe (include/qmoe.h): argument checks, workspace layout and
+// kernel launches.  Every check happens before anything is enqueued; a
+// failing call returns its MOE_ERR_* code with a message and touches no
+// output.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/qmoe.h"
+#include "k_decode.h"
+#include "k_misc.h"
+#include "k_prefill.h"
+#include "k_route.h"
+#include "qmoe_internal.h"
+
+using namespace qmoe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_fail(const char* where, hipError_t e) {
+  return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+int n_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+// Shape and pointer checks of a weight set; on success fills the derived
+// sizes.
+struct Geometry {
+  int E, H, I, Is, I_pad, Is_pad;
+  int fmt_ug, fmt_dn;
+  size_t up_bytes, down_bytes;
+};
+
+int check_weights(const moe_weights* w, Geometry* g, const char* fn) {
+  const std::string f(fn);
+  if (!w) return fail(MOE_ERR_INVALID_ARG, f + ": weights is NULL");
+  if (w->n_experts < 1 || w->n_experts > 1024)
+    return fail(MOE_ERR_INVALID_ARG, f + ": n_experts must be in [1, 1024]");
+  if (w->hidden < 256 || w->hidden % 256 != 0 || w->hidden > 8192)
+    return fail(MOE_ERR_INVALID_ARG, f + ": hidden must be a multiple of 256 in [256, 8192]");
+  if (w->inter < 16 || w->inter % 16 != 0 || w->inter > 16384)
+    return fail(MOE_ERR_INVALID_ARG, f + ": inter must be a multiple of 16 in [16, 16384]");
+  if (w->shared_inter < 0 || w->shared_inter % 16 != 0 || w->shared_inter > 16384)
+    return fail(MOE_ERR_INVALID_ARG, f + ": shared_inter must be 0 or a multiple of 16 (<= 16384)");
+  const bool cb2 = w->fmt_up == MOE_FMT_CB2 && w->fmt_gate == MOE_FMT_CB2 && w->fmt_down == MOE_FMT_K2;
+  const bool k4 = w->fmt_up == MOE_FMT_K4 && w->fmt_gate == MOE_FMT_K4 && w->fmt_down == MOE_FMT_K4;
+  if (!cb2 && !k4)
+    return fail(MOE_ERR_UNSUPPORTED, f + ": formats must be (CB2, CB2, K2) or (K4, K4, K4)");
+  if (!w->up || !w->gate || !w->down) return fail(MOE_ERR_INVALID_ARG, f + ": expert weight pointer is NULL");
+  if (!aligned16(w->up) || !aligned16(w->gate) || !aligned16(w->down))
+    return fail(MOE_ERR_INVALID_ARG, f + ": expert weights must be 16-byte aligned");
+  if (cb2 && !w->codebook) return fail(MOE_ERR_INVALID_ARG, f + ": CB2 weights need the codebook");
+  if (w->shared_inter > 0) {
+    if (!w->shared_up || !w->shared_gate || !w->shared_down)
+      return fail(MOE_ERR_INVALID_ARG, f + ": shared expert pointer is NULL");
+    if (!aligned16(w->shared_up) || !aligned16(w->shared_gate) || !aligned16(w->shared_down))
+      return fail(MOE_ERR_INVALID_ARG, f + ": shared expert weights must be 16-byte aligned");
+  }
+  g->E = w->n_experts;
+  g->H = w->hidden;
+  g->I = w->inter;
+  g->Is = w->shared_inter;
+  g->I_pad = (int)pad256(w->inter);
+  g->Is_pad = (int)pad256(w->shared_inter > 0 ? w->shared_inter : 1);
+  g->fmt_ug = w->fmt_up;
+  g->fmt_dn = w->fmt_down;
+  g->up_bytes = moe_packed_bytes(w->fmt_up, w->inter, w->hidden);
+  g->down_bytes = moe_packed_bytes(w->fmt_down, w->hidden, w->inter);
+  return MOE_OK;
+}
+
+struct DecLayout {
+  size_t h, hs, hsum, ybuf, ysh, err, total;
+};
+
+DecLayout dec_layout(const Geometry& g, int T, int k) {
+  DecLayout L;
+  size_t off = 0;
+  L.h = off;
+  off = align_up(off + (size_t)T * k * g.I * 2);
+  L.hs = off;
+  off = align_up(off + (size_t)T * (g.Is > 0 ? g.Is : 1) * 2);
+  L.hsum = off;
+  off = align_up(off + (size_t)T * k * (g.I_pad / 16) * 2 * 4);
+  L.ybuf = off;
+  off = align_up(off + (size_t)T * k * g.H * 4);
+  L.ysh = off;
+  off = align_up(off + (size_t)T * g.H * 4);
+  L.err = off;
+  off = align_up(off + 4);
+  L.total = off;
+  return L;
+}
+
+struct PfLayout {
+  size_t h, hs, yslot, ysh, total;
+};
+
+PfLayout pf_layout(const Geometry& g, int64_t T, int k) {
+  PfLayout L;
+  size_t off = 0;
+  L.h = off;
+  off = align_up(off + (size_t)T * k * g.I * 2);
+  L.hs = off;
+  off = align_up(off + (size_t)T * (g.Is > 0 ? g.Is : 1) * 2);
+  L.yslot = off;
+  off = align_up(off + (size_t)T * k * g.H * 4);
+  L.ysh = off;
+  off = align_up(off + (size_t)T * g.H * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+
+extern "C" size_t moe_route_workspace_bytes(int32_t T, int32_t E) {
+  if (T < 1 || E < 1) return 0;
+  return align_up((size_t)T * E * 4);
+}
+
+extern "C" int moe_route(const void* x_bf16, const float* w_router, const float* logit_bias, int32_t T,
+                         int32_t H, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w, void* ws,
+                         size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!x_bf16 || !w_router || !topk_idx || !topk_w || !ws)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: NULL pointer");
+  if (T < 1 || H < 8 || H % 8 != 0 || E < 1 || E > 1024)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: need T >= 1, H a positive multiple of 8, 1 <= E <= 1024");
+  if (k < 1 || k > E || k > 16) return fail(MOE_ERR_INVALID_ARG, "moe_route: need 1 <= k <= min(E, 16)");
+  if (!aligned16(x_bf16) || !aligned16(w_router))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: x and w_router must be 16-byte aligned");
+  if (ws_bytes < moe_route_workspace_bytes(T, E))
+    return fail(MOE_ERR_WORKSPACE, "moe_route: workspace too small");
+  hipError_t e = launch_route((const uint16_t*)x_bf16, w_router, logit_bias, T, H, E, k, (float*)ws, topk_idx,
+                              topk_w, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("moe_route", e);
+  return MOE_OK;
+}
+
+extern "C" size_t moe_group_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  if (T < 1 || k < 1 || E < 1) return 0;
+  return kAlign;
+}
+
+extern "C" int moe_group_tokens(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_pos, void* ws,
+                                size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!topk_idx || !expert_offsets || !sorted_slots || !slot_pos || !ws)
+    return fail(MOE_ERR_INVALID_ARG, "moe_group_tokens: NULL pointer");
+  if (T < 1 || k < 1 || k > 16 || E < 1 || E > 1024 || (int64_t)T * k > (1 << 22))
+    return fail(MOE_ERR_INVALID_ARG, "moe_group_tokens: need T >= 1, 1 <= k <= 16, 1 <= E <= 1024, T*k <= 2^22");
+  if (ws_bytes < moe_group_workspace_bytes(T, k, E))
+    return fail(MOE_ERR_WORKSPACE, "moe_group_tokens: workspace too small");
+  hipError_t e = launch_group(topk_idx, T * k, E, expert_offsets, sorted_slots, slot_pos, (int*)ws,
+                              (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("moe_group_tokens", e);
+  return MOE_OK;
+}
+
+extern "C" size_t moe_ffn_workspace_bytes(const moe_weights* w, int32_t T, int32_t k, int prefill) {
+  Geometry g;
+  if (check_weights(w, &g, "moe_ffn_workspace_bytes") != MOE_OK) return 0;
+  if (T < 1 || k < 1 || k > 16) return 0;
+  if (!prefill) {
+    if (T > 16) return 0;
+    return dec_layout(g, T, k).total;
+  }
+  return pf_layout(g, T, k).total;
+}
+
+extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
+                                     const int32_t* topk_idx, const float* topk_w, float* y, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  clear_error();
+  Geometry g;
+  int rc = check_weights(w, &g, "moe_expert_ffn_decode");
+  if (rc != MOE_OK) return rc;
+  if (!x_bf16 || !topk_idx || !topk_w || !y || !ws)
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: NULL pointer");
+  if (T < 1 || T > 16) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: T must be in [1, 16]");
+  if (k < 1 || k > 16 || k > g.E) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: need 1 <= k <= min(E, 16)");
+  if (!aligned16(x_bf16) || !aligned16(ws))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: x and ws must be 16-byte aligned");
+  const DecLayout L = dec_layout(g, T, k);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn_decode: workspace too small (need " + std::to_string(L.total) + ")");
+  uint8_t* wsb = (uint8_t*)ws;
+  DecArgs a{};
+  a.x = (const uint16_t*)x_bf16;
+  a.T = T;
+  a.H = g.H;
+  a.I = g.I;
+  a.Is = g.Is;
+  a.I_pad = g.I_pad;
+  a.Is_pad = g.Is_pad;
+  a.k = k;
+  a.E = g.E;
+  const int n_chunks = g.H / 256;
+  const int cpw = n_chunks > 16 ? 2 : 1;
+  a.nw_ug = (n_chunks + cpw - 1) / cpw;
+  if (a.nw_ug < 4) a.nw_ug = 4;
+  int nd = g.I_pad / 256;
+  a.nw_dn = nd < 4 ? 4 : (nd > 16 ? 16 : nd);
+  a.tb_ug = tile_bytes(g.fmt_ug);
+  a.tb_dn = tile_bytes(g.fmt_dn);
+  a.topk_idx = topk_idx;
+  a.up = (const uint8_t*)w->up;
+  a.gate = (const uint8_t*)w->gate;
+  a.down = (const uint8_t*)w->down;
+  a.expert_bytes = g.up_bytes;
+  a.expert_bytes_down = g.down_bytes;
+  a.sup = (const uint8_t*)w->shared_up;
+  a.sgate = (const uint8_t*)w->shared_gate;
+  a.sdown = (const uint8_t*)w->shared_down;
+  a.codebook = w->codebook;
+  a.h = (_Float16*)(wsb + L.h);
+  a.hs = (_Float16*)(wsb + L.hs);
+  a.hsum = (float*)(wsb + L.hsum);
+  a.ybuf = (float*)(wsb + L.ybuf);
+  a.ysh = (float*)(wsb + L.ysh);
+  a.err_count = (int*)(wsb + L.err);
+  const int cus = n_cus();
+  const int64_t nd_max = (int64_t)(T * k < g.E ? T * k : g.E);
+  const int64_t items_ug = nd_max * (g.I / 16) + g.Is / 16;
+  const int64_t items_dn = nd_max * (g.H / 16) + (g.Is > 0 ? g.H / 16 : 0);
+  const int grid_ug = (int)(items_ug < cus ? items_ug : cus);
+  const int grid_dn = (int)(items_dn < 2 * cus ? items_dn : 2 * cus);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_dec_upgate(a, g.fmt_ug, cpw, grid_ug, s);
+  if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode (up/gate)", e);
+  e = launch_dec_down(a, g.fmt_dn, grid_dn, s);
+  if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode (down)", e);
+  e = launch_combine(a, topk_idx, topk_w, y, s);
+  if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode (combine)", e);
+  return MOE_OK;
+}
+
+extern "C" int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
+                                      const int32_t* topk_idx, const float* topk_w,
+                                      const int32_t* expert_offsets, const int32_t* sorted_slots,
+                                      const int32_t* slot_pos, float* y, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  clear_error();
+  Geometry g;
+  int rc = check_weights(w, &g, "moe_expert_ffn_prefill");
+  if (rc != MOE_OK) return rc;
+  if (!x_bf16 || !topk_idx || !topk_w || !expert_offsets || !sorted_slots || !slot_pos || !y || !ws)
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_prefill: NULL pointer");
+  if (T < 1 || (int64_t)T * 16 > (1ll << 26))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_prefill: T must be in [1, 2^22]");
+  if (k < 1 || k > 16 || k > g.E) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_prefill: need 1 <= k <= min(E, 16)");
+  if (!aligned16(x_bf16) || !aligned16(ws))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_prefill: x and ws must be 16-byte aligned");
+  const PfLayout L = pf_layout(g, T, k);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn_prefill: workspace too small (need " + std::to_string(L.total) + ")");
+  uint8_t* wsb = (uint8_t*)ws;
+  PfArgs a{};
+  a.x = (const uint16_t*)x_bf16;
+  a.T = T;
+  a.H = g.H;
+  a.I = g.I;
+  a.Is = g.Is;
+  a.I_pad = g.I_pad;
+  a.Is_pad = g.Is_pad;
+  a.k = k;
+  a.E = g.E;
+  a.offsets = expert_offsets;
+  a.sorted_slots = sorted_slots;
+  a.slot_pos = slot_pos;
+  a.up = (const uint8_t*)w->up;
+  a.gate = (const uint8_t*)w->gate;
+  a.down = (const uint8_t*)w->down;
+  a.expert_bytes = g.up_bytes;
+  a.expert_bytes_down = g.down_bytes;
+  a.sup = (const uint8_t*)w->shared_up;
+  a.sgate = (const uint8_t*)w->shared_gate;
+  a.sdown = (const uint8_t*)w->shared_down;
+  a.codebook = w->codebook;
+  a.h = (_Float16*)(wsb + L.h);
+  a.hs = (_Float16*)(wsb + L.hs);
+  a.yslot = (float*)(wsb + L.yslot);
+  a.ysh = (float*)(wsb + L.ysh);
+  hipError_t e = launch_prefill(a, g.fmt_ug, g.fmt_dn, topk_w, y, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("moe_expert_ffn_prefill", e);
+  return MOE_OK;
+}
+
+extern "C" int moe_debug_dequant(int fmt, const void* packed, int64_t rows, int64_t k, const int8_t* codebook,
+                                 float* out, void* stream) {
+  clear_error();
+  if (moe_packed_bytes(fmt, rows, k) == 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_debug_dequant: bad format or shape");
+  if (!packed || !out) return fail(MOE_ERR_INVALID_ARG, "moe_debug_dequant: NULL pointer");
+  if (fmt == MOE_FMT_CB2 && !codebook) return fail(MOE_ERR_INVALID_ARG, "moe_debug_dequant: CB2 needs the codebook");
+  if (!aligned16(packed)) return fail(MOE_ERR_INVALID_ARG, "moe_debug_dequant: packed must be 16-byte aligned");
+  hipError_t e = launch_dequant(fmt, (const uint8_t*)packed, rows, pad256(k), codebook, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("moe_debug_dequant", e);
+  return MOE_OK;
+}

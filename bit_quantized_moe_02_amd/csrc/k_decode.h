@@ -1,0 +1,41 @@
+// Launch interface of the decode-shape expert FFN kernels (k_decode.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+struct DecArgs {
+  const uint16_t* x;          // bf16 [T][H]
+  int T, H, I, Is, I_pad, Is_pad, k, E;
+  int nw_ug, nw_dn;           // waves per workgroup of the two kernels
+  int tb_ug, tb_dn;           // tile bytes of the routed up/gate and down formats
+  const int32_t* topk_idx;    // [T][k]
+  const uint8_t* up;          // routed experts, packed, expert-major
+  const uint8_t* gate;
+  const uint8_t* down;
+  size_t expert_bytes;        // bytes of one packed up (= gate) matrix
+  size_t expert_bytes_down;   // bytes of one packed down matrix
+  const uint8_t* sup;         // shared expert, BF16 tiles (or null)
+  const uint8_t* sgate;
+  const uint8_t* sdown;
+  const int8_t* codebook;     // CB2 table (device)
+  // workspace
+  _Float16* h;                // [T*k][I]   fp16, slot order
+  _Float16* hs;               // [T][Is]    fp16
+  float* hsum;                // [T*k][I_pad/16][2]  (sum h, offset sum) per 16 rows
+  float* ybuf;                // [T*k][H]   fp32 per-slot down outputs
+  float* ysh;                 // [T][H]     fp32 shared-expert output
+  int* err_count;             // invalid expert ids seen
+};
+
+size_t dec_upgate_lds(const DecArgs& a, int fmt);
+size_t dec_down_lds(const DecArgs& a);
+hipError_t launch_dec_upgate(const DecArgs& a, int fmt, int cpw, int grid, hipStream_t s);
+hipError_t launch_dec_down(const DecArgs& a, int fmt, int grid, hipStream_t s);
+hipError_t launch_combine(const DecArgs& a, const int32_t* topk_idx, const float* topk_w, float* y,
+                          hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,201 @@
+// Test decoder of packed matrices and the stable expert grouping of slots.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qmoe.h"
+#include "device_common.hpp"
+#include "k_misc.h"
+
+using namespace qmoe_dev;
+
+namespace {
+
+// Decodes packed tiles to fp32 with the FFN kernels' lane decoders: each
+// wave takes one tile at a time; lane c writes weights (n, kb, qq, j) of its
+// slice.  Every value is the exact format value rounded once to fp32:
+//   CB2: s * (T/4, sign flipped), exact;  K2/K4: fma(-dmin, m, d*sc*q), where
+//   d*sc*q is exact in fp32 and the fma rounds once;  BF16: the value itself.
+template <int FMT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* packed, int64_t n_rt, int64_t n_kc,
+                                                      const int8_t* codebook, float* out) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* val_tab = smem;
+  uint8_t* flip_tab = smem + kCb2TableBytes;
+  if (FMT == MOE_FMT_CB2) {
+    cb2_fill_tables(codebook, val_tab, flip_tab, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, qq = lane >> 4;
+  const int64_t kp = n_kc * 256;
+  const int64_t n_tiles = n_rt * n_kc;
+  const int waves = (blockDim.x >> 6) * gridDim.x;
+  for (int64_t tile_i = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); tile_i < n_tiles;
+       tile_i += waves) {
+    const int64_t rt = tile_i / n_kc, kc = tile_i % n_kc;
+    float* orow = out + (rt * 16 + n) * kp + kc * 256 + qq * 8;
+    if (FMT == MOE_FMT_CB2) {
+      const uint8_t* tile = packed + tile_i * kCb2Tile;
+      const u32x4 codes = load16(tile + 16 * lane);
+      const u32x4 scl = load16(tile + 1024 + 16 * n);
+      for (int kb = 0; kb < 8; ++kb) {
+        const half8 v = cb2_group((codes[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu, val_tab + (lane & 7) * 16,
+                                  flip_tab + (lane & 7) * 16);
+        const float s = h2f((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu);
+        for (int j = 0; j < 8; ++j) orow[kb * 32 + j] = s * (float)v[j];
+      }
+    } else if (FMT == MOE_FMT_K2) {
+      const uint8_t* tile = packed + tile_i * kK2Tile;
+      const u32x4 qw = load16(tile + 16 * lane);
+      const u32x4 scm = load16(tile + 1024 + 16 * n);
+      const uint32_t dd = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
+      const float d = h2f(dd & 0xFFFFu), dmin = h2f(dd >> 16);
+      for (int kb = 0; kb < 8; ++kb) {
+        const half8 v = as_half8(k2_magic(qw, kb));
+        const int sb = 2 * kb + (qq >> 1);
+        const uint32_t byte = (scm[sb >> 2] >> (8 * (sb & 3))) & 0xFFu;
+        const float dsc = d * (float)(byte & 15u), mn = (float)(byte >> 4);
+        for (int j = 0; j < 8; ++j) {
+          const float q = ((float)v[j] - 1024.0f) * __builtin_ldexpf(1.0f, -2 * k2_slot_t(kb, j >> 1));
+          orow[kb * 32 + j] = fmaf(-dmin, mn, dsc * q);
+        }
+      }
+    } else if (FMT == MOE_FMT_K4) {
+      const uint8_t* tile = packed + tile_i * kK4Tile;
+      const u32x4 q0 = load16(tile + 16 * lane);
+      const u32x4 q1 = load16(tile + 1024 + 16 * lane);
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(tile + 2048 + 12 * n);
+      const uint32_t s0 = sp[0], s1 = sp[1], s2 = sp[2];
+      const uint32_t dd = *reinterpret_cast<const uint32_t*>(tile + 2240 + 4 * n);
+      const float d = h2f(dd & 0xFFFFu), dmin = h2f(dd >> 16);
+      for (int kb = 0; kb < 8; ++kb) {
+        const half8 v = as_half8(k4_magic(kb < 4 ? q0[kb & 3] : q1[kb & 3]));
+        const float dsc = d * (float)k4_scale_value(s0, s1, s2, kb);
+        const float mn = (float)k4_scale_value(s0, s1, s2, 8 + kb);
+        for (int j = 0; j < 8; ++j) orow[kb * 32 + j] = fmaf(-dmin, mn, dsc * ((float)v[j] - 1024.0f));
+      }
+    } else {
+      const uint8_t* tile = packed + tile_i * kBf16Tile;
+      for (int kb = 0; kb < 8; ++kb) {
+        const u32x4 raw = load16(tile + 1024 * kb + 16 * lane);
+        for (int j = 0; j < 8; ++j) orow[kb * 32 + j] = bf2f((raw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      }
+    }
+  }
+}
+
+// Stable counting sort of the slots by expert, one workgroup of 16 waves.
+// Wave w owns the contiguous slot range [w*S, (w+1)*S): it counts its
+// experts, the counts are scanned (expert-major, then wave order), and each
+// wave writes its slots in slot order, ranking equal experts inside every
+// 64-slot chunk with a lane-order count.
+constexpr int kGroupWaves = 16;
+
+__global__ __launch_bounds__(1024) void group_kernel(const int32_t* topk_idx, int n_slots, int E,
+                                                     int32_t* offsets, int32_t* sorted_slots,
+                                                     int32_t* slot_pos, int* err_count) {
+  extern __shared__ __align__(16) int gsm[];
+  int* cnt = gsm;                          // [16][E]: counts, then running cursors
+  int* tot = gsm + kGroupWaves * E;        // [E + 1]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kGroupWaves * E; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int S = (n_slots + kGroupWaves - 1) / kGroupWaves;
+  const int s0 = wave * S, s1 = min(n_slots, s0 + S);
+  int bad = 0;
+  for (int s = s0 + lane; s < s1; s += 64) {
+    const int e = topk_idx[s];
+    if (e >= 0 && e < E) atomicAdd(&cnt[wave * E + e], 1);
+    else ++bad;
+  }
+  __syncthreads();
+  // per expert: cursors = exclusive prefix over waves, totals
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < kGroupWaves; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan of the totals, in expert order
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = tot[e];
+      tot[e] = run;
+      offsets[e] = run;
+      run += c;
+    }
+    tot[E] = run;
+    offsets[E] = run;
+  }
+  __syncthreads();
+  for (int c0 = s0; c0 < s1; c0 += 64) {
+    const int s = c0 + lane;
+    const int e = (s < s1) ? topk_idx[s] : -1;
+    const bool valid = e >= 0 && e < E;
+    int rank = 0, same = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __shfl(e, j);
+      if (ej == e) {
+        if (j < lane) ++rank;
+        ++same;
+      }
+    }
+    int cursor = 0;
+    if (valid) cursor = cnt[wave * E + e];
+    if (valid) {
+      const int pos = tot[e] + cursor + rank;
+      sorted_slots[pos] = s;
+      slot_pos[s] = pos;
+    } else if (s < s1) {
+      slot_pos[s] = -1;
+    }
+    // the last lane of each expert in this chunk advances the cursor
+    if (valid && rank == same - 1) cnt[wave * E + e] = cursor + same;
+  }
+  for (int o = 1; o < 64; o <<= 1) bad += __shfl_xor(bad, o);
+  if (lane == 0 && bad) atomicAdd(err_count, bad);
+}
+
+}  // namespace
+
+namespace qmoe {
+
+hipError_t launch_dequant(int fmt, const uint8_t* packed, int64_t rows, int64_t kp, const int8_t* codebook,
+                          float* out, hipStream_t s) {
+  const int64_t n_rt = rows / 16, n_kc = kp / 256;
+  const int64_t n_tiles = n_rt * n_kc;
+  const int grid = (int)((n_tiles + 3) / 4 < 1024 ? (n_tiles + 3) / 4 : 1024);
+  const size_t lds = (fmt == MOE_FMT_CB2) ? 2 * kCb2TableBytes : 0;
+  void (*fn)(const uint8_t*, int64_t, int64_t, const int8_t*, float*) = nullptr;
+  switch (fmt) {
+    case MOE_FMT_CB2: fn = dequant_kernel<MOE_FMT_CB2>; break;
+    case MOE_FMT_K2: fn = dequant_kernel<MOE_FMT_K2>; break;
+    case MOE_FMT_K4: fn = dequant_kernel<MOE_FMT_K4>; break;
+    default: fn = dequant_kernel<MOE_FMT_BF16>; break;
+  }
+  if (lds > 0) {
+    hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, s, packed, n_rt, n_kc, codebook, out);
+  return hipGetLastError();
+}
+
+size_t group_lds(int E) { return (size_t)(kGroupWaves * E + E + 1) * 4; }
+
+hipError_t launch_group(const int32_t* topk_idx, int n_slots, int E, int32_t* offsets, int32_t* sorted_slots,
+                        int32_t* slot_pos, int* err_count, hipStream_t s) {
+  const size_t lds = group_lds(E);
+  hipError_t err = hipFuncSetAttribute((const void*)group_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(64 * kGroupWaves), lds, s, topk_idx, n_slots, E, offsets,
+                     sorted_slots, slot_pos, err_count);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

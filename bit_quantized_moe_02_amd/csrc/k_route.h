@@ -1,0 +1,13 @@
+// Launch interface of the router kernels (k_route.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// logits: workspace fp32 [T][E].
+hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
+                        int k, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s);
+
+}  // namespace qmoe

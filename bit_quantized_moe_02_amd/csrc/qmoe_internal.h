@@ -1,0 +1,25 @@
+// Internal declarations shared by the host and device translation units of
+// libqmoe.  Not part of the public ABI (include/qmoe.h).
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+
+namespace qmoe {
+
+// Records the message moe_last_error() returns on this thread and passes
+// `code` through, so call sites can write `return fail(MOE_ERR_..., "...")`.
+int fail(int code, const std::string& msg);
+void clear_error();
+
+// Tile geometry (see include/qmoe.h): 16 rows x 256 columns per tile.
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 256;
+
+inline int64_t pad256(int64_t k) { return (k + 255) / 256 * 256; }
+
+// Bytes of one tile of each format; 0 for an unknown format.
+int tile_bytes(int fmt);
+
+}  // namespace qmoe

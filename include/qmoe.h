@@ -1,0 +1,242 @@
+/*
+ * qmoe.h -- C ABI of the quantized routed-MoE layer for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What the layer computes comes from the ds4 pages:
+ *   [digest]  "antirez/ds4 - Metal向け DeepSeek V4 Flash ローカル推論エンジン"
+ *             (ja.news.hada.io/topic?id=29299), sections "Model weights"
+ *             (only the routed MoE experts are quantized: up/gate in a 2-bit
+ *             codebook format, down in a 2-bit K-quant format; shared expert
+ *             and routing stay unquantized) and the overview (few active
+ *             parameters -- sparse top-k experts -- is what makes it fast).
+ *   [upppp]   "ds4 ..." article (upppp.jp/open-source/20260512-142644),
+ *             section "asymmetric 2-bit quantization" (experts take most of
+ *             the bytes; shared expert / projections kept at higher precision).
+ *   [osrepos] "ds4: A Fast Local Inference Engine ..." (osrepos.com), the
+ *             "Q4KExperts" model file name (a 4-bit K-quant expert variant).
+ *   [blog]    Korean user blog (modu-print.com), server log excerpts
+ *             (prompts are prefilled in chunks of 2048 tokens, cap 8192).
+ *
+ * The pages name the formats but do not define their bytes.  This header is
+ * the format definition; the CB2/K2/K4/BF16 paragraphs below are normative.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every call
+ *   Ownership: the caller owns every buffer.  The library never allocates or
+ *     frees device memory and keeps no pointer after a call returns.
+ *   Pointers: "device" pointers are HIP device memory on the current device;
+ *     "host" pointers are ordinary process memory.  Device base pointers must
+ *     be 16-byte aligned.
+ *   Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Device calls enqueue kernels and return without waiting.
+ *   Errors: arguments are checked on the host before anything is enqueued.
+ *     On failure a call returns a nonzero MOE_ERR_* code, leaves its outputs
+ *     untouched and sets a thread-local message readable with
+ *     moe_last_error().  A failed kernel launch returns MOE_ERR_HIP.  No call
+ *     aborts, exits or lets a C++ exception escape.
+ *   Determinism: every result is a fixed-order computation (no atomics in
+ *     any floating-point sum), so repeated calls give identical bits.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1
+#define MOE_ERR_UNSUPPORTED 2
+#define MOE_ERR_WORKSPACE 3
+#define MOE_ERR_HIP 4
+
+/* Weight formats.
+ *
+ * Every weight matrix W [rows, k] (rows = output features, k = reduction
+ * dimension, row-major) is stored as tiles of 16 rows x 256 columns.  k is
+ * zero-padded up to kp = 256 * ceil(k / 256); rows must be a multiple of 16.
+ * Tiles are stored row-tile major: tile (rt, kc) starts at byte
+ * (rt * kp/256 + kc) * TILE, rt = row / 16, kc = col / 256.
+ * Inside a tile, row n = row % 16 and column kk = col % 256 split as
+ *   kb = kk / 32, qq = (kk % 32) / 8, j = kk % 8, and lane c = 16*qq + n.
+ * Lane c owns weights (n, kb, qq, j = 0..7) for kb = 0..7: exactly the 8
+ * values one lane of a 64-wide wavefront feeds to a 16x16x32 MFMA as its B
+ * operand for k-block kb.  All multi-byte fields are little-endian.
+ *
+ * MOE_FMT_CB2 (2-bit codebook, 2.5 bits/weight; [digest] "Model weights",
+ *   up/gate).  A group is 8 consecutive weights (n, kb, qq, j=0..7).  It holds
+ *   an 8-bit index into a 256 x 8 table T of values in {-3,-1,1,3} (units of
+ *   1/4, see moe_codebook_generate) and 8 flip bits; every 32 weights (n, kb)
+ *   share one fp16 scale s.  Weight j = s * T[idx][j] / 4, negated when flip
+ *   bit j is set.  Tile (1280 bytes):
+ *     [0, 1024)    lane c at 16*c: 8 uint16 codes, code for kb at byte 2*kb,
+ *                  code = idx | flip << 8 (flip bit j = bit 8+j).
+ *     [1024, 1280) row n at 1024 + 16*n: 8 fp16 scales, kb at byte 2*kb.
+ *
+ * MOE_FMT_K2 (2-bit K-quant, 2.625 bits/weight; [digest] "Model weights",
+ *   down).  Each row's 256 columns of a tile form one super-block of 16
+ *   sub-blocks of 16 (sub-block sb = kk / 16 = 2*kb + qq/2), with 2-bit codes
+ *   q, 4-bit sc and m per sub-block and fp16 d, dmin per super-block:
+ *   weight = d*sc*q - dmin*m.  Tile (1344 bytes):
+ *     [0, 1024)    lane c at 16*c: 4 uint32 words; word i holds kb = 2i and
+ *                  2i+1: the code of (kb, j) sits at bit 2*(4*(kb%2) + j/2)
+ *                  + 16*(j%2).
+ *     [1024, 1280) row n at 1024 + 16*n: byte sb = sc | m << 4.
+ *     [1280, 1344) row n at 1280 + 4*n: fp16 d, fp16 dmin.
+ *
+ * MOE_FMT_K4 (4-bit K-quant, 4.5 bits/weight; [osrepos] "Q4KExperts").  One
+ *   super-block per row per tile of 8 sub-blocks of 32 (sub-block = kb), 4-bit
+ *   q, 6-bit sc and m, fp16 d, dmin: weight = d*sc*q - dmin*m.  Tile (2304):
+ *     [0, 2048)    for half h = kb / 4: lane c at 1024*h + 16*c: 4 uint32
+ *                  words, word kb%4 holds the 8 codes of kb: code of j at bit
+ *                  4*(j/2) + 16*(j%2).
+ *     [2048, 2240) row n at 2048 + 12*n: 96-bit little-endian bit stream of
+ *                  16 six-bit values sc0..sc7, m0..m7 (value i at bit 6*i).
+ *     [2240, 2304) row n at 2240 + 4*n: fp16 d, fp16 dmin.
+ *
+ * MOE_FMT_BF16 (unquantized shared expert).  Tile (8192 bytes): element
+ *   (n, kb, qq, j) at byte 1024*kb + 16*c + 2*j (c = 16*qq + n), bf16.
+ */
+#define MOE_FMT_BF16 0
+#define MOE_FMT_CB2 1
+#define MOE_FMT_K2 2
+#define MOE_FMT_K4 3
+
+/* ---------------------------------------------------------------------------
+ * Host-only calls (no GPU needed).
+ */
+
+/* Fills table_out[256*8] (entry-major) with the CB2 codebook: SplitMix64
+ * (Steele, Lea, Flood, OOPSLA 2014) started from `seed`; draw i sets entry
+ * i/8, value i%8 to {-3,-1,1,3}[draw >> 62].  Returns MOE_OK, or
+ * MOE_ERR_INVALID_ARG if table_out is NULL. */
+int moe_codebook_generate(uint64_t seed, int8_t* table_out);
+
+/* Bytes of a packed matrix [rows, k] in format fmt (k padded to 256).
+ * Returns 0 when rows is not a positive multiple of 16, k < 1 or fmt is
+ * unknown. */
+size_t moe_packed_bytes(int fmt, int64_t rows, int64_t k);
+
+/* Quantizes and packs a host fp32 matrix w [rows, k] (row-major) into
+ * out (host, out_bytes >= moe_packed_bytes(fmt, rows, k)).  Columns beyond k
+ * up to the next multiple of 256 are taken as zero.
+ *   CB2: per 32 weights s = fp16(max|w| / 0.75) (fp64 quotient, one rounding
+ *        to fp16); per group the lowest index e minimizing
+ *        sum_{j=0..7} (|w_j| - s*|T[e][j]|/4)^2 (fp64, j ascending); flip bit j
+ *        = (w_j < 0) != (T[e][j] < 0).  `codebook` = the 256x8 table (host).
+ *   K2/K4: per sub-block lo = min(0, min w), hi = max w, a = (hi-lo)/Q,
+ *        b = 0-lo; d = fp16(max a / S), dmin = fp16(max b / S);
+ *        sc = min(S, floor(a/d + 1/2)), m = min(S, floor(b/dmin + 1/2))
+ *        (0 when d or dmin is 0); q = clamp(floor((w + dmin*m)/(d*sc) + 1/2),
+ *        0, Q) (0 when d*sc is 0).  K2: Q=3, S=15; K4: Q=15, S=63.
+ *   BF16: each value rounded to bf16 (nearest, ties to even).
+ * n_threads <= 0 uses all hardware threads.  Errors: MOE_ERR_INVALID_ARG for
+ * NULL pointers, bad shapes, non-finite weights, |w| too large for an fp16
+ * scale, a missing codebook (CB2) or out_bytes too small. */
+int moe_quantize_pack(int fmt, const float* w, int64_t rows, int64_t k,
+                      const int8_t* codebook, void* out, size_t out_bytes,
+                      int n_threads);
+
+/* ---------------------------------------------------------------------------
+ * Device calls.
+ */
+
+/* One MoE layer's weights (all pointers device, 16-byte aligned).
+ *   up, gate: n_experts packed matrices [inter, hidden] back to back, each
+ *             moe_packed_bytes(fmt_up, inter, hidden) bytes.
+ *   down:     n_experts packed matrices [hidden, inter].
+ *   shared_*: MOE_FMT_BF16 packed [shared_inter, hidden] (up, gate) and
+ *             [hidden, shared_inter] (down); NULL when shared_inter == 0.
+ *   codebook: device copy of the 256x8 CB2 table (int8), or NULL if no CB2.
+ * Supported: hidden a multiple of 256; inter and shared_inter multiples of
+ * 16; (fmt_up, fmt_gate, fmt_down) = (CB2, CB2, K2) or (K4, K4, K4). */
+typedef struct moe_weights {
+  int32_t n_experts;
+  int32_t hidden;
+  int32_t inter;
+  int32_t shared_inter;
+  int32_t fmt_up, fmt_gate, fmt_down;
+  int32_t reserved;
+  const void* up;
+  const void* gate;
+  const void* down;
+  const int8_t* codebook;
+  const void* shared_up;
+  const void* shared_gate;
+  const void* shared_down;
+} moe_weights;
+
+/* Workspace bytes moe_route needs for T tokens over E experts. */
+size_t moe_route_workspace_bytes(int32_t T, int32_t E);
+
+/* Router ([digest] "Model weights": routing stays unquantized; the function
+ * is softmax over experts, keep the top k, renormalize over the kept k).
+ *   x_bf16   device bf16 [T, H];  w_router device fp32 [E, H];
+ *   logit_bias device fp32 [E] added to the logits, or NULL.
+ *   topk_idx device int32 [T, k]: experts by descending logit, ties to the
+ *            lower index;  topk_w device fp32 [T, k]: exp(l_j - l_0) /
+ *            sum_i exp(l_i - l_0) over the kept logits.
+ * Logits are fp32 sums.  ws: device, >= moe_route_workspace_bytes(T, E).
+ * Limits: 1 <= k <= min(E, 16), E <= 1024, H a multiple of 8. */
+int moe_route(const void* x_bf16, const float* w_router, const float* logit_bias,
+              int32_t T, int32_t H, int32_t E, int32_t k, int32_t* topk_idx,
+              float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes moe_group_tokens needs. */
+size_t moe_group_workspace_bytes(int32_t T, int32_t k, int32_t E);
+
+/* Stable grouping of the T*k (token, choice) slots by expert (slot = t*k + j)
+ * -- the per-expert token lists that sparse activation works on ([digest]
+ * overview).  Outputs (device int32): expert_offsets [E+1] (exclusive scan of
+ * per-expert counts), sorted_slots [T*k] (slots ordered by expert, slot order
+ * kept within an expert), slot_pos [T*k] (inverse of sorted_slots).  Expert
+ * ids outside [0, E) make the call's kernels count them in the workspace and
+ * drop the slot (its position is left -1). */
+int moe_group_tokens(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                     int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_pos,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of the expert FFN for T tokens with k choices each
+ * (prefill != 0: the grouped prefill path; else decode, T <= 16). */
+size_t moe_ffn_workspace_bytes(const moe_weights* w, int32_t T, int32_t k, int prefill);
+
+/* Expert FFN for 1..16 tokens (decode / draft verification):
+ *   y[t] = sum_j topk_w[t,j] * FFN_{topk_idx[t,j]}(x[t]) + FFN_shared(x[t]),
+ *   FFN(x) = W_down (SiLU(W_gate x) * (W_up x)), summed j = 0..k-1 then the
+ *   shared expert.  x_bf16 device bf16 [T, H]; y device fp32 [T, H]
+ *   (overwritten).  The intermediate h is fp16; weights are decoded exactly;
+ *   sums are fp32.  The first bytes of ws hold h as fp16 [T*k, inter] (slot
+ *   order) after the call.  Limits: 1 <= T <= 16, 1 <= k <= 16. */
+int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
+                          const int32_t* topk_idx, const float* topk_w, float* y,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFN for a prefill chunk (any T >= 1), same result as the decode
+ * call, computed as grouped GEMMs over moe_group_tokens' output (device
+ * int32 arrays as that call writes them).  Dequantized weights and h are
+ * fp16 MFMA operands; sums are fp32.  The first bytes of ws hold h as fp16
+ * [T*k, inter] in grouped (sorted_slots) order after the call. */
+int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const int32_t* expert_offsets, const int32_t* sorted_slots,
+                           const int32_t* slot_pos, float* y, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Decodes a packed matrix on the device into fp32 out [rows, kp] with the
+ * same decode routines the FFN kernels use (kp = k padded to 256).  For
+ * tests: every value is the exact format value rounded once to fp32. */
+int moe_debug_dequant(int fmt, const void* packed, int64_t rows, int64_t k,
+                      const int8_t* codebook, float* out, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

@@ -382,9 +382,8 @@ def pack_matrix(f: dict) -> np.ndarray:
     if fmt == "cb2":
         R, G = f["idx"].shape
         K = G * 8
-        # one 16-bit code per group: flip bits 0-3, index, flip bits 4-7
-        code = (f["flip"].astype(np.uint16) & 0xF) | (f["idx"].astype(np.uint16) << 4) \
-            | ((f["flip"].astype(np.uint16) >> 4) << 12)                         # [R, K/8]
+        # one 16-bit code per group: index in bits 0-7, flip bits in 8-15
+        code = f["idx"].astype(np.uint16) | (f["flip"].astype(np.uint16) << 8)   # [R, K/8]
         per_w = np.repeat(code, 8, axis=1)                                       # [R, K]
         lanes = _lanes(per_w, R, K)[..., 0]                                      # j = 0
         codes = lanes.astype("<u2").view(np.uint8).reshape(R // 16, K // 256, 1024)
@@ -454,8 +453,8 @@ def unpack_matrix(fmt: str, packed: np.ndarray, rows: int, k: int) -> dict:
         codes = t[..., :1024].copy().view("<u2").reshape(R // 16, K // 256, 64, 8)
         per_w = np.repeat(codes[..., None], 8, axis=-1)                  # [.., 64, kb, j]
         code = _unlanes(per_w, R, K)[:, ::8]                             # [R, K/8]
-        idx = ((code >> 4) & 0xFF).astype(np.uint8)
-        flip = ((code & 0xF) | ((code >> 12) << 4)).astype(np.uint8)
+        idx = (code & 0xFF).astype(np.uint8)
+        flip = (code >> 8).astype(np.uint8)
         sc = t[..., 1024:].copy().view("<u2").reshape(R // 16, K // 256, 16, 8)
         sc = np.moveaxis(sc, 1, 2).reshape(R, K // 32)
         return {"fmt": fmt, "idx": idx, "flip": flip, "scale": _f16_from_bits(sc)}

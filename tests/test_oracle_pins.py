@@ -366,7 +366,7 @@ def test_layout_single_weight_positions():
     base = (1 * (K // 256) + 1) * 1280
     code_off = base + lane * 16 + 2 * 1
     code = int(p[code_off]) | (int(p[code_off + 1]) << 8)
-    assert code == (0xAB << 4) | (1 << 12)
+    assert code == 0xAB | (1 << 12)
     assert np.count_nonzero(p) == 2
     # CB2 scale of block (r, k // 32) at 1024 + n*16 + kb*2
     f["flip"][:] = 0
