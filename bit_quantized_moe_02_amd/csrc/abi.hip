@@ -130,7 +130,7 @@ PfLayout pf_layout(const Geometry& g, int64_t T, int k) {
 
 extern "C" size_t moe_route_workspace_bytes(int32_t T, int32_t E) {
   if (T < 1 || E < 1) return 0;
-  return align_up((size_t)T * E * 4);
+  return align_up(route_logit_floats(T, E) * 4);
 }
 
 extern "C" int moe_route(const void* x_bf16, const float* w_router, const float* logit_bias, int32_t T,
@@ -236,12 +236,18 @@ extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, i
   a.ysh = (float*)(wsb + L.ysh);
   a.err_count = (int*)(wsb + L.err);
   const int cus = n_cus();
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 1 && dec1_down_lds(a, 16) <= 160 * 1024) {
+    const int64_t items = (int64_t)k * (g.I / 16) + g.Is / 16;
+    hipError_t e = launch_dec1(a, g.fmt_ug, g.fmt_dn, cpw, topk_w, y, (int)(items < cus ? items : cus), s);
+    if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode", e);
+    return MOE_OK;
+  }
   const int64_t nd_max = (int64_t)(T * k < g.E ? T * k : g.E);
   const int64_t items_ug = nd_max * (g.I / 16) + g.Is / 16;
   const int64_t items_dn = nd_max * (g.H / 16) + (g.Is > 0 ? g.H / 16 : 0);
   const int grid_ug = (int)(items_ug < cus ? items_ug : cus);
   const int grid_dn = (int)(items_dn < 2 * cus ? items_dn : 2 * cus);
-  hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_dec_upgate(a, g.fmt_ug, cpw, grid_ug, s);
   if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode (up/gate)", e);
   e = launch_dec_down(a, g.fmt_dn, grid_dn, s);
@@ -299,6 +305,24 @@ extern "C" int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, 
   a.ysh = (float*)(wsb + L.ysh);
   hipError_t e = launch_prefill(a, g.fmt_ug, g.fmt_dn, topk_w, y, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("moe_expert_ffn_prefill", e);
+  return MOE_OK;
+}
+
+extern "C" int moe_profile_next_launch(int kernel_id, void* start_event, void* stop_event) {
+  clear_error();
+  ProfileHook& hk = profile_hook();
+  if (kernel_id == -1) {
+    hk.n = 0;
+    return MOE_OK;
+  }
+  if (kernel_id < MOE_KERNEL_ROUTE_LOGITS || kernel_id > MOE_KERNEL_PREFILL_COMBINE)
+    return fail(MOE_ERR_INVALID_ARG, "moe_profile_next_launch: unknown kernel id");
+  if (!start_event || !stop_event) return fail(MOE_ERR_INVALID_ARG, "moe_profile_next_launch: NULL event");
+  if (hk.n >= ProfileHook::kMax) return fail(MOE_ERR_INVALID_ARG, "moe_profile_next_launch: too many pending");
+  hk.kernel_id[hk.n] = kernel_id;
+  hk.start[hk.n] = start_event;
+  hk.stop[hk.n] = stop_event;
+  ++hk.n;
   return MOE_OK;
 }
 

@@ -31,6 +31,11 @@ int fail(int code, const std::string& msg) {
 
 void clear_error() { g_last_error.clear(); }
 
+ProfileHook& profile_hook() {
+  static thread_local ProfileHook hook;
+  return hook;
+}
+
 int tile_bytes(int fmt) {
   switch (fmt) {
     case MOE_FMT_CB2: return 1280;

@@ -26,6 +26,7 @@
 #include "../../include/qmoe.h"
 #include "device_common.hpp"
 #include "k_decode.h"
+#include "launch_util.h"
 
 using namespace qmoe_dev;
 using qmoe::DecArgs;
@@ -531,27 +532,27 @@ hipError_t launch_dec_upgate(const DecArgs& a, int fmt, int cpw, int grid, hipSt
   void (*fn)(DecArgs) = nullptr;
   if (fmt == MOE_FMT_CB2) fn = cpw == 1 ? dec_upgate_kernel<MOE_FMT_CB2, 1> : dec_upgate_kernel<MOE_FMT_CB2, 2>;
   else fn = cpw == 1 ? dec_upgate_kernel<MOE_FMT_K4, 1> : dec_upgate_kernel<MOE_FMT_K4, 2>;
-  hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t err = ensure_dyn_lds((const void*)fn);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(fn, dim3(grid), block, lds, s, a);
-  return hipGetLastError();
+  return launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] { hipLaunchKernelGGL(fn, dim3(grid), block, lds, s, a); });
 }
 
 hipError_t launch_dec_down(const DecArgs& a, int fmt, int grid, hipStream_t s) {
   const size_t lds = dec_down_lds(a);
   void (*fn)(DecArgs) = fmt == MOE_FMT_K2 ? dec_down_kernel<MOE_FMT_K2> : dec_down_kernel<MOE_FMT_K4>;
-  hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t err = ensure_dyn_lds((const void*)fn);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * a.nw_dn), lds, s, a);
-  return hipGetLastError();
+  return launch_timed(MOE_KERNEL_DECODE_DOWN, s,
+                      [&] { hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * a.nw_dn), lds, s, a); });
 }
 
 hipError_t launch_combine(const DecArgs& a, const int32_t* topk_idx, const float* topk_w, float* y,
                           hipStream_t s) {
   const int64_t n = (int64_t)a.T * a.H;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.ybuf,
-                     a.Is > 0 ? a.ysh : nullptr, topk_idx, topk_w, a.T, a.k, a.H, a.E, y);
-  return hipGetLastError();
+  return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&] {
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.ybuf,
+                       a.Is > 0 ? a.ysh : nullptr, topk_idx, topk_w, a.T, a.k, a.H, a.E, y);
+  });
 }
 
 }  // namespace qmoe

@@ -5,6 +5,7 @@
 #include "../../include/qmoe.h"
 #include "device_common.hpp"
 #include "k_misc.h"
+#include "launch_util.h"
 
 using namespace qmoe_dev;
 
@@ -179,7 +180,7 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, int64_t rows, int64_t 
     default: fn = dequant_kernel<MOE_FMT_BF16>; break;
   }
   if (lds > 0) {
-    hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, s, packed, n_rt, n_kc, codebook, out);
@@ -191,11 +192,12 @@ size_t group_lds(int E) { return (size_t)(kGroupWaves * E + E + 1) * 4; }
 hipError_t launch_group(const int32_t* topk_idx, int n_slots, int E, int32_t* offsets, int32_t* sorted_slots,
                         int32_t* slot_pos, int* err_count, hipStream_t s) {
   const size_t lds = group_lds(E);
-  hipError_t err = hipFuncSetAttribute((const void*)group_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t err = ensure_dyn_lds((const void*)group_kernel);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(64 * kGroupWaves), lds, s, topk_idx, n_slots, E, offsets,
-                     sorted_slots, slot_pos, err_count);
-  return hipGetLastError();
+  return launch_timed(MOE_KERNEL_GROUP, s, [&] {
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(64 * kGroupWaves), lds, s, topk_idx, n_slots, E, offsets,
+                       sorted_slots, slot_pos, err_count);
+  });
 }
 
 }  // namespace qmoe

@@ -18,6 +18,7 @@
 #include "../../include/qmoe.h"
 #include "device_common.hpp"
 #include "k_prefill.h"
+#include "launch_util.h"
 
 using namespace qmoe_dev;
 using qmoe::PfArgs;
@@ -335,10 +336,9 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
     const size_t lds = kMTiles * 8192 + 2 * kCb2TableBytes;
     void (*fn)(PfArgs) = fmt_ug == MOE_FMT_CB2 ? pf_upgate_kernel<MOE_FMT_CB2, kMTiles>
                                                : pf_upgate_kernel<MOE_FMT_K4, kMTiles>;
-    hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(fn, grid, block, lds, s, a);
-    err = hipGetLastError();
+    err = launch_timed(MOE_KERNEL_PREFILL_UPGATE, s, [&] { hipLaunchKernelGGL(fn, grid, block, lds, s, a); });
     if (err != hipSuccess) return err;
   }
   {
@@ -346,16 +346,16 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
     const size_t lds = kMTiles * 8192;
     void (*fn)(PfArgs) = fmt_dn == MOE_FMT_K2 ? pf_down_kernel<MOE_FMT_K2, kMTiles>
                                               : pf_down_kernel<MOE_FMT_K4, kMTiles>;
-    hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(fn, grid, block, lds, s, a);
-    err = hipGetLastError();
+    err = launch_timed(MOE_KERNEL_PREFILL_DOWN, s, [&] { hipLaunchKernelGGL(fn, grid, block, lds, s, a); });
     if (err != hipSuccess) return err;
   }
   const int64_t n = (int64_t)a.T * a.H;
-  hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.yslot,
-                     a.Is > 0 ? a.ysh : nullptr, a.slot_pos, topk_w, a.T, a.k, a.H, y);
-  return hipGetLastError();
+  return launch_timed(MOE_KERNEL_PREFILL_COMBINE, s, [&] {
+    hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.yslot,
+                       a.Is > 0 ? a.ysh : nullptr, a.slot_pos, topk_w, a.T, a.k, a.H, y);
+  });
 }
 
 }  // namespace qmoe

@@ -6,7 +6,8 @@
 
 namespace qmoe {
 
-// logits: workspace fp32 [T][E].
+// logits: workspace fp32, route_logit_floats(T, E) of them.
+inline size_t route_logit_floats(int T, int E) { return (size_t)(T <= 16 ? 4 : 1) * T * E; }
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
                         int k, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s);
 

@@ -7,23 +7,31 @@
 
 #include "device_common.hpp"
 #include "k_route.h"
+#include "../../include/qmoe.h"
+#include "launch_util.h"
 
 using namespace qmoe_dev;
 
 namespace {
 
-// Few tokens (T <= 16): one wave per expert, each lane a strided 8-column
-// slice of H, then a butterfly sum across the wave.
+// Few tokens (T <= 16): one wave per (expert, quarter of H); each lane takes
+// a strided 8-column slice, the wave sums it with a butterfly and writes the
+// quarter's partial logit (the top-k kernel adds the quarters in order).
+constexpr int kLogitSplit = 4;
+
 __global__ __launch_bounds__(256) void logits_small_kernel(const uint16_t* x, const float* wr,
                                                            const float* bias, int T, int H, int E,
                                                            float* logits) {
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int part = blockIdx.y;
   if (e >= E) return;
   float acc[16];
   for (int t = 0; t < 16; ++t) acc[t] = 0.f;
   const float* w = wr + (size_t)e * H;
-  for (int h0 = 8 * lane; h0 < H; h0 += 512) {
+  const int hq = (H / 8 + kLogitSplit - 1) / kLogitSplit * 8;      // columns per part
+  const int h_end = min(H, (part + 1) * hq);
+  for (int h0 = part * hq + 8 * lane; h0 < h_end; h0 += 512) {
     const float4v w0 = *reinterpret_cast<const float4v*>(w + h0);
     const float4v w1 = *reinterpret_cast<const float4v*>(w + h0 + 4);
     for (int t = 0; t < T; ++t) {
@@ -43,7 +51,7 @@ __global__ __launch_bounds__(256) void logits_small_kernel(const uint16_t* x, co
   for (int t = 0; t < T; ++t) {
     float v = acc[t];
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0) logits[(size_t)t * E + e] = v + (bias ? bias[e] : 0.f);
+    if (lane == 0) logits[((size_t)part * T + t) * E + e] = v + ((bias && part == 0) ? bias[e] : 0.f);
   }
 }
 
@@ -84,24 +92,34 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(const uint16_t* x, co
     }
 }
 
-// One wave per token: k rounds of a wave-wide arg-max over (logit, -index)
-// -- larger logit first, equal logits keep the lower expert index -- then
-// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the kept logits.
-__global__ __launch_bounds__(256) void topk_kernel(const float* logits, int T, int E, int k,
+// One wave per token: the logit of expert e is the sum of n_parts partial
+// logits (in part order); then k rounds of a wave-wide arg-max over
+// (logit, -index) -- larger logit first, equal logits keep the lower expert
+// index -- and w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the kept
+// logits.  Lane j keeps round j's winner (no register arrays are indexed by
+// run-time values).
+__global__ __launch_bounds__(256) void topk_kernel(const float* logits, int n_parts, int T, int E, int k,
                                                    int32_t* topk_idx, float* topk_w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   float v[16];
+#pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? logits[(size_t)t * E + e] : -INFINITY;
+    float s = -INFINITY;
+    if (e < E) {
+      s = logits[(size_t)t * E + e];
+      for (int p = 1; p < n_parts; ++p) s += logits[((size_t)p * T + t) * E + e];
+    }
+    v[i] = s;
   }
-  float kept_v[16];
-  int kept_i[16];
+  float my_v = -INFINITY, top_v = 0.f;
+  int my_i = 0;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = lane + 64 * i;
       if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) {
@@ -117,17 +135,22 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* logits, int T, i
         bi = oi;
       }
     }
-    kept_v[j] = bv;
-    kept_i[j] = bi;
-    if ((bi & 63) == lane) v[bi >> 6] = -INFINITY;
-  }
-  if (lane == 0) {
-    float z = 0.f;
-    for (int j = 0; j < k; ++j) z += expf(kept_v[j] - kept_v[0]);
-    for (int j = 0; j < k; ++j) {
-      topk_idx[(size_t)t * k + j] = kept_i[j];
-      topk_w[(size_t)t * k + j] = expf(kept_v[j] - kept_v[0]) / z;
+    if (j == 0) top_v = bv;
+    if (lane == j) {
+      my_v = bv;
+      my_i = bi;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (lane + 64 * i == bi) v[i] = -INFINITY;
+  }
+  const float p = (lane < k) ? expf(my_v - top_v) : 0.f;
+  // z = sum over j = 0..k-1 in j order (lane order), as a serial sum by lane 0
+  float z = 0.f;
+  for (int j = 0; j < k; ++j) z += __shfl(p, j);
+  if (lane < k) {
+    topk_idx[(size_t)t * k + lane] = my_i;
+    topk_w[(size_t)t * k + lane] = p / z;
   }
 }
 
@@ -137,17 +160,20 @@ namespace qmoe {
 
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
                         int k, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
-  if (T <= 16) {
-    hipLaunchKernelGGL(logits_small_kernel, dim3((E + 3) / 4), dim3(256), 0, s, x, wr, bias, T, H, E,
-                       logits);
-  } else {
-    hipLaunchKernelGGL(logits_tiled_kernel, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x,
-                       wr, bias, T, H, E, logits);
-  }
-  hipError_t err = hipGetLastError();
+  const int n_parts = T <= 16 ? kLogitSplit : 1;
+  hipError_t err = launch_timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+    if (T <= 16)
+      hipLaunchKernelGGL(logits_small_kernel, dim3((E + 3) / 4, kLogitSplit), dim3(256), 0, s, x, wr, bias, T,
+                         H, E, logits);
+    else
+      hipLaunchKernelGGL(logits_tiled_kernel, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x,
+                         wr, bias, T, H, E, logits);
+  });
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, topk_idx, topk_w);
-  return hipGetLastError();
+  return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
+    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, n_parts, T, E, k, topk_idx,
+                       topk_w);
+  });
 }
 
 }  // namespace qmoe

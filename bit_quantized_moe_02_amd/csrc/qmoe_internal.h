@@ -22,4 +22,16 @@ inline int64_t pad256(int64_t k) { return (k + 255) / 256 * 256; }
 // Bytes of one tile of each format; 0 for an unknown format.
 int tile_bytes(int fmt);
 
+// Measurement hook (moe_profile_next_launch): pending (kernel id, start
+// event, stop event) entries of this thread; each is consumed by the next
+// launch of its kernel.
+struct ProfileHook {
+  static constexpr int kMax = 8;
+  int n = 0;
+  int kernel_id[kMax];
+  void* start[kMax];
+  void* stop[kMax];
+};
+ProfileHook& profile_hook();
+
 }  // namespace qmoe

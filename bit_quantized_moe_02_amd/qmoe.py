@@ -35,8 +35,12 @@ EXPORTED = [
     "moe_codebook_generate", "moe_packed_bytes", "moe_quantize_pack",
     "moe_route_workspace_bytes", "moe_route", "moe_group_workspace_bytes",
     "moe_group_tokens", "moe_ffn_workspace_bytes", "moe_expert_ffn_decode",
-    "moe_expert_ffn_prefill", "moe_debug_dequant", "moe_last_error",
+    "moe_expert_ffn_prefill", "moe_debug_dequant", "moe_profile_next_launch", "moe_last_error",
 ]
+
+MOE_KERNEL = {"route_logits": 0, "route_topk": 1, "decode_upgate": 2, "decode_down": 3,
+              "decode_combine": 4, "group": 5, "prefill_upgate": 6, "prefill_down": 7,
+              "prefill_combine": 8}
 
 
 class QmoeError(RuntimeError):
@@ -78,6 +82,7 @@ def _load():
         "moe_expert_ffn_prefill": (ctypes.c_int, [ctypes.POINTER(MoeWeights), vp, i32, i32, vp, vp, vp,
                                                   vp, vp, vp, vp, sz, vp]),
         "moe_debug_dequant": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp, vp]),
+        "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, vp, vp]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -180,6 +185,14 @@ def moe_expert_ffn_prefill(w: MoeWeights, x_bf16, T, k, topk_idx, topk_w, expert
 def moe_debug_dequant(fmt, packed, rows, k, codebook, out, stream=None):
     _check(lib.moe_debug_dequant(FMT.get(fmt, fmt), _ptr(packed), rows, k, _ptr(codebook), _ptr(out),
                                  _stream(stream)))
+
+
+def moe_profile_next_launch(kernel, start_event, stop_event):
+    """Record torch.cuda.Event (or raw hipEvent_t) start/stop around the next
+    launch of `kernel` (name or id) by this thread."""
+    kid = MOE_KERNEL.get(kernel, kernel)
+    ev = lambda e: None if e is None else (e.cuda_event if hasattr(e, "cuda_event") else e)
+    _check(lib.moe_profile_next_launch(kid, ev(start_event), ev(stop_event)))
 
 
 def moe_last_error() -> str:

@@ -232,6 +232,27 @@ int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, int32_t T, 
 int moe_debug_dequant(int fmt, const void* packed, int64_t rows, int64_t k,
                       const int8_t* codebook, float* out, void* stream);
 
+/* Measurement hook.  Kernel ids for moe_profile_next_launch: */
+#define MOE_KERNEL_ROUTE_LOGITS 0
+#define MOE_KERNEL_ROUTE_TOPK 1
+#define MOE_KERNEL_DECODE_UPGATE 2
+#define MOE_KERNEL_DECODE_DOWN 3
+#define MOE_KERNEL_DECODE_COMBINE 4
+#define MOE_KERNEL_GROUP 5
+#define MOE_KERNEL_PREFILL_UPGATE 6
+#define MOE_KERNEL_PREFILL_DOWN 7
+#define MOE_KERNEL_PREFILL_COMBINE 8
+
+/* Makes the next launch of kernel `kernel_id` by this thread record the HIP
+ * events start_event / stop_event (hipEvent_t as void*, owned by the caller)
+ * on its stream immediately before and after itself, so that
+ * hipEventElapsedTime gives that one kernel's duration.  Up to 8 requests
+ * (for different or repeated ids) can be pending; each is consumed by the
+ * next launch of its kernel.  kernel_id -1 drops all pending requests.
+ * Returns MOE_ERR_INVALID_ARG for an unknown id, NULL events or more than 8
+ * pending requests. */
+int moe_profile_next_launch(int kernel_id, void* start_event, void* stop_event);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* moe_last_error(void);
 

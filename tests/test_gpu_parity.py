@@ -227,6 +227,32 @@ def test_decode_single_token_full_size(q, name, steps):
     print("per-token errors", [float(e[0]) for e in errs])
 
 
+ODD_CB2 = register(synth.Workload("odd_cb2_test", 512, 160, 32, 5, 96, "cb2", "cb2", "k2", seed=13, tokens=1))
+ODD_K4 = register(synth.Workload("odd_k4_test", 768, 96, 24, 3, 48, "k4", "k4", "k4", seed=14, tokens=1))
+
+
+@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], ODD_CB2, ODD_K4], ids=lambda w: w.name)
+def test_decode_single_token_odd_shapes(q, wl):
+    """The single-token kernels on padded I / I_s, k = 2, 3, 5, with and
+    without a shared expert, against the oracle and against the multi-token
+    kernels on the same token."""
+    print(f"decode T=1 {wl.name}", flush=True)
+    layer = device_layer(wl)
+    for step in range(3):
+        xb, x64 = x_bits(wl, 1, step=step)
+        idx, w = _route(q, layer, xb, wl.top_k)
+        y1, _ = _decode(q, layer, xb, idx, w, wl.top_k)
+        _check_layer(y1.cpu().numpy(), wl, x64, mirror_tol=2e-4)
+    # two tokens go through the multi-token kernels; each must agree with the
+    # single-token result for that token
+    xb2, x642 = x_bits(wl, 2, step=7)
+    idx2, w2 = _route(q, layer, xb2, wl.top_k)
+    y2, _ = _decode(q, layer, xb2, idx2, w2, wl.top_k)
+    for t in range(2):
+        y1, _ = _decode(q, layer, xb2[t:t + 1], idx2[t:t + 1], w2[t:t + 1], wl.top_k)
+        assert rel_err(y1.cpu().numpy(), y2.cpu().numpy()[t:t + 1]).max() <= 1e-4
+
+
 def test_decode_16_tokens_skewed(q):
     print("decode_b16_hot", flush=True)
     wl = synth.WORKLOADS["decode_b16_hot"]

@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(q):
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(q.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -190,6 +190,12 @@ def test_device_call_argument_errors(q):
     assert lib.moe_debug_dequant(1, P, 16, 256, None, P, None) == 1
     assert lib.moe_debug_dequant(1, P, 17, 256, P, P, None) == 1
     assert lib.moe_debug_dequant(5, P, 16, 256, P, P, None) == 1
+
+
+def test_profile_hook_arguments(q):
+    assert q.lib.moe_profile_next_launch(99, 0x10, 0x20) == 1
+    assert q.lib.moe_profile_next_launch(2, None, 0x20) == 1
+    assert q.lib.moe_profile_next_launch(-1, None, None) == 0
 
 
 def test_binding_raises_with_message(q):
