@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time the steps without the per-kernel events")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every step from Python instead of replaying one captured HIP graph "
+                        "(decode workloads; prefill always runs eagerly)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="also run one elementwise pass (torch.neg) over MIB MiB: a kernel of known "
                         "traffic that the hardware byte counters are scaled by")
@@ -235,11 +238,40 @@ def main():
     for s in range(warmup):
         step(s, None)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(warmup + i, None if args.no_kernel_events else i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    use_graph = decode and not args.eager
+    eager_tps = None
+    if use_graph:
+        # The K timed steps are captured back to back into one HIP graph (each
+        # step: route + expert FFN of its own token, with its own input row,
+        # layer copy and output slots), so host launch overhead -- which a
+        # whole-model decode graph spreads over all its layers -- stays out of
+        # the per-layer figure.  One untimed replay uploads the graph first.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                step(warmup + i, None)
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if not args.no_kernel_events:
+            # Events recorded inside a graph carry no usable timestamps, so the
+            # kernel durations come from a second timed region: the same K
+            # steps launched one by one, with HIP events around each kernel on
+            # the stream it runs on.
+            te0 = time.perf_counter()
+            for i in range(steps):
+                step(warmup + i, i)
+            torch.cuda.synchronize()
+            eager_tps = steps * T / (time.perf_counter() - te0)
+    else:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(warmup + i, None if args.no_kernel_events else i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
     tokens_per_s = steps * T / (t1 - t0)
 
@@ -280,9 +312,12 @@ def main():
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "inter": I, "experts": E, "top_k": k, "shared_inter": Is,
                    "tokens_per_step": T, "formats": "/".join(f.upper() for f in wl.fmts),
-                   "layer_instances": instances},
+                   "layer_instances": instances, "launch": "hip_graph" if use_graph else "eager"},
         "roofline": roof,
         "kernels": per_kernel,
+        "kernel_events_pass": None if per_kernel is None else {
+            "launch": "eager" if use_graph else "same as timed region",
+            "tokens_per_s": None if eager_tps is None else round(eager_tps, 1)},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")

@@ -238,8 +238,7 @@ extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, i
   const int cus = n_cus();
   hipStream_t s = (hipStream_t)stream;
   if (T == 1 && dec1_down_lds(a, 16) <= 160 * 1024) {
-    const int64_t items = (int64_t)k * (g.I / 16) + g.Is / 16;
-    hipError_t e = launch_dec1(a, g.fmt_ug, g.fmt_dn, cpw, topk_w, y, (int)(items < cus ? items : cus), s);
+    hipError_t e = launch_dec1(a, g.fmt_ug, g.fmt_dn, cpw, topk_w, y, cus, s);
     if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode", e);
     return MOE_OK;
   }

@@ -38,8 +38,9 @@ hipError_t launch_dec_down(const DecArgs& a, int fmt, int grid, hipStream_t s);
 // Single-token path (k_decode1.hip): up/gate then down with the shared
 // expert and the weighted combine fused; writes y directly.
 size_t dec1_down_lds(const DecArgs& a, int nw);
+// cus = compute units of the device (the grids are sized from it).
 hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const float* topk_w, float* y,
-                       int grid_ug, hipStream_t s);
+                       int cus, hipStream_t s);
 hipError_t launch_combine(const DecArgs& a, const int32_t* topk_idx, const float* topk_w, float* y,
                           hipStream_t s);
 

@@ -267,15 +267,325 @@ __global__ __launch_bounds__(1024) void dec1_upgate_kernel(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Down + shared down + combine.  Workgroup = one 16-row tile of y.
+// CB2 up/gate at one token (H <= 4096: one K-chunk of 256 columns per wave).
+//
+// Work split: every workgroup takes an even share of both kinds of work --
+// half row tiles (8 rows) of the bf16 shared expert and whole 16-row tiles
+// of the routed experts -- so the LDS-heavy codebook decode is spread over
+// all compute units while the shared expert's plain bf16 stream keeps HBM
+// busy next to it.
+//
+// Decode table (LDS offset 0, 64 KB): entry (idx, half, nib) at byte
+// ((idx*2 + half)*16 + nib)*8 holds the 4 fp16 values T[idx][4*half+i]/4,
+// negated where bit i of nib is set, so a group of 8 weights is two 8-byte
+// reads addressed straight from its 16-bit code (idx | flip << 8).
+//
+// A operands are block-diagonal: A_kb holds x's k-block kb in row kb, so 8
+// accumulating MFMAs leave the per-block dots C[kb][n] (kb = 4g + i in lane
+// (g, n), g < 2), each then scaled by its own fp16 scale.
+//
+// Shared-expert half tiles use the same A registers: for k-block pair p,
+// lanes with n < 8 load row n of k-block 2p and lanes n >= 8 row n-8 of
+// k-block 2p+1, and A_{2p} | A_{2p+1} supplies both activation rows, so one
+// MFMA covers two k-blocks of 8 rows with all 64 lanes loading useful bytes.
+
+constexpr int kCb2CombBytes = 256 * 2 * 16 * 8;
+constexpr int kRedBatch = 8;      // routed row tiles per cross-wave reduction
+constexpr int kPrefetch3 = 3;     // routed row tiles in flight per wave
+
+struct Cb2Pay {
+  u32x4 code[2];     // up, gate: the lane's 8 group codes
+  uint32_t sc[2][2]; // up, gate: fp16 scales of k-blocks 4(g&1) .. 4(g&1)+3 of row n
+  bool ok;           // false: the loads were aimed at a stand-in tile, contribute 0
+};
+
+// Loads are unconditional (a stand-in tile when the item is out of range or
+// its expert id invalid) so they can all be in flight at once.
+__device__ __forceinline__ void cb2_pay_load(Cb2Pay& p, const DecArgs& a, int e, int rt, int chunk, int lane,
+                                             int n_chunks, bool ok) {
+  const int n = lane & 15, g = lane >> 4;
+  const size_t t_off = (size_t)e * a.expert_bytes + ((size_t)rt * n_chunks + chunk) * kCb2Tile;
+  for (int mat = 0; mat < 2; ++mat) {
+    const uint8_t* tile = (mat ? a.gate : a.up) + t_off;
+    p.code[mat] = load16(tile + 16 * lane);
+    const uint2 sp = *reinterpret_cast<const uint2*>(tile + 1024 + 16 * n + 8 * (g & 1));
+    p.sc[mat][0] = sp.x;
+    p.sc[mat][1] = sp.y;
+  }
+  p.ok = ok;
+}
+
+// Group of 8 weights for k-block kb from the lane's code dword (kb, kb^1).
+__device__ __forceinline__ half8 cb2_comb(uint32_t w, int odd, const uint8_t* tab) {
+  const uint32_t c = odd ? (w >> 16) : (w & 0xFFFFu);
+  const uint32_t base = (c & 0xFFu) << 8;
+  const uint32_t a0 = base | ((c >> 5) & 0x78u);          // nib = flip & 15
+  const uint32_t a1 = base | ((c >> 9) & 0x78u);          // nib = flip >> 4
+  const uint2 lo = *reinterpret_cast<const uint2*>(tab + a0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(tab + 128 + a1);
+  return as_half8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+__device__ __forceinline__ float cb2_scaled(const float4v& c, const uint32_t sc[2], bool ok) {
+  float v = h2f(sc[0] & 0xFFFFu) * c[0];
+  v = fmaf(h2f(sc[0] >> 16), c[1], v);
+  v = fmaf(h2f(sc[1] & 0xFFFFu), c[2], v);
+  v = fmaf(h2f(sc[1] >> 16), c[3], v);
+  return ok ? v : 0.f;
+}
+
+__global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* tab = smem;                                                     // [0, 64 KB)
+  const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float* red_r = reinterpret_cast<float*>(smem + kCb2CombBytes);          // [kRedBatch][2][NW][32]
+  float* red_s = red_r + kRedBatch * 2 * NW * 32;                         // [NW][2][8]
+
+  const int k = a.k, n_chunks = a.H / 256, n_rt = a.I / 16, n_rts = a.Is / 16;
+  const int G = gridDim.x, gi = blockIdx.x;
+  const int U_s = 2 * n_rts, U_r = k * n_rt;
+  const int s_lo = (int)((int64_t)gi * U_s / G), s_hi = (int)((int64_t)(gi + 1) * U_s / G);
+  const int r_lo = (int)((int64_t)gi * U_r / G), r_hi = (int)((int64_t)(gi + 1) * U_r / G);
+  const bool active = wave < n_chunks;       // idle waves (H < 1024) load chunk 0 and discard it
+  const int chunk = active ? wave : 0;
+  const int n = lane & 15, g = lane >> 4, m = lane & 15, qq = lane >> 4;
+
+  // ---- prologue.  Loads are issued oldest-first in the order they are
+  // needed (codebook and x, then the shared tile, then a routed tile), so
+  // the table can be built while the weights are still in flight.
+  int8_t cbv[4] = {0, 0, 0, 0};
+  if (tid < 512) {
+    const int8_t* cbp = a.codebook + (tid >> 1) * 8 + 4 * (tid & 1);
+    for (int i = 0; i < 4; ++i) cbv[i] = cbp[i];
+  }
+  u32x4 xr = {0u, 0u, 0u, 0u};
+  if (m < 8) xr = load16(a.x + chunk * 256 + m * 32 + qq * 8);
+
+  // shared half tile loads: 2 matrices x 4 k-block pairs
+  u32x4 sraw[2][4];
+  auto issue_shared = [&](int su) {
+    const int rt = su >> 1, hr = su & 1;
+    const int r = 8 * hr + (n & 7);
+    for (int mat = 0; mat < 2; ++mat) {
+      const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kBf16Tile;
+      for (int p = 0; p < 4; ++p) sraw[mat][p] = load16(tile + 1024 * (2 * p + (n >> 3)) + 16 * (16 * qq + r));
+    }
+  };
+  if (s_lo < s_hi) issue_shared(s_lo);
+
+  int j_ld = r_lo / n_rt, rt_ld = r_lo - j_ld * n_rt;      // next routed item to load
+  Cb2Pay P0, P1, P2;
+  auto issue = [&](Cb2Pay& P, int r) {
+    int e = -1;
+    if (r < r_hi) {
+      e = a.topk_idx[j_ld];
+      if (e >= a.E) e = -1;
+    }
+    const bool ok = e >= 0 && active;
+    cb2_pay_load(P, a, ok ? e : 0, ok ? rt_ld : 0, chunk, lane, n_chunks, ok);
+    if (++rt_ld == n_rt) {
+      rt_ld = 0;
+      ++j_ld;
+    }
+  };
+  issue(P0, r_lo);
+
+  // block-diagonal activations: lane (qq, m) holds x block m (m < 8)
+  half8 A[8];
+  {
+    const u32x4 xh = active ? as_u32x4(bf16x8_to_half8(xr)) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < 8; ++kb) A[kb] = as_half8(m == kb ? xh : z);
+  }
+
+  // decode table, two steps: the 4 fp16 values of each (idx, half) pair
+  // into a staging area, then the 16 sign variants of each, written by
+  // consecutive lanes to consecutive entries (no bank conflicts)
+  uint2* val4 = reinterpret_cast<uint2*>(red_r);          // [512], reuses the reduction area
+  auto put_val4 = [&](int pr, const int8_t* v) {
+    uint32_t w[2];
+    for (int p = 0; p < 2; ++p) {
+      const _Float16 lo = (_Float16)((float)v[2 * p] * 0.25f), hi = (_Float16)((float)v[2 * p + 1] * 0.25f);
+      w[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    val4[pr] = make_uint2(w[0], w[1]);
+  };
+  if (tid < 512) put_val4(tid, cbv);
+  for (int pr = tid + (int)blockDim.x; pr < 512; pr += blockDim.x) {     // workgroups under 512 threads
+    int8_t v[4];
+    for (int i = 0; i < 4; ++i) v[i] = a.codebook[(pr >> 1) * 8 + 4 * (pr & 1) + i];
+    put_val4(pr, v);
+  }
+  __syncthreads();
+  for (int i = tid; i < 512 * 16; i += blockDim.x) {
+    const uint2 v = val4[i >> 4];
+    const uint32_t nib = i & 15;
+    const uint32_t m01 = ((nib & 1u) << 15) | ((nib & 2u) << 30);
+    const uint32_t m23 = ((nib & 4u) << 13) | ((nib & 8u) << 28);
+    *reinterpret_cast<uint2*>(tab + (size_t)i * 8) = make_uint2(v.x ^ m01, v.y ^ m23);
+  }
+  __syncthreads();
+
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- shared expert half tiles
+  for (int su = s_lo; su < s_hi; ++su) {
+    if (su != s_lo) issue_shared(su);
+    float v[2];
+    for (int mat = 0; mat < 2; ++mat) {
+      float4v c = zero;
+      for (int p = 0; p < 4; ++p) {
+        const half8 Ap = as_half8(as_u32x4(A[2 * p]) | as_u32x4(A[2 * p + 1]));
+        c = mfma_f16(Ap, bf16x8_to_half8(sraw[mat][p]), c);
+      }
+      float t = (n < 8) ? c[0] + c[2] : c[1] + c[3];
+      if (g >= 2) t = 0.f;
+      t += __shfl_xor(t, 8);
+      t += __shfl_xor(t, 16);
+      v[mat] = t;
+    }
+    if (lane < 8 && active) {
+      red_s[(wave * 2 + 0) * 8 + lane] = v[0];
+      red_s[(wave * 2 + 1) * 8 + lane] = v[1];
+    }
+    __syncthreads();
+    if (tid < 8) {
+      float u = 0.f, gg = 0.f;
+      for (int w = 0; w < n_chunks; ++w) {
+        u += red_s[(w * 2 + 0) * 8 + tid];
+        gg += red_s[(w * 2 + 1) * 8 + tid];
+      }
+      a.hs[(su >> 1) * 16 + 8 * (su & 1) + tid] = (_Float16)(silu(gg) * u);
+    }
+    __syncthreads();
+  }
+
+  // ---- routed row tiles, kPrefetch3 in flight per wave (the second and
+  // third are issued only now: their registers held the shared tile)
+  issue(P1, r_lo + 1);
+  issue(P2, r_lo + 2);
+  auto compute = [&](const Cb2Pay& P, int b) {
+    float4v cu = zero, cg = zero;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      cu = mfma_f16(A[kb], cb2_comb(P.code[0][kb >> 1], kb & 1, tab), cu);
+      cg = mfma_f16(A[kb], cb2_comb(P.code[1][kb >> 1], kb & 1, tab), cg);
+    }
+    if (lane < 32 && active) {
+      red_r[((b * 2 + 0) * NW + wave) * 32 + lane] = cb2_scaled(cu, P.sc[0], P.ok);
+      red_r[((b * 2 + 1) * NW + wave) * 32 + lane] = cb2_scaled(cg, P.sc[1], P.ok);
+    }
+  };
+  auto flush = [&](int first, int nb) {
+    __syncthreads();
+    if (tid < nb * 16) {
+      const int b = tid >> 4, item = first + b;
+      float u = 0.f, gg = 0.f;
+      for (int w = 0; w < n_chunks; ++w) {
+        u += red_r[((b * 2 + 0) * NW + w) * 32 + n];
+        u += red_r[((b * 2 + 0) * NW + w) * 32 + 16 + n];
+        gg += red_r[((b * 2 + 1) * NW + w) * 32 + n];
+        gg += red_r[((b * 2 + 1) * NW + w) * 32 + 16 + n];
+      }
+      const _Float16 h16 = (_Float16)(silu(gg) * u);
+      const float hv = (float)h16;
+      const int j = item / n_rt, rt = item - j * n_rt;
+      a.h[(size_t)j * a.I + rt * 16 + n] = h16;
+      const int kk = (rt * 16 + n) & 255;
+      const int t = k2_slot_t(kk >> 5, (kk & 7) >> 1);
+      float X = hv, O = 1024.0f * (float)(_Float16)(hv * __builtin_ldexpf(1.0f, -2 * t));
+      for (int o = 8; o >= 1; o >>= 1) {
+        X += __shfl_xor(X, o);
+        O += __shfl_xor(O, o);
+      }
+      if (n == 0) {
+        float* hsm = a.hsum + ((size_t)j * (a.I_pad / 16) + rt) * 2;
+        hsm[0] = X;
+        hsm[1] = O;
+      }
+    }
+    __syncthreads();
+  };
+
+  int nb = 0, first = r_lo;
+  for (int r = r_lo; r < r_hi; r += kPrefetch3) {
+    compute(P0, nb);
+    issue(P0, r + 3);
+    if (++nb == kRedBatch || r + 1 == r_hi) {
+      flush(first, nb);
+      first = r + 1;
+      nb = 0;
+    }
+    if (r + 1 >= r_hi) break;
+    compute(P1, nb);
+    issue(P1, r + 4);
+    if (++nb == kRedBatch || r + 2 == r_hi) {
+      flush(first, nb);
+      first = r + 2;
+      nb = 0;
+    }
+    if (r + 2 >= r_hi) break;
+    compute(P2, nb);
+    issue(P2, r + 5);
+    if (++nb == kRedBatch || r + 3 == r_hi) {
+      flush(first, nb);
+      first = r + 3;
+      nb = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-wave payload of one routed down unit (one K-chunk of one 16-row tile).
+
+template <int FMT>
+struct DnPay;
+template <>
+struct DnPay<MOE_FMT_K2> {
+  u32x4 q;
+  uint32_t scm, dd;
+};
+template <>
+struct DnPay<MOE_FMT_K4> {
+  u32x4 q0, q1;
+  uint32_t s0, s1, s2, dd;
+};
+
+template <int FMT>
+__device__ __forceinline__ void dn_load(DnPay<FMT>& p, const uint8_t* tile, int lane) {
+  const int n = lane & 15, g4 = lane >> 4;
+  if constexpr (FMT == MOE_FMT_K2) {
+    p.q = load16(tile + 16 * lane);
+    p.scm = *reinterpret_cast<const uint32_t*>(tile + 1024 + 16 * n + 4 * g4);
+    p.dd = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
+  } else {
+    p.q0 = load16(tile + 16 * lane);
+    p.q1 = load16(tile + 1024 + 16 * lane);
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(tile + 2048 + 12 * n);
+    p.s0 = sp[0];
+    p.s1 = sp[1];
+    p.s2 = sp[2];
+    p.dd = *reinterpret_cast<const uint32_t*>(tile + 2240 + 4 * n);
+  }
+}
+
+// Down + shared down + combine.  Workgroup = one 16-row tile of y; the k
+// routed down matrices and the shared one form one stacked GEMV over
+// K = k*I + I_s, split over the waves in units of one 256-column K-chunk
+// (routed) or half a chunk (shared).  Every wave issues the loads of all its
+// units before the activations are staged, so HBM latency overlaps staging.
+constexpr int kDnUnits = 4;    // routed units held in registers per wave
+constexpr int kStageVec = 4;   // staged 16-byte vectors per thread per pass
 
 template <int FMT>
 __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float* topk_w, float* y) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = a.k, I = a.I, I_pad = a.I_pad, Is = a.Is, Is_pad = a.Is_pad;
   const int n_ck = I_pad / 256, n_cks = Is > 0 ? Is_pad / 256 : 0;
-  // LDS: staged activations (fp16), per-16-row sums, routing, reduction
+  // LDS: staged activations (fp16), per-16-row sums, reduction
   _Float16* hst = reinterpret_cast<_Float16*>(smem);                        // [k][I_pad] (K2: prescaled)
   _Float16* hss = hst + (size_t)k * I_pad;                                    // [Is_pad]
   size_t off = ((size_t)k * I_pad + Is_pad) * 2;
@@ -284,103 +594,148 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
   off += 16;
   float* xo = reinterpret_cast<float*>(smem + off);                           // [k][I_pad/16][2]
   off += (size_t)k * (I_pad / 16) * 2 * 4;
-  float* wj = reinterpret_cast<float*>(smem + off);                           // [k]
-  int* ej = reinterpret_cast<int*>(wj + 16);                                  // [k]
-  float* red = reinterpret_cast<float*>(ej + 16);                             // [NW][16]
+  float* red = reinterpret_cast<float*>(smem + off);                          // [NW][16]
 
-  for (int i = tid; i < k * I_pad; i += blockDim.x) {
-    const int j = i / I_pad, col = i % I_pad;
-    _Float16 v = (_Float16)0.0f;
-    if (col < I) {
-      v = a.h[(size_t)j * I + col];
-      if (FMT == MOE_FMT_K2) {
-        const int kk = col & 255;
-        v = v * (_Float16)__builtin_ldexpf(1.0f, -2 * k2_slot_t(kk >> 5, (kk & 7) >> 1));
+  const int rt = blockIdx.x;
+  const int n = lane & 15, g4 = lane >> 4, m = lane & 15;
+  const int n_units = k * n_ck, n_sunits = 2 * n_cks;
+  const size_t tb = FMT == MOE_FMT_K2 ? kK2Tile : kK4Tile;
+
+  // ---- first round of loads: routed units wave + NW*i, one shared unit
+  DnPay<FMT> P[kDnUnits];
+  int uj[kDnUnits], ukc[kDnUnits], ue[kDnUnits];
+  auto issue_round = [&](int base) {
+    for (int i = 0; i < kDnUnits; ++i) {
+      const int u = base + wave + NW * i;
+      ue[i] = -1;
+      if (u < n_units) {
+        const int j = u / n_ck;
+        uj[i] = j;
+        ukc[i] = u - j * n_ck;
+        const int e = a.topk_idx[j];
+        if (e >= 0 && e < a.E) {
+          ue[i] = e;
+          dn_load<FMT>(P[i], a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + ukc[i]) * tb, lane);
+        }
       }
     }
-    hst[i] = v;
-  }
-  for (int i = tid; i < Is_pad; i += blockDim.x) hss[i] = (i < Is) ? a.hs[i] : (_Float16)0.0f;
-  for (int i = tid; i < k * (I_pad / 16) * 2; i += blockDim.x) {
-    const int j = i / ((I_pad / 16) * 2), r = i % ((I_pad / 16) * 2);
-    xo[i] = (r / 2 < I / 16) ? a.hsum[(size_t)j * (I_pad / 16) * 2 + r] : 0.f;
+  };
+  u32x4 sraw[4];
+  int s_kc = -1, s_kb0 = 0;
+  auto issue_shared = [&](int su) {
+    s_kc = -1;
+    if (su < n_sunits) {
+      s_kc = su >> 1;
+      s_kb0 = 4 * (su & 1);
+      const uint8_t* tile = a.sdown + ((size_t)rt * n_cks + s_kc) * kBf16Tile;
+      for (int q = 0; q < 4; ++q) sraw[q] = load16(tile + 1024 * (s_kb0 + q) + 16 * lane);
+    }
+  };
+  issue_round(0);
+  issue_shared(wave);
+
+  // ---- stage the activations.  Every thread issues all of its loads
+  // (h vectors, per-16-row sums, shared h) before it uses any of them, so
+  // the staging costs one memory round trip.
+  const int cvp = I_pad / 8, cv = I / 8;              // 8-column vectors per slot row
+  const int nrp = I_pad / 16, nr = I / 16;            // 16-row sums per slot row
+  const int n_hv = k * cvp, n_xv = k * (nrp / 2), n_sv = Is_pad / 8;
+  for (int base = 0; base < n_hv + n_xv + n_sv; base += kStageVec * (int)blockDim.x) {
+    u32x4 v[kStageVec];
+    int dst[kStageVec];      // LDS byte offset, -1 = nothing
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const int id = base + tid + i * (int)blockDim.x;
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+      dst[i] = -1;
+      if (id < n_hv) {
+        const int j = id / cvp, c = id - j * cvp;
+        if (c < cv) v[i] = load16(a.h + (size_t)j * I + 8 * c);
+        dst[i] = (j * I_pad + 8 * c) * 2;
+        if (FMT == MOE_FMT_K2) dst[i] |= (c >> 2) & 1 ? 0x40000000 : 0x20000000;
+      } else if (id < n_hv + n_xv) {
+        const int q = id - n_hv, j = q / (nrp / 2), c = q - j * (nrp / 2);
+        const float* src = a.hsum + ((size_t)j * nrp + 2 * c) * 2;
+        if (2 * c + 1 < nr) v[i] = load16(src);
+        else if (2 * c < nr) v[i] = u32x4{__builtin_bit_cast(uint32_t, src[0]), __builtin_bit_cast(uint32_t, src[1]), 0u, 0u};
+        dst[i] = (int)((uint8_t*)(xo + ((size_t)j * nrp + 2 * c) * 2) - smem);
+      } else if (id < n_hv + n_xv + n_sv) {
+        const int c = id - n_hv - n_xv;
+        if (c < Is / 8) v[i] = load16(a.hs + 8 * c);
+        dst[i] = (int)((uint8_t*)(hss + 8 * c) - smem);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      if (dst[i] < 0) continue;
+      u32x4 w = v[i];
+      if (FMT == MOE_FMT_K2 && (dst[i] & 0x60000000)) {
+        // column pair s of an 8-column group sits at slot t(kb, s); scale by 4^-t
+        const half8 f = (dst[i] & 0x40000000)
+                            ? half8{0.00390625f16, 0.00390625f16, 1.0f16, 1.0f16, 0.25f16, 0.25f16, 0.0625f16, 0.0625f16}
+                            : half8{1.0f16, 1.0f16, 0.25f16, 0.25f16, 0.0625f16, 0.0625f16, 0.015625f16, 0.015625f16};
+        w = as_u32x4(as_half8(w) * f);
+      }
+      *reinterpret_cast<u32x4*>(smem + (dst[i] & 0x1FFFFFFF)) = w;
+    }
   }
   if (tid < 4) reinterpret_cast<uint32_t*>(zero16)[tid] = 0u;
-  if (tid < k) {
-    const int e = a.topk_idx[tid];
-    ej[tid] = (e >= 0 && e < a.E) ? e : -1;
-    wj[tid] = topk_w[tid];
-  }
   __syncthreads();
 
-  const int64_t rt = blockIdx.x;
-  const int n = lane & 15, g4 = lane >> 4, m = lane & 15;
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
   float acc = 0.f;
-  const int n_units = k * n_ck;
-  for (int u = wave; u < n_units; u += NW) {
-    const int j = u / n_ck, kc = u % n_ck;
-    const int e = ej[j];
-    if (e < 0) continue;
-    const float wgt = wj[j];
-    if constexpr (FMT == MOE_FMT_K2) {
-      const uint8_t* tile = a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + kc) * kK2Tile;
-      const u32x4 qw = load16(tile + 16 * lane);
-      const uint32_t scm = *reinterpret_cast<const uint32_t*>(tile + 1024 + 16 * n + 4 * g4);
-      const uint32_t dd = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
-      float4v c = zero;
+  for (int base = 0; base < n_units; base += kDnUnits * NW) {
+    if (base > 0) issue_round(base);
+    for (int i = 0; i < kDnUnits; ++i) {
+      if (ue[i] < 0) continue;
+      const int j = uj[i], kc = ukc[i];
+      const float wgt = topk_w[j];
+      const DnPay<FMT>& p = P[i];
       const _Float16* hbase = hst + (size_t)j * I_pad + kc * 256 + g4 * 8;
-      for (int kb = 0; kb < 8; ++kb) {
-        const bool active = m == 2 * kb + (g4 >> 1);
-        const uint8_t* src = active ? reinterpret_cast<const uint8_t*>(hbase + kb * 32) : zero16;
-        c = mfma_f16(as_half8(load16(src)), as_half8(k2_magic(qw, kb)), c);
+      if constexpr (FMT == MOE_FMT_K2) {
+        float4v c = zero;
+        for (int kb = 0; kb < 8; ++kb) {
+          const bool act = m == 2 * kb + (g4 >> 1);
+          const uint8_t* src = act ? reinterpret_cast<const uint8_t*>(hbase + kb * 32) : zero16;
+          c = mfma_f16(as_half8(load16(src)), as_half8(k2_magic(p.q, kb)), c);
+        }
+        // C[4 g4 + i][n] = sub-block 4 g4 + i of this super-block; xo holds
+        // (X, O) of sub-block s at 2s, 2s+1
+        const float4v X = *reinterpret_cast<const float4v*>(xo + ((size_t)j * (I_pad / 16) + kc * 16 + 4 * g4) * 2);
+        const float4v O = *reinterpret_cast<const float4v*>(xo + ((size_t)j * (I_pad / 16) + kc * 16 + 4 * g4) * 2 + 4);
+        const float xs[4] = {X[0], X[2], O[0], O[2]};
+        const float os[4] = {X[1], X[3], O[1], O[3]};
+        float dsum = 0.f, msum = 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t byte = (p.scm >> (8 * q)) & 0xFFu;
+          dsum += (float)(byte & 15u) * (c[q] - os[q]);
+          msum += (float)(byte >> 4) * xs[q];
+        }
+        acc += (wgt * h2f(p.dd & 0xFFFFu)) * dsum - (wgt * h2f(p.dd >> 16)) * msum;
+      } else {  // K4
+        const float d = h2f(p.dd & 0xFFFFu), dmin = h2f(p.dd >> 16);
+        float part = 0.f;
+        for (int kb = 0; kb < 8; ++kb) {
+          const uint8_t* src = (m == 0) ? reinterpret_cast<const uint8_t*>(hbase + kb * 32) : zero16;
+          const uint32_t w = kb < 4 ? p.q0[kb & 3] : p.q1[kb & 3];
+          const float4v c = mfma_f16(as_half8(load16(src)), as_half8(k4_magic(w)), zero);
+          const float dsc = d * (float)k4_scale_value(p.s0, p.s1, p.s2, kb);
+          const float corr = 1024.0f * dsc + dmin * (float)k4_scale_value(p.s0, p.s1, p.s2, 8 + kb);
+          const float* xk = xo + ((size_t)j * (I_pad / 16) + kc * 16 + 2 * kb) * 2;
+          part += dsc * c[0] - corr * (xk[0] + xk[2]);
+        }
+        if (g4 == 0) acc += wgt * part;
       }
-      // C[4 g4 + i][n] = sub-block 4 g4 + i of this super-block
-      const float4v X = *reinterpret_cast<const float4v*>(xo + ((size_t)j * (I_pad / 16) + kc * 16 + 4 * g4) * 2);
-      const float4v O = *reinterpret_cast<const float4v*>(xo + ((size_t)j * (I_pad / 16) + kc * 16 + 4 * g4) * 2 + 4);
-      // xo is (X, O) interleaved: X of sub-block s at 2s, O at 2s+1
-      const float xs[4] = {X[0], X[2], O[0], O[2]};
-      const float os[4] = {X[1], X[3], O[1], O[3]};
-      float dsum = 0.f, msum = 0.f;
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t byte = (scm >> (8 * i)) & 0xFFu;
-        dsum += (float)(byte & 15u) * (c[i] - os[i]);
-        msum += (float)(byte >> 4) * xs[i];
-      }
-      acc += (wgt * h2f(dd & 0xFFFFu)) * dsum - (wgt * h2f(dd >> 16)) * msum;
-    } else {  // K4
-      const uint8_t* tile = a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + kc) * kK4Tile;
-      const u32x4 q0 = load16(tile + 16 * lane);
-      const u32x4 q1 = load16(tile + 1024 + 16 * lane);
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(tile + 2048 + 12 * n);
-      const uint32_t s0 = sp[0], s1 = sp[1], s2 = sp[2];
-      const uint32_t dd = *reinterpret_cast<const uint32_t*>(tile + 2240 + 4 * n);
-      const float d = h2f(dd & 0xFFFFu), dmin = h2f(dd >> 16);
-      const _Float16* hbase = hst + (size_t)j * I_pad + kc * 256 + g4 * 8;
-      float part = 0.f;
-      for (int kb = 0; kb < 8; ++kb) {
-        const uint8_t* src = (m == 0) ? reinterpret_cast<const uint8_t*>(hbase + kb * 32) : zero16;
-        const uint32_t w = kb < 4 ? q0[kb & 3] : q1[kb & 3];
-        const float4v c = mfma_f16(as_half8(load16(src)), as_half8(k4_magic(w)), zero);
-        const float dsc = d * (float)k4_scale_value(s0, s1, s2, kb);
-        const float corr = 1024.0f * dsc + dmin * (float)k4_scale_value(s0, s1, s2, 8 + kb);
-        const float* xk = xo + ((size_t)j * (I_pad / 16) + kc * 16 + 2 * kb) * 2;
-        part += dsc * c[0] - corr * (xk[0] + xk[2]);
-      }
-      if (g4 == 0) acc += wgt * part;
     }
   }
   // shared expert: units of half a K-chunk (4 k-blocks)
-  for (int u = wave; u < 2 * n_cks; u += NW) {
-    const int kc = u >> 1, kb0 = 4 * (u & 1);
-    const uint8_t* tile = a.sdown + ((size_t)rt * n_cks + kc) * kBf16Tile;
-    u32x4 raw[4];
-    for (int q = 0; q < 4; ++q) raw[q] = load16(tile + 1024 * (kb0 + q) + 16 * lane);
+  for (int su = wave; su < n_sunits; su += NW) {
+    if (su != wave) issue_shared(su);
     float4v c = zero;
-    const _Float16* hbase = hss + kc * 256 + g4 * 8;
+    const _Float16* hbase = hss + s_kc * 256 + g4 * 8;
     for (int q = 0; q < 4; ++q) {
-      const uint8_t* src = (m == 0) ? reinterpret_cast<const uint8_t*>(hbase + (kb0 + q) * 32) : zero16;
-      c = mfma_f16(as_half8(load16(src)), bf16x8_to_half8(raw[q]), c);
+      const uint8_t* src = (m == 0) ? reinterpret_cast<const uint8_t*>(hbase + (s_kb0 + q) * 32) : zero16;
+      c = mfma_f16(as_half8(load16(src)), bf16x8_to_half8(sraw[q]), c);
     }
     acc += c[0];
   }
@@ -411,20 +766,41 @@ size_t dec1_down_lds(const DecArgs& a, int nw) {
   size_t off = ((size_t)a.k * a.I_pad + a.Is_pad) * 2;
   off = (off + 15) & ~size_t(15);
   off += 16 + (size_t)a.k * (a.I_pad / 16) * 2 * 4;
-  return off + 16 * 4 + 16 * 4 + (size_t)nw * 16 * 4;
+  return off + (size_t)nw * 16 * 4;
+}
+
+size_t dec1_cb2_upgate_lds(int nw) {
+  return (size_t)kCb2CombBytes + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4;
 }
 
 hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const float* topk_w, float* y,
-                       int grid_ug, hipStream_t s) {
-  const int nw_ug = (a.H / 256 + cpw - 1) / cpw;
-  void (*fu)(DecArgs) = nullptr;
-  if (fmt_ug == MOE_FMT_CB2) fu = cpw == 1 ? dec1_upgate_kernel<MOE_FMT_CB2, 1> : dec1_upgate_kernel<MOE_FMT_CB2, 2>;
-  else fu = cpw == 1 ? dec1_upgate_kernel<MOE_FMT_K4, 1> : dec1_upgate_kernel<MOE_FMT_K4, 2>;
-  hipError_t err = ensure_dyn_lds((const void*)fu);
-  if (err != hipSuccess) return err;
-  const size_t lds_ug = dec1_upgate_lds(a, fmt_ug, nw_ug);
-  err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s,
-                     [&] { hipLaunchKernelGGL(fu, dim3(grid_ug), dim3(64 * nw_ug), lds_ug, s, a); });
+                       int cus, hipStream_t s) {
+  hipError_t err;
+  const int n_chunks = a.H / 256;
+  if (fmt_ug == MOE_FMT_CB2 && n_chunks <= 16) {
+    const int nw = n_chunks < 4 ? 4 : n_chunks;
+    const int U_s = 2 * (a.Is / 16), U_r = a.k * (a.I / 16);
+    const int most = U_s > U_r ? U_s : U_r;
+    const int grid = most < cus ? most : cus;
+    err = ensure_dyn_lds((const void*)dec1_cb2_upgate_kernel);
+    if (err != hipSuccess) return err;
+    const size_t lds = dec1_cb2_upgate_lds(nw);
+    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
+      hipLaunchKernelGGL(dec1_cb2_upgate_kernel, dim3(grid), dim3(64 * nw), lds, s, a);
+    });
+  } else {
+    const int nw_ug = (n_chunks + cpw - 1) / cpw;
+    const int64_t items = (int64_t)a.k * (a.I / 16) + a.Is / 16;
+    const int grid_ug = (int)(items < cus ? items : cus);
+    void (*fu)(DecArgs) = nullptr;
+    if (fmt_ug == MOE_FMT_CB2) fu = cpw == 1 ? dec1_upgate_kernel<MOE_FMT_CB2, 1> : dec1_upgate_kernel<MOE_FMT_CB2, 2>;
+    else fu = cpw == 1 ? dec1_upgate_kernel<MOE_FMT_K4, 1> : dec1_upgate_kernel<MOE_FMT_K4, 2>;
+    err = ensure_dyn_lds((const void*)fu);
+    if (err != hipSuccess) return err;
+    const size_t lds_ug = dec1_upgate_lds(a, fmt_ug, nw_ug);
+    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s,
+                       [&] { hipLaunchKernelGGL(fu, dim3(grid_ug), dim3(64 * nw_ug), lds_ug, s, a); });
+  }
   if (err != hipSuccess) return err;
   constexpr int nw_dn = 16;
   void (*fd)(DecArgs, const float*, float*) =

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "k_route.h"
 #include "../../include/qmoe.h"
@@ -14,24 +16,26 @@ using namespace qmoe_dev;
 
 namespace {
 
-// Few tokens (T <= 16): one wave per (expert, quarter of H); each lane takes
-// a strided 8-column slice, the wave sums it with a butterfly and writes the
-// quarter's partial logit (the top-k kernel adds the quarters in order).
-constexpr int kLogitSplit = 4;
+// Few tokens (T <= 16): one wave per (expert, 1/n_parts of H); each lane
+// takes 8 consecutive columns of each 512-column slice (one slice per wave
+// when H <= 8192, so every load of a wave is in flight at once), the wave sums
+// with a butterfly and writes its part's partial logit (the top-k kernel adds
+// the parts in part order).
+constexpr int kMaxLogitParts = 16;
 
 __global__ __launch_bounds__(256) void logits_small_kernel(const uint16_t* x, const float* wr,
                                                            const float* bias, int T, int H, int E,
                                                            float* logits) {
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int part = blockIdx.y;
+  const int part = blockIdx.y, n_parts = gridDim.y;
   if (e >= E) return;
   float acc[16];
   for (int t = 0; t < 16; ++t) acc[t] = 0.f;
   const float* w = wr + (size_t)e * H;
-  const int hq = (H / 8 + kLogitSplit - 1) / kLogitSplit * 8;      // columns per part
-  const int h_end = min(H, (part + 1) * hq);
-  for (int h0 = part * hq + 8 * lane; h0 < h_end; h0 += 512) {
+  const int cpp = (H + 512 * n_parts - 1) / (512 * n_parts) * 512;     // columns per part
+  const int h_end = min(H, (part + 1) * cpp);
+  for (int h0 = part * cpp + 8 * lane; h0 < h_end; h0 += 512) {
     const float4v w0 = *reinterpret_cast<const float4v*>(w + h0);
     const float4v w1 = *reinterpret_cast<const float4v*>(w + h0 + 4);
     for (int t = 0; t < T; ++t) {
@@ -92,65 +96,83 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(const uint16_t* x, co
     }
 }
 
-// One wave per token: the logit of expert e is the sum of n_parts partial
-// logits (in part order); then k rounds of a wave-wide arg-max over
-// (logit, -index) -- larger logit first, equal logits keep the lower expert
-// index -- and w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the kept
-// logits.  Lane j keeps round j's winner (no register arrays are indexed by
-// run-time values).
-__global__ __launch_bounds__(256) void topk_kernel(const float* logits, int n_parts, int T, int E, int k,
-                                                   int32_t* topk_idx, float* topk_w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    float s = -INFINITY;
+// Top-k by rank counting, one 1024-thread workgroup per token.  The logit of
+// expert e is the sum of n_parts partial logits (in part order).  Each
+// (logit, e) becomes a 64-bit key whose integer order is "larger logit first,
+// equal logits (+0 and -0 identified) lower index first"; all keys are
+// distinct, so the rank of a key -- the number of keys above it -- is its
+// position in that order.  Four threads count each key's rank over a quarter
+// of the keys each.  The experts of rank < k are kept, and
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) with the sum taken in rank
+// order.
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+  if (l == 0.0f) l = 0.0f;
+  uint32_t b = __builtin_bit_cast(uint32_t, l);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+constexpr int kTopkThreads = 1024;
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits, int n_parts, int T, int E, int k,
+                                                            int32_t* topk_idx, float* topk_w) {
+  __shared__ __align__(16) uint64_t key[1024];
+  __shared__ float lg[1024];
+  __shared__ int part_rank[4][256];
+  __shared__ float kv[16];
+  __shared__ int ki[16];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int Ep = (E + 7) & ~7;                 // keys padded with 0 (below every real key)
+  for (int e = tid; e < Ep; e += kTopkThreads) {
+    float s = 0.f;
+    uint64_t kk = 0;
     if (e < E) {
-      s = logits[(size_t)t * E + e];
-      for (int p = 1; p < n_parts; ++p) s += logits[((size_t)p * T + t) * E + e];
-    }
-    v[i] = s;
-  }
-  float my_v = -INFINITY, top_v = 0.f;
-  int my_i = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+      float pv[kMaxLogitParts];                // all partial loads in flight together
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
+      for (int p = 0; p < kMaxLogitParts; ++p)
+        pv[p] = p < n_parts ? logits[((size_t)p * T + t) * E + e] : 0.f;
+      s = pv[0];
+#pragma unroll
+      for (int p = 1; p < kMaxLogitParts; ++p)
+        if (p < n_parts) s += pv[p];
+      kk = route_key(s, e);
+    }
+    key[e] = kk;
+    lg[e] = s;
+  }
+  __syncthreads();
+  const int q = tid >> 8, el = tid & 255;
+  const int span = Ep / 4;                      // multiple of 2
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int e = e0 + el;
+    int cnt = 0;
+    if (e < E) {
+      const uint64_t mine = key[e];
+      const int i_end = (q + 1) * span;
+      for (int i = q * span; i < i_end; i += 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&key[i]);
+        const uint64_t k0 = (uint64_t)v.x | ((uint64_t)v.y << 32);
+        const uint64_t k1 = (uint64_t)v.z | ((uint64_t)v.w << 32);
+        cnt += (k0 > mine) + (k1 > mine);
       }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
+    part_rank[q][el] = cnt;
+    __syncthreads();
+    if (q == 0 && e < E) {
+      const int rank = part_rank[0][el] + part_rank[1][el] + part_rank[2][el] + part_rank[3][el];
+      if (rank < k) {
+        kv[rank] = lg[e];
+        ki[rank] = e;
       }
     }
-    if (j == 0) top_v = bv;
-    if (lane == j) {
-      my_v = bv;
-      my_i = bi;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (lane + 64 * i == bi) v[i] = -INFINITY;
+    __syncthreads();
   }
-  const float p = (lane < k) ? expf(my_v - top_v) : 0.f;
-  // z = sum over j = 0..k-1 in j order (lane order), as a serial sum by lane 0
-  float z = 0.f;
-  for (int j = 0; j < k; ++j) z += __shfl(p, j);
-  if (lane < k) {
-    topk_idx[(size_t)t * k + lane] = my_i;
-    topk_w[(size_t)t * k + lane] = p / z;
+  if (tid < k) {
+    const float top = kv[0];
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += expf(kv[j] - top);
+    topk_idx[(size_t)t * k + tid] = ki[tid];
+    topk_w[(size_t)t * k + tid] = expf(kv[tid] - top) / z;
   }
 }
 
@@ -160,10 +182,10 @@ namespace qmoe {
 
 hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
                         int k, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
-  const int n_parts = T <= 16 ? kLogitSplit : 1;
+  const int n_parts = T <= 16 ? std::min(kMaxLogitParts, (H + 511) / 512) : 1;
   hipError_t err = launch_timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
     if (T <= 16)
-      hipLaunchKernelGGL(logits_small_kernel, dim3((E + 3) / 4, kLogitSplit), dim3(256), 0, s, x, wr, bias, T,
+      hipLaunchKernelGGL(logits_small_kernel, dim3((E + 3) / 4, n_parts), dim3(256), 0, s, x, wr, bias, T,
                          H, E, logits);
     else
       hipLaunchKernelGGL(logits_tiled_kernel, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x,
@@ -171,7 +193,7 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
   });
   if (err != hipSuccess) return err;
   return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
-    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, n_parts, T, E, k, topk_idx,
+    hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(kTopkThreads), 0, s, logits, n_parts, T, E, k, topk_idx,
                        topk_w);
   });
 }
