@@ -195,8 +195,8 @@ extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, i
     return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: NULL pointer");
   if (T < 1 || T > 16) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: T must be in [1, 16]");
   if (k < 1 || k > 16 || k > g.E) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: need 1 <= k <= min(E, 16)");
-  if (!aligned16(x_bf16) || !aligned16(ws))
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: x and ws must be 16-byte aligned");
+  if (!aligned16(x_bf16) || !aligned16(ws) || !aligned16(y))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: x, y and ws must be 16-byte aligned");
   const DecLayout L = dec_layout(g, T, k);
   if (ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn_decode: workspace too small (need " + std::to_string(L.total) + ")");
@@ -270,8 +270,8 @@ extern "C" int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, 
   if (T < 1 || (int64_t)T * 16 > (1ll << 26))
     return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_prefill: T must be in [1, 2^22]");
   if (k < 1 || k > 16 || k > g.E) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_prefill: need 1 <= k <= min(E, 16)");
-  if (!aligned16(x_bf16) || !aligned16(ws))
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_prefill: x and ws must be 16-byte aligned");
+  if (!aligned16(x_bf16) || !aligned16(ws) || !aligned16(y))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_prefill: x, y and ws must be 16-byte aligned");
   const PfLayout L = pf_layout(g, T, k);
   if (ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn_prefill: workspace too small (need " + std::to_string(L.total) + ")");

@@ -110,6 +110,58 @@ __device__ __forceinline__ half8 cb2_group(uint32_t code, const uint8_t* val_lan
   return as_half8(v ^ m);
 }
 
+// CB2 combined table (64 KB, the kernels place it at LDS offset 0): entry
+// (idx, half, nib) at byte ((idx*2 + half)*16 + nib)*8 holds the 4 fp16
+// values T[idx][4*half+i]/4, negated where bit i of nib is set, so a group of
+// 8 weights is two 8-byte reads addressed straight from its 16-bit code
+// (idx | flip << 8): half 0 takes flip bits 0..3, half 1 bits 4..7.
+constexpr int kCb2CombBytes = 256 * 2 * 16 * 8;
+
+// Group of 8 weights from a dword holding the codes of k-blocks (kb, kb^1):
+// the low 16 bits for even kb (odd = 0), the high 16 bits for odd kb.
+__device__ __forceinline__ half8 cb2_comb(uint32_t w, int odd, const uint8_t* tab) {
+  const uint32_t c = odd ? (w >> 16) : (w & 0xFFFFu);
+  const uint32_t base = (c & 0xFFu) << 8;
+  const uint32_t a0 = base | ((c >> 5) & 0x78u);          // nib = flip & 15
+  const uint32_t a1 = base | ((c >> 9) & 0x78u);          // nib = flip >> 4
+  const uint2 lo = *reinterpret_cast<const uint2*>(tab + a0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(tab + 128 + a1);
+  return as_half8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+// The 4 fp16 values T[idx][4*half .. 4*half+3]/4 of pair pr = 2*idx + half,
+// packed as two dwords (from the 4 int8 table entries v).
+__device__ __forceinline__ uint2 cb2_pair_values(const int8_t* v) {
+  uint32_t w[2];
+  for (int p = 0; p < 2; ++p) {
+    const _Float16 lo = (_Float16)((float)v[2 * p] * 0.25f), hi = (_Float16)((float)v[2 * p + 1] * 0.25f);
+    w[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// Entry i of the table from the values of its pair (val = cb2_pair_values).
+__device__ __forceinline__ void cb2_comb_put(uint8_t* tab, int i, uint2 val) {
+  const uint32_t nib = i & 15;
+  const uint32_t m01 = ((nib & 1u) << 15) | ((nib & 2u) << 30);
+  const uint32_t m23 = ((nib & 4u) << 13) | ((nib & 8u) << 28);
+  *reinterpret_cast<uint2*>(tab + (size_t)i * 8) = make_uint2(val.x ^ m01, val.y ^ m23);
+}
+
+// Builds the table with the whole workgroup; val4 is 4 KB of LDS scratch.
+// Contains two barriers.
+__device__ __forceinline__ void cb2_comb_fill(const int8_t* codebook, uint8_t* tab, uint2* val4, int tid,
+                                              int nthreads) {
+  for (int pr = tid; pr < 512; pr += nthreads) {
+    int8_t v[4];
+    for (int i = 0; i < 4; ++i) v[i] = codebook[(pr >> 1) * 8 + 4 * (pr & 1) + i];
+    val4[pr] = cb2_pair_values(v);
+  }
+  __syncthreads();
+  for (int i = tid; i < 512 * 16; i += nthreads) cb2_comb_put(tab, i, val4[i >> 4]);
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // K2: the lane's 16 bytes are 4 words; word kb/2 holds kb.  For even kb the
 // code pair of slot s (weights 2s, 2s+1) sits at bits 2s and 2s+16 (t = s);

@@ -275,10 +275,8 @@ __global__ __launch_bounds__(1024) void dec1_upgate_kernel(DecArgs a) {
 // all compute units while the shared expert's plain bf16 stream keeps HBM
 // busy next to it.
 //
-// Decode table (LDS offset 0, 64 KB): entry (idx, half, nib) at byte
-// ((idx*2 + half)*16 + nib)*8 holds the 4 fp16 values T[idx][4*half+i]/4,
-// negated where bit i of nib is set, so a group of 8 weights is two 8-byte
-// reads addressed straight from its 16-bit code (idx | flip << 8).
+// Decode table: the 64 KB (index, half, sign nibble) table of cb2_comb at
+// LDS offset 0.
 //
 // A operands are block-diagonal: A_kb holds x's k-block kb in row kb, so 8
 // accumulating MFMAs leave the per-block dots C[kb][n] (kb = 4g + i in lane
@@ -289,7 +287,6 @@ __global__ __launch_bounds__(1024) void dec1_upgate_kernel(DecArgs a) {
 // k-block 2p+1, and A_{2p} | A_{2p+1} supplies both activation rows, so one
 // MFMA covers two k-blocks of 8 rows with all 64 lanes loading useful bytes.
 
-constexpr int kCb2CombBytes = 256 * 2 * 16 * 8;
 constexpr int kRedBatch = 8;      // routed row tiles per cross-wave reduction
 constexpr int kPrefetch3 = 3;     // routed row tiles in flight per wave
 
@@ -313,17 +310,6 @@ __device__ __forceinline__ void cb2_pay_load(Cb2Pay& p, const DecArgs& a, int e,
     p.sc[mat][1] = sp.y;
   }
   p.ok = ok;
-}
-
-// Group of 8 weights for k-block kb from the lane's code dword (kb, kb^1).
-__device__ __forceinline__ half8 cb2_comb(uint32_t w, int odd, const uint8_t* tab) {
-  const uint32_t c = odd ? (w >> 16) : (w & 0xFFFFu);
-  const uint32_t base = (c & 0xFFu) << 8;
-  const uint32_t a0 = base | ((c >> 5) & 0x78u);          // nib = flip & 15
-  const uint32_t a1 = base | ((c >> 9) & 0x78u);          // nib = flip >> 4
-  const uint2 lo = *reinterpret_cast<const uint2*>(tab + a0);
-  const uint2 hi = *reinterpret_cast<const uint2*>(tab + 128 + a1);
-  return as_half8(u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
 __device__ __forceinline__ float cb2_scaled(const float4v& c, const uint32_t sc[2], bool ok) {
@@ -403,28 +389,14 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   // into a staging area, then the 16 sign variants of each, written by
   // consecutive lanes to consecutive entries (no bank conflicts)
   uint2* val4 = reinterpret_cast<uint2*>(red_r);          // [512], reuses the reduction area
-  auto put_val4 = [&](int pr, const int8_t* v) {
-    uint32_t w[2];
-    for (int p = 0; p < 2; ++p) {
-      const _Float16 lo = (_Float16)((float)v[2 * p] * 0.25f), hi = (_Float16)((float)v[2 * p + 1] * 0.25f);
-      w[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    val4[pr] = make_uint2(w[0], w[1]);
-  };
-  if (tid < 512) put_val4(tid, cbv);
+  if (tid < 512) val4[tid] = cb2_pair_values(cbv);
   for (int pr = tid + (int)blockDim.x; pr < 512; pr += blockDim.x) {     // workgroups under 512 threads
     int8_t v[4];
     for (int i = 0; i < 4; ++i) v[i] = a.codebook[(pr >> 1) * 8 + 4 * (pr & 1) + i];
-    put_val4(pr, v);
+    val4[pr] = cb2_pair_values(v);
   }
   __syncthreads();
-  for (int i = tid; i < 512 * 16; i += blockDim.x) {
-    const uint2 v = val4[i >> 4];
-    const uint32_t nib = i & 15;
-    const uint32_t m01 = ((nib & 1u) << 15) | ((nib & 2u) << 30);
-    const uint32_t m23 = ((nib & 4u) << 13) | ((nib & 8u) << 28);
-    *reinterpret_cast<uint2*>(tab + (size_t)i * 8) = make_uint2(v.x ^ m01, v.y ^ m23);
-  }
+  for (int i = tid; i < 512 * 16; i += blockDim.x) cb2_comb_put(tab, i, val4[i >> 4]);
   __syncthreads();
 
   const float4v zero = {0.f, 0.f, 0.f, 0.f};

@@ -2,16 +2,20 @@
 // ([blog] server logs: prompts are prefilled in chunks of 2048, cap 8192;
 // [digest] "Model weights": quantized routed experts, bf16 shared expert).
 //
-// A workgroup owns (expert, N-tile of rows) and loops over all of the
-// expert's tokens (positions in moe_group_tokens order), M_TILES*16 at a
-// time.  Each wave owns two 16-row tiles of every weight matrix it touches
-// (up and gate together for the first GEMM), dequantizes its tiles of a
-// K-chunk exactly once into fp16 MFMA B operands in registers -- the
-// quantization scales folded in, one fp16 rounding per weight -- and
-// multiplies them against every M-tile.  Token rows are gathered, converted
-// to fp16 and staged in LDS in MFMA A-operand order, 256 columns at a time.
+// A workgroup owns (expert, N-tile of weight rows) and loops over the
+// expert's tokens (positions in moe_group_tokens order) 96 at a time; the
+// shared expert runs as extra workgroups over 96-token chunks of all tokens.
+// Each wave owns 32 weight rows (two 16-row tiles) per matrix and multiplies
+// them with v_mfma_f32_32x32x16 against up to three 32-token M-tiles: every
+// weight is dequantized once per workgroup pass into an fp16 B operand (the
+// quantization scales folded in, one fp16 rounding per weight) and used by
+// 32 tokens per instruction.  M-tiles past the expert's last token are
+// skipped.  Token rows are gathered into LDS one 256-column K-chunk at a
+// time (bf16 -> fp16 for the quantized experts); the next chunk's rows and
+// weights are loaded into registers while the current chunk is multiplied.
 // fp16 operands with fp32 accumulation keep the layer within the 2e-3
-// tolerance, which bf16 operands do not.
+// tolerance, which bf16 operands do not; the shared expert's up/gate uses
+// bf16 operands directly because both x and its weights are exact in bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,53 +29,160 @@ using qmoe::PfArgs;
 
 namespace {
 
-constexpr int kWaves = 8;     // waves per workgroup
-constexpr int kTilesPerWave = 2;
-constexpr int kRowsPerWg = kWaves * kTilesPerWave * 16;   // 256
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMT = 3;                                   // 32-token M-tiles per pass
+constexpr int kMRows = 32 * kMT;                         // 96 tokens per pass
+constexpr int kUgRowsPerWg = kWaves * 32;                // up/gate: 256 rows of I
+constexpr int kDnTiles = 1;                              // down: 32-row B tiles per wave
+constexpr int kDnRowsPerWg = kWaves * 32 * kDnTiles;     // 256 rows of H
+constexpr int kStageBytes = kMRows * 256 * 2;            // one staged 256-column chunk (48 KB)
+constexpr int kPieces = kMRows * 32 / kThreads;          // 16-byte pieces per thread per chunk (6)
+
+__device__ __forceinline__ float16v mfma32(const half8& a, const half8& b, const float16v& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float16v mfma32_bf(const u32x4& a, const u32x4& b, const float16v& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// Stage rows [m0, m0 + M_TILES*16) x columns [col0, col0 + 256) of a
-// row-major fp16/bf16 source into A-operand order:
-//   byte ((mt*8 + kb)*64 + lane)*16 + 2j holds row 16 mt + lane%16,
-//   column 32 kb + 8 (lane/16) + j.
-// row_of(r) returns the source row of local row r, or -1 for a zero row.
-template <int M_TILES, bool SRC_BF16, typename RowOf>
-__device__ __forceinline__ void stage_a(uint8_t* a_lds, const uint16_t* src, int64_t ld, int col0,
-                                        int col_valid, RowOf row_of) {
-  constexpr int kChunks = M_TILES * 16 * 32;     // 16-byte pieces
-  for (int p = threadIdx.x; p < kChunks; p += blockDim.x) {
-    const int r = p >> 5, piece = p & 31;        // piece = kb*4 + g
-    const int kb = piece >> 2, g = piece & 3;
-    const int col = col0 + kb * 32 + g * 8;
-    const int64_t row = row_of(r);
-    u32x4 v = {0, 0, 0, 0};
-    if (row >= 0 && col < col_valid) {
-      const u32x4 raw = load16(src + row * ld + col);
-      v = SRC_BF16 ? as_u32x4(bf16x8_to_half8(raw)) : raw;
-    }
-    const int mt = r >> 4, lane = g * 16 + (r & 15);
-    *reinterpret_cast<u32x4*>(a_lds + ((mt * 8 + kb) * 64 + lane) * 16) = v;
+// ---------------------------------------------------------------------------
+// A staging.  MFMA 32x32x16: lane l of M-tile mt, 16-column step kk reads the
+// 8 values of row 32 mt + l%32, columns 16 kk + 8 (l/32) .. +7.  In LDS the
+// 16-byte piece (row r, step kk, half hf) sits at slot
+//   (r/32 * 16 + kk) * 64 + 32 hf + ((r%32 + kk) & 31)
+// (a rotation by kk within each half), so that both the row-wise stores of
+// the staging and the MFMA reads are free of bank conflicts.
+__device__ __forceinline__ int a_slot(int r, int kk, int hf) {
+  return ((r >> 5) * 16 + kk) * 64 + 32 * hf + (((r & 31) + kk) & 31);
+}
+__device__ __forceinline__ half8 a_read(const uint8_t* lds, int mt, int kk, int lane) {
+  const int slot = (mt * 16 + kk) * 64 + (lane & 32) + ((lane + kk) & 31);
+  return as_half8(*reinterpret_cast<const u32x4*>(lds + slot * 16));
+}
+
+// Thread tid stages pieces p = tid + kThreads*i: row r = p/32 = tid/32 + 16 i,
+// 8-column group c8 = tid%32.  rows[i] = source row (or -1: zero row).
+struct AStage {
+  u32x4 v[kPieces];
+};
+
+__device__ __forceinline__ void a_load(AStage& st, const uint16_t* src, int64_t ld, const int* rows, int col0,
+                                       int col_valid) {
+  const int col = col0 + 8 * (threadIdx.x & 31);
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i)
+    st.v[i] = (rows[i] >= 0 && col < col_valid) ? load16(src + (int64_t)rows[i] * ld + col) : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <bool BF16_TO_F16>
+__device__ __forceinline__ void a_store(const AStage& st, uint8_t* lds) {
+  const int c8 = threadIdx.x & 31, kk = c8 >> 1, hf = c8 & 1;
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int r = (threadIdx.x >> 5) + 16 * i;
+    const u32x4 v = BF16_TO_F16 ? as_u32x4(bf16x8_to_half8(st.v[i])) : st.v[i];
+    *reinterpret_cast<u32x4*>(lds + a_slot(r, kk, hf) * 16) = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-// B-operand dequantizers for prefill (scale folded in, fp16).
+// B operands.  For a wave's 32 rows starting at weight row-tile rt0 (two
+// 16-row tiles), lane l takes row n = l%16 of tile rt0 + (l%32)/16; in step
+// kk of a chunk it needs the 8 weights (n, kb = kk/2, qq = 2(kk%2) + l/32,
+// j = 0..7), i.e. the group that the tile format keeps at lane c = 16 qq + n.
+// So per chunk a lane loads the data of lanes c = 16 (l/32) + n (even kk) and
+// c = 16 (2 + l/32) + n (odd kk) plus row n's scales.
 
-__device__ __forceinline__ half8 pf_cb2(const u32x4& codes, const u32x4& scl, int kb,
-                                        const uint8_t* val_lane, const uint8_t* flip_lane) {
-  const half8 v = cb2_group((codes[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu, val_lane, flip_lane);
-  const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu));
+struct Cb2B {
+  u32x4 c0, c1, sc;
+};
+struct K4B {
+  u32x4 q[2][2];     // [odd kk][half kb/4]
+  uint32_t s0, s1, s2, dd;
+};
+struct K2B {
+  u32x4 q0, q1, scm;
+  uint32_t dd;
+};
+
+template <int FMT>
+struct BRegs;
+template <>
+struct BRegs<MOE_FMT_CB2> {
+  using T = Cb2B;
+};
+template <>
+struct BRegs<MOE_FMT_K4> {
+  using T = K4B;
+};
+template <>
+struct BRegs<MOE_FMT_K2> {
+  using T = K2B;
+};
+
+__device__ __forceinline__ void b_load(Cb2B& b, const uint8_t* tile, int lane) {
+  const int n = lane & 15, hl = lane >> 5;
+  b.c0 = load16(tile + 16 * (16 * hl + n));
+  b.c1 = load16(tile + 16 * (16 * (2 + hl) + n));
+  b.sc = load16(tile + 1024 + 16 * n);
+}
+__device__ __forceinline__ void b_load(K4B& b, const uint8_t* tile, int lane) {
+  const int n = lane & 15, hl = lane >> 5;
+  for (int v = 0; v < 2; ++v)
+    for (int h = 0; h < 2; ++h) b.q[v][h] = load16(tile + 1024 * h + 16 * (16 * (2 * v + hl) + n));
+  const uint32_t* sp = reinterpret_cast<const uint32_t*>(tile + 2048 + 12 * n);
+  b.s0 = sp[0];
+  b.s1 = sp[1];
+  b.s2 = sp[2];
+  b.dd = *reinterpret_cast<const uint32_t*>(tile + 2240 + 4 * n);
+}
+__device__ __forceinline__ void b_load(K2B& b, const uint8_t* tile, int lane) {
+  const int n = lane & 15, hl = lane >> 5;
+  b.q0 = load16(tile + 16 * (16 * hl + n));
+  b.q1 = load16(tile + 16 * (16 * (2 + hl) + n));
+  b.scm = load16(tile + 1024 + 16 * n);
+  b.dd = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
+}
+
+// CB2: table value * fp16 scale (one rounding).
+__device__ __forceinline__ half8 b_decode(const Cb2B& b, int kk, const uint8_t* tab) {
+  const int kb = kk >> 1;
+  const uint32_t w = (kk & 1) ? b.c1[kb >> 1] : b.c0[kb >> 1];
+  const half8 v = cb2_comb(w, kb & 1, tab);
+  const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)((b.sc[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu));
   return v * s;
 }
 
-// K2 weight of slot s: (magic * 4^-t - 1024 * 4^-t) = q exactly, then
-// q * fp16(d*sc) - fp16(dmin*m).
-__device__ __forceinline__ half8 pf_k2(const u32x4& qw, const u32x4& scm, float d, float dmin, int kb,
-                                       int qq) {
-  const half8 mg = as_half8(k2_magic(qw, kb));
-  const int sb = 2 * kb + (qq >> 1);
-  const uint32_t byte = (scm[sb >> 2] >> (8 * (sb & 3))) & 0xFFu;
+// K4: (magic - 1024) = q exactly, then q * fp16(d*sc) - fp16(dmin*m).
+__device__ __forceinline__ half8 b_decode(const K4B& b, int kk, const uint8_t*) {
+  const int kb = kk >> 1;
+  const uint32_t word = b.q[kk & 1][kb >> 2][kb & 3];
+  const half8 mg = as_half8(k4_magic(word));
+  const float d = h2f(b.dd & 0xFFFFu), dmin = h2f(b.dd >> 16);
+  const _Float16 dsc = (_Float16)(d * (float)k4_scale_value(b.s0, b.s1, b.s2, kb));
+  const _Float16 ndm = (_Float16)(-(dmin * (float)k4_scale_value(b.s0, b.s1, b.s2, 8 + kb)));
+  const _Float16 m1024 = (_Float16)(-1024.0f);
+  half8 w;
+  for (int j = 0; j < 8; ++j) w[j] = (mg[j] + m1024) * dsc + ndm;
+  return w;
+}
+
+// K2: code pair of slot s decodes to 1024*4^-t + q exactly after scaling the
+// magic value by 4^-t; then q * fp16(d*sc) - fp16(dmin*m).  The lane's
+// sub-block is 2 kb + qq/2 = 2 kb + kk%2.
+__device__ __forceinline__ half8 b_decode(const K2B& b, int kk, const uint8_t*) {
+  const int kb = kk >> 1;
+  const half8 mg = as_half8(k2_magic((kk & 1) ? b.q1 : b.q0, kb));
+  const int sb = 2 * kb + (kk & 1);
+  const uint32_t byte = (b.scm[sb >> 2] >> (8 * (sb & 3))) & 0xFFu;
+  const float d = h2f(b.dd & 0xFFFFu), dmin = h2f(b.dd >> 16);
   const _Float16 dsc = (_Float16)(d * (float)(byte & 15u));
   const _Float16 ndm = (_Float16)(-(dmin * (float)(byte >> 4)));
   half8 w;
@@ -87,273 +198,378 @@ __device__ __forceinline__ half8 pf_k2(const u32x4& qw, const u32x4& scm, float 
   return w;
 }
 
-__device__ __forceinline__ half8 pf_k4(uint32_t word, float d, float dmin, uint32_t sc, uint32_t mn) {
-  const half8 mg = as_half8(k4_magic(word));
-  const _Float16 dsc = (_Float16)(d * (float)sc);
-  const _Float16 ndm = (_Float16)(-(dmin * (float)mn));
-  const _Float16 m1024 = (_Float16)(-1024.0f);
-  half8 w;
-  for (int j = 0; j < 8; ++j) w[j] = (mg[j] + m1024) * dsc + ndm;
-  return w;
+// BF16 tiles: the lane's 16 bytes for step kk (raw bf16).
+__device__ __forceinline__ u32x4 bf16_piece(const uint8_t* tile, int kk, int lane) {
+  const int n = lane & 15, hl = lane >> 5, kb = kk >> 1, qq = 2 * (kk & 1) + hl;
+  return load16(tile + 1024 * kb + 16 * (16 * qq + n));
 }
 
-// Per-lane state of one weight tile for one K-chunk (enough to produce the
-// B operand of every kb).
-struct TileRegs {
-  u32x4 a, b;        // CB2: codes, scales | K2: q words, sc/m | K4: q halves 0/1
-  uint32_t s0, s1, s2, dd;
-};
+__device__ __forceinline__ float16v zero16v() {
+  float16v z;
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
 
-template <int FMT>
-__device__ __forceinline__ TileRegs load_tile(const uint8_t* tile, int lane) {
-  TileRegs r;
-  const int n = lane & 15;
-  if (FMT == MOE_FMT_CB2) {
-    r.a = load16(tile + 16 * lane);
-    r.b = load16(tile + 1024 + 16 * n);
-  } else if (FMT == MOE_FMT_K2) {
-    r.a = load16(tile + 16 * lane);
-    r.b = load16(tile + 1024 + 16 * n);
-    r.dd = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
-  } else if (FMT == MOE_FMT_K4) {
-    r.a = load16(tile + 16 * lane);
-    r.b = load16(tile + 1024 + 16 * lane);
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(tile + 2048 + 12 * n);
-    r.s0 = sp[0];
-    r.s1 = sp[1];
-    r.s2 = sp[2];
-    r.dd = *reinterpret_cast<const uint32_t*>(tile + 2240 + 4 * n);
+// Rows of this thread's staging pieces for the pass starting at m0.
+template <typename RowOf>
+__device__ __forceinline__ void stage_rows(int* rows, int64_t m0, int64_t p_end, RowOf row_of) {
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int64_t p = m0 + (threadIdx.x >> 5) + 16 * i;
+    rows[i] = p < p_end ? (int)row_of(p) : -1;
   }
-  return r;
-}
-
-template <int FMT>
-__device__ __forceinline__ half8 tile_b(const TileRegs& r, const uint8_t* tile, int kb, int lane,
-                                        const uint8_t* val_lane, const uint8_t* flip_lane) {
-  if (FMT == MOE_FMT_CB2) return pf_cb2(r.a, r.b, kb, val_lane, flip_lane);
-  if (FMT == MOE_FMT_K2) return pf_k2(r.a, r.b, h2f(r.dd & 0xFFFFu), h2f(r.dd >> 16), kb, lane >> 4);
-  if (FMT == MOE_FMT_K4)
-    return pf_k4(kb < 4 ? r.a[kb & 3] : r.b[kb & 3], h2f(r.dd & 0xFFFFu), h2f(r.dd >> 16),
-                 k4_scale_value(r.s0, r.s1, r.s2, kb), k4_scale_value(r.s0, r.s1, r.s2, 8 + kb));
-  return bf16x8_to_half8(load16(tile + 1024 * kb + 16 * lane));   // BF16
 }
 
 // ---------------------------------------------------------------------------
-// Up/gate.  blockIdx.x = N-tile (256 rows of I), blockIdx.y < E: routed
-// expert; blockIdx.y >= E: shared-expert M-chunk blockIdx.y - E.
+// Up/gate, routed experts (CB2 or K4).  blockIdx.x = 256-row N-tile of I.
 
-template <int FMT, int M_TILES>
-__global__ __launch_bounds__(512) void pf_upgate_kernel(PfArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* a_lds = smem;                                   // M_TILES * 8 KB
-  uint8_t* val_tab = smem + M_TILES * 8192;
-  uint8_t* flip_tab = val_tab + kCb2TableBytes;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool shared = blockIdx.y >= (unsigned)a.E;
-  const int e = (int)blockIdx.y;
-  int64_t p_begin, p_end;
-  if (shared) {
-    p_begin = (int64_t)(blockIdx.y - a.E) * M_TILES * 16;
-    p_end = min((int64_t)a.T, p_begin + M_TILES * 16);
-  } else {
-    p_begin = a.offsets[e];
-    p_end = a.offsets[e + 1];
-  }
+template <int FMT>
+__device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e) {
+  const int64_t p_begin = a.offsets[e], p_end = a.offsets[e + 1];
   if (p_begin >= p_end) return;
-  const int rows_total = shared ? a.Is : a.I;
-  const int n_rt = rows_total / 16;
-  const int rt0 = blockIdx.x * (kRowsPerWg / 16) + wave * kTilesPerWave;
-  if (blockIdx.x * kRowsPerWg >= rows_total) return;
-  if (!shared && FMT == MOE_FMT_CB2) {
-    cb2_fill_tables(a.codebook, val_tab, flip_tab, tid, blockDim.x);
-  }
-  const uint8_t* val_lane = val_tab + (lane & 7) * 16;
-  const uint8_t* flip_lane = flip_tab + (lane & 7) * 16;
-  const int n_chunks = a.H / 256;
-  const int tb = shared ? kBf16Tile : (FMT == MOE_FMT_CB2 ? kCb2Tile : kK4Tile);
-  const uint8_t* base_u = shared ? a.sup : a.up + (size_t)e * a.expert_bytes;
-  const uint8_t* base_g = shared ? a.sgate : a.gate + (size_t)e * a.expert_bytes;
-  const int k = a.k;
-  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t* tab = smem;                                                 // CB2 table at offset 0
+  uint8_t* a_lds = smem + (FMT == MOE_FMT_CB2 ? kCb2CombBytes : 0);
+  if (FMT == MOE_FMT_CB2) cb2_comb_fill(a.codebook, tab, reinterpret_cast<uint2*>(a_lds), tid, blockDim.x);
+  const int n_rt = a.I / 16, n_chunks = a.H / 256, k = a.k;
+  const int rt0 = (blockIdx.x * kUgRowsPerWg + wave * 32) / 16;
+  const bool active = rt0 < n_rt;
+  const int rt_l = min(rt0 + ((lane & 31) >> 4), n_rt - 1);            // clamped: loads stay in the matrix
+  const int tb = FMT == MOE_FMT_CB2 ? kCb2Tile : kK4Tile;
+  const uint8_t* tu = a.up + (size_t)e * a.expert_bytes + (size_t)rt_l * n_chunks * tb;
+  const uint8_t* tg = a.gate + (size_t)e * a.expert_bytes + (size_t)rt_l * n_chunks * tb;
+  using B = typename BRegs<FMT>::T;
 
-  for (int64_t m0 = p_begin; m0 < p_end; m0 += M_TILES * 16) {
-    float4v acc[2][kTilesPerWave][M_TILES];
-    for (int mat = 0; mat < 2; ++mat)
-      for (int t = 0; t < kTilesPerWave; ++t)
-        for (int mt = 0; mt < M_TILES; ++mt) acc[mat][t][mt] = zero;
+  for (int64_t m0 = p_begin; m0 < p_end; m0 += kMRows) {
+    const int mta = (int)min((int64_t)kMT, (p_end - m0 + 31) / 32);
+    int rows[kPieces];
+    stage_rows(rows, m0, p_end, [&](int64_t p) { return (int64_t)(a.sorted_slots[p] / k); });
+    float16v acc[2][kMT];
+    for (int mt = 0; mt < kMT; ++mt) acc[0][mt] = acc[1][mt] = zero16v();
+    AStage st;
+    B cu, cg, nu, ng;
+    a_load(st, a.x, a.H, rows, 0, a.H);
+    b_load(cu, tu, lane);
+    b_load(cg, tg, lane);
     for (int chunk = 0; chunk < n_chunks; ++chunk) {
       __syncthreads();
-      stage_a<M_TILES, true>(a_lds, a.x, a.H, chunk * 256, a.H, [&](int r) -> int64_t {
-        const int64_t p = m0 + r;
-        if (p >= p_end) return -1;
-        return shared ? p : (int64_t)(a.sorted_slots[p] / k);
-      });
+      a_store<true>(st, a_lds);
       __syncthreads();
-      TileRegs tr[2][kTilesPerWave];
-      const uint8_t* tp[2][kTilesPerWave];
-      for (int mat = 0; mat < 2; ++mat)
-        for (int t = 0; t < kTilesPerWave; ++t) {
-          const int rt = min(rt0 + t, n_rt - 1);
-          tp[mat][t] = (mat ? base_g : base_u) + ((size_t)rt * n_chunks + chunk) * tb;
-          if (shared) tr[mat][t] = load_tile<MOE_FMT_BF16>(tp[mat][t], lane);
-          else tr[mat][t] = load_tile<FMT>(tp[mat][t], lane);
-        }
-      for (int kb = 0; kb < 8; ++kb) {
-        half8 b[2][kTilesPerWave];
-        for (int mat = 0; mat < 2; ++mat)
-          for (int t = 0; t < kTilesPerWave; ++t)
-            b[mat][t] = shared ? tile_b<MOE_FMT_BF16>(tr[mat][t], tp[mat][t], kb, lane, val_lane, flip_lane)
-                               : tile_b<FMT>(tr[mat][t], tp[mat][t], kb, lane, val_lane, flip_lane);
-        for (int mt = 0; mt < M_TILES; ++mt) {
-          const half8 av = as_half8(*reinterpret_cast<const u32x4*>(a_lds + ((mt * 8 + kb) * 64 + lane) * 16));
-          for (int mat = 0; mat < 2; ++mat)
-            for (int t = 0; t < kTilesPerWave; ++t) acc[mat][t][mt] = mfma_f16(av, b[mat][t], acc[mat][t][mt]);
+      if (chunk + 1 < n_chunks) {
+        a_load(st, a.x, a.H, rows, (chunk + 1) * 256, a.H);
+        b_load(nu, tu + (size_t)(chunk + 1) * tb, lane);
+        b_load(ng, tg + (size_t)(chunk + 1) * tb, lane);
+      }
+      if (active) {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const half8 bu = b_decode(cu, kk, tab), bg = b_decode(cg, kk, tab);
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt)
+            if (mt < mta) {
+              const half8 av = a_read(a_lds, mt, kk, lane);
+              acc[0][mt] = mfma32(av, bu, acc[0][mt]);
+              acc[1][mt] = mfma32(av, bg, acc[1][mt]);
+            }
         }
       }
+      cu = nu;
+      cg = ng;
     }
-    // epilogue: h = SiLU(g) * u for C[m = 4(lane/16) + i][n = lane%16]
-    for (int t = 0; t < kTilesPerWave; ++t) {
-      const int rt = rt0 + t;
-      if (rt >= n_rt) continue;
-      const int row = rt * 16 + (lane & 15);
-      for (int mt = 0; mt < M_TILES; ++mt)
-        for (int i = 0; i < 4; ++i) {
-          const int64_t p = m0 + mt * 16 + 4 * (lane >> 4) + i;
-          if (p >= p_end) continue;
-          const _Float16 hv = (_Float16)(silu(acc[1][t][mt][i]) * acc[0][t][mt][i]);
-          if (shared) a.hs[p * a.Is + row] = hv;
-          else a.h[p * a.I + row] = hv;
+    // epilogue: C[m][n], m = 8(i/4) + 4(l/32) + i%4, n = l%32
+    const int row = rt0 * 16 + (lane & 31);
+    if (active && row < a.I)
+      for (int mt = 0; mt < kMT; ++mt)
+        for (int i = 0; i < 16; ++i) {
+          const int64_t p = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (p < p_end) a.h[p * a.I + row] = (_Float16)(silu(acc[1][mt][i]) * acc[0][mt][i]);
         }
+  }
+}
+
+// Up/gate, shared expert (bf16 x bf16 on bf16 matrix cores).  blockIdx.y - E
+// = 96-token chunk.  Weights stream a quarter chunk (4 steps) at a time, the
+// next quarter's loads in flight during the current one.
+__device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc) {
+  const int64_t p_begin = (int64_t)mc * kMRows, p_end = min((int64_t)a.T, p_begin + kMRows);
+  if (p_begin >= p_end) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t* a_lds = smem;
+  const int n_rt = a.Is / 16, n_chunks = a.H / 256;
+  const int rt0 = (blockIdx.x * kUgRowsPerWg + wave * 32) / 16;
+  const bool active = rt0 < n_rt;
+  const int rt_l = min(rt0 + ((lane & 31) >> 4), n_rt - 1);
+  const uint8_t* tu = a.sup + (size_t)rt_l * n_chunks * kBf16Tile;
+  const uint8_t* tg = a.sgate + (size_t)rt_l * n_chunks * kBf16Tile;
+  const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
+  int rows[kPieces];
+  stage_rows(rows, p_begin, p_end, [](int64_t p) { return p; });
+  float16v acc[2][kMT];
+  for (int mt = 0; mt < kMT; ++mt) acc[0][mt] = acc[1][mt] = zero16v();
+  AStage st;
+  a_load(st, a.x, a.H, rows, 0, a.H);
+  u32x4 cu[4], cg[4], nu[4], ng[4];
+  for (int q = 0; q < 4; ++q) {
+    cu[q] = bf16_piece(tu, q, lane);
+    cg[q] = bf16_piece(tg, q, lane);
+  }
+  const int n_quarters = 4 * n_chunks;
+  for (int gq = 0; gq < n_quarters; ++gq) {
+    const int chunk = gq >> 2, q0 = 4 * (gq & 3);
+    if ((gq & 3) == 0) {
+      __syncthreads();
+      a_store<false>(st, a_lds);
+      __syncthreads();
+      if (chunk + 1 < n_chunks) a_load(st, a.x, a.H, rows, (chunk + 1) * 256, a.H);
     }
+    if (gq + 1 < n_quarters) {
+      const int c1 = (gq + 1) >> 2, k1 = 4 * ((gq + 1) & 3);
+      for (int q = 0; q < 4; ++q) {
+        nu[q] = bf16_piece(tu + (size_t)c1 * kBf16Tile, k1 + q, lane);
+        ng[q] = bf16_piece(tg + (size_t)c1 * kBf16Tile, k1 + q, lane);
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+          if (mt < mta) {
+            const u32x4 av = as_u32x4(a_read(a_lds, mt, q0 + q, lane));
+            acc[0][mt] = mfma32_bf(av, cu[q], acc[0][mt]);
+            acc[1][mt] = mfma32_bf(av, cg[q], acc[1][mt]);
+          }
+    }
+    for (int q = 0; q < 4; ++q) {
+      cu[q] = nu[q];
+      cg[q] = ng[q];
+    }
+  }
+  const int row = rt0 * 16 + (lane & 31);
+  if (active && row < a.Is)
+    for (int mt = 0; mt < kMT; ++mt)
+      for (int i = 0; i < 16; ++i) {
+        const int64_t p = p_begin + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (p < p_end) a.hs[p * a.Is + row] = (_Float16)(silu(acc[1][mt][i]) * acc[0][mt][i]);
+      }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void pf_upgate_kernel(PfArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if (blockIdx.y < (unsigned)a.E) {
+    if ((int)blockIdx.x * kUgRowsPerWg >= a.I) return;
+    ug_routed<FMT>(a, smem, (int)blockIdx.y);
+  } else {
+    if ((int)blockIdx.x * kUgRowsPerWg >= a.Is) return;
+    ug_shared(a, smem, (int)blockIdx.y - a.E);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Down.  blockIdx.x = N-tile (256 rows of H); blockIdx.y as for up/gate.
+// Down.  blockIdx.x = 256-row N-tile of H (one 32-row B tile per wave).
 // Routed outputs go to yslot[position], shared outputs to ysh[token].
 
-template <int FMT, int M_TILES>
-__global__ __launch_bounds__(512) void pf_down_kernel(PfArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* a_lds = smem;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool shared = blockIdx.y >= (unsigned)a.E;
-  const int e = (int)blockIdx.y;
-  int64_t p_begin, p_end;
-  if (shared) {
-    p_begin = (int64_t)(blockIdx.y - a.E) * M_TILES * 16;
-    p_end = min((int64_t)a.T, p_begin + M_TILES * 16);
-  } else {
-    p_begin = a.offsets[e];
-    p_end = a.offsets[e + 1];
-  }
+template <int FMT>
+__device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e) {
+  const int64_t p_begin = a.offsets[e], p_end = a.offsets[e + 1];
   if (p_begin >= p_end) return;
-  const int n_rt = a.H / 16;
-  const int rt0 = blockIdx.x * (kRowsPerWg / 16) + wave * kTilesPerWave;
-  const int Kvalid = shared ? a.Is : a.I;
-  const int n_chunks = (shared ? a.Is_pad : a.I_pad) / 256;
-  const int tb = shared ? kBf16Tile : (FMT == MOE_FMT_K2 ? kK2Tile : kK4Tile);
-  const uint8_t* base = shared ? a.sdown : a.down + (size_t)e * a.expert_bytes_down;
-  const uint16_t* src = reinterpret_cast<const uint16_t*>(shared ? a.hs : a.h);
-  const int64_t ld = Kvalid;
-  const float4v zero = {0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t m0 = p_begin; m0 < p_end; m0 += M_TILES * 16) {
-    float4v acc[kTilesPerWave][M_TILES];
-    for (int t = 0; t < kTilesPerWave; ++t)
-      for (int mt = 0; mt < M_TILES; ++mt) acc[t][mt] = zero;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t* a_lds = smem;
+  const int n_rt = a.H / 16, n_chunks = a.I_pad / 256;
+  const int tb = FMT == MOE_FMT_K2 ? kK2Tile : kK4Tile;
+  int rt0[kDnTiles];
+  const uint8_t* tp[kDnTiles];
+  for (int b = 0; b < kDnTiles; ++b) {
+    rt0[b] = (blockIdx.x * kDnRowsPerWg + wave * 32 * kDnTiles + 32 * b) / 16;
+    const int rt_l = min(rt0[b] + ((lane & 31) >> 4), n_rt - 1);
+    tp[b] = a.down + (size_t)e * a.expert_bytes_down + (size_t)rt_l * n_chunks * tb;
+  }
+  using B = typename BRegs<FMT>::T;
+  for (int64_t m0 = p_begin; m0 < p_end; m0 += kMRows) {
+    const int mta = (int)min((int64_t)kMT, (p_end - m0 + 31) / 32);
+    int rows[kPieces];
+    stage_rows(rows, m0, p_end, [](int64_t p) { return p; });
+    float16v acc[kDnTiles][kMT];
+    for (int b = 0; b < kDnTiles; ++b)
+      for (int mt = 0; mt < kMT; ++mt) acc[b][mt] = zero16v();
+    AStage st;
+    B cur[kDnTiles], nxt[kDnTiles];
+    a_load(st, reinterpret_cast<const uint16_t*>(a.h), a.I, rows, 0, a.I);
+    for (int b = 0; b < kDnTiles; ++b) b_load(cur[b], tp[b], lane);
     for (int chunk = 0; chunk < n_chunks; ++chunk) {
       __syncthreads();
-      stage_a<M_TILES, false>(a_lds, src, ld, chunk * 256, Kvalid, [&](int r) -> int64_t {
-        const int64_t p = m0 + r;
-        return p < p_end ? p : -1;
-      });
+      a_store<false>(st, a_lds);
       __syncthreads();
-      TileRegs tr[kTilesPerWave];
-      const uint8_t* tp[kTilesPerWave];
-      for (int t = 0; t < kTilesPerWave; ++t) {
-        const int rt = min(rt0 + t, n_rt - 1);
-        tp[t] = base + ((size_t)rt * n_chunks + chunk) * tb;
-        tr[t] = shared ? load_tile<MOE_FMT_BF16>(tp[t], lane) : load_tile<FMT>(tp[t], lane);
+      if (chunk + 1 < n_chunks) {
+        a_load(st, reinterpret_cast<const uint16_t*>(a.h), a.I, rows, (chunk + 1) * 256, a.I);
+        for (int b = 0; b < kDnTiles; ++b) b_load(nxt[b], tp[b] + (size_t)(chunk + 1) * tb, lane);
       }
-      for (int kb = 0; kb < 8; ++kb) {
-        half8 b[kTilesPerWave];
-        for (int t = 0; t < kTilesPerWave; ++t)
-          b[t] = shared ? tile_b<MOE_FMT_BF16>(tr[t], tp[t], kb, lane, nullptr, nullptr)
-                        : tile_b<FMT>(tr[t], tp[t], kb, lane, nullptr, nullptr);
-        for (int mt = 0; mt < M_TILES; ++mt) {
-          const half8 av = as_half8(*reinterpret_cast<const u32x4*>(a_lds + ((mt * 8 + kb) * 64 + lane) * 16));
-          for (int t = 0; t < kTilesPerWave; ++t) acc[t][mt] = mfma_f16(av, b[t], acc[t][mt]);
-        }
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        half8 bw[kDnTiles];
+        for (int b = 0; b < kDnTiles; ++b) bw[b] = b_decode(cur[b], kk, nullptr);
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+          if (mt < mta) {
+            const half8 av = a_read(a_lds, mt, kk, lane);
+            for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
+          }
       }
+      for (int b = 0; b < kDnTiles; ++b) cur[b] = nxt[b];
     }
-    for (int t = 0; t < kTilesPerWave; ++t) {
-      const int rt = rt0 + t;
-      if (rt >= n_rt) continue;
-      const int row = rt * 16 + (lane & 15);
-      for (int mt = 0; mt < M_TILES; ++mt)
-        for (int i = 0; i < 4; ++i) {
-          const int64_t p = m0 + mt * 16 + 4 * (lane >> 4) + i;
-          if (p >= p_end) continue;
-          if (shared) a.ysh[p * a.H + row] = acc[t][mt][i];
-          else a.yslot[p * a.H + row] = acc[t][mt][i];
+    for (int b = 0; b < kDnTiles; ++b) {
+      const int row = rt0[b] * 16 + (lane & 31);
+      if (row >= a.H) continue;
+      for (int mt = 0; mt < kMT; ++mt)
+        for (int i = 0; i < 16; ++i) {
+          const int64_t p = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (p < p_end) a.yslot[p * a.H + row] = acc[b][mt][i];
         }
     }
   }
 }
 
-// y[t][h] = sum_j w[t][j] * yslot[slot_pos[t*k + j]][h] + ysh[t][h].
-__global__ void pf_combine_kernel(const float* yslot, const float* ysh, const int32_t* slot_pos,
-                                  const float* topk_w, int T, int k, int H, float* y) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)T * H) return;
-  const int t = (int)(i / H), h = (int)(i % H);
-  float acc = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int p = slot_pos[t * k + j];
-    if (p < 0) continue;
-    acc += topk_w[t * k + j] * yslot[(size_t)p * H + h];
+// Shared expert down: hs (fp16) x bf16 weights converted to fp16 in
+// registers, weights streamed a quarter chunk at a time.
+__device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc) {
+  const int64_t p_begin = (int64_t)mc * kMRows, p_end = min((int64_t)a.T, p_begin + kMRows);
+  if (p_begin >= p_end) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t* a_lds = smem;
+  const int n_rt = a.H / 16, n_chunks = a.Is_pad / 256;
+  int rt0[kDnTiles];
+  const uint8_t* tp[kDnTiles];
+  for (int b = 0; b < kDnTiles; ++b) {
+    rt0[b] = (blockIdx.x * kDnRowsPerWg + wave * 32 * kDnTiles + 32 * b) / 16;
+    const int rt_l = min(rt0[b] + ((lane & 31) >> 4), n_rt - 1);
+    tp[b] = a.sdown + (size_t)rt_l * n_chunks * kBf16Tile;
   }
-  if (ysh) acc += ysh[(size_t)t * H + h];
-  y[i] = acc;
+  const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
+  int rows[kPieces];
+  stage_rows(rows, p_begin, p_end, [](int64_t p) { return p; });
+  float16v acc[kDnTiles][kMT];
+  for (int b = 0; b < kDnTiles; ++b)
+    for (int mt = 0; mt < kMT; ++mt) acc[b][mt] = zero16v();
+  AStage st;
+  a_load(st, reinterpret_cast<const uint16_t*>(a.hs), a.Is, rows, 0, a.Is);
+  u32x4 cw[kDnTiles][4], nw[kDnTiles][4];
+  for (int b = 0; b < kDnTiles; ++b)
+    for (int q = 0; q < 4; ++q) cw[b][q] = bf16_piece(tp[b], q, lane);
+  const int n_quarters = 4 * n_chunks;
+  for (int gq = 0; gq < n_quarters; ++gq) {
+    const int chunk = gq >> 2, q0 = 4 * (gq & 3);
+    if ((gq & 3) == 0) {
+      __syncthreads();
+      a_store<false>(st, a_lds);
+      __syncthreads();
+      if (chunk + 1 < n_chunks)
+        a_load(st, reinterpret_cast<const uint16_t*>(a.hs), a.Is, rows, (chunk + 1) * 256, a.Is);
+    }
+    if (gq + 1 < n_quarters) {
+      const int c1 = (gq + 1) >> 2, k1 = 4 * ((gq + 1) & 3);
+      for (int b = 0; b < kDnTiles; ++b)
+        for (int q = 0; q < 4; ++q) nw[b][q] = bf16_piece(tp[b] + (size_t)c1 * kBf16Tile, k1 + q, lane);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      half8 bw[kDnTiles];
+      for (int b = 0; b < kDnTiles; ++b) bw[b] = bf16x8_to_half8(cw[b][q]);
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+        if (mt < mta) {
+          const half8 av = a_read(a_lds, mt, q0 + q, lane);
+          for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
+        }
+    }
+    for (int b = 0; b < kDnTiles; ++b)
+      for (int q = 0; q < 4; ++q) cw[b][q] = nw[b][q];
+  }
+  for (int b = 0; b < kDnTiles; ++b) {
+    const int row = rt0[b] * 16 + (lane & 31);
+    if (row >= a.H) continue;
+    for (int mt = 0; mt < kMT; ++mt)
+      for (int i = 0; i < 16; ++i) {
+        const int64_t p = p_begin + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (p < p_end) a.ysh[p * a.H + row] = acc[b][mt][i];
+      }
+  }
 }
 
-constexpr int kMTiles = 6;
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void pf_down_kernel(PfArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if ((int)blockIdx.x * kDnRowsPerWg >= a.H) return;
+  if (blockIdx.y < (unsigned)a.E) dn_routed<FMT>(a, smem, (int)blockIdx.y);
+  else dn_shared(a, smem, (int)blockIdx.y - a.E);
+}
+
+// y[t][h] = sum_j w[t][j] * yslot[slot_pos[t*k + j]][h] + ysh[t][h], summed in
+// j order.  One workgroup per token; each thread takes 4 consecutive h and
+// issues the loads of all k slots before summing.
+constexpr int kMaxK = 16;
+
+__global__ __launch_bounds__(256) void pf_combine_kernel(const float* yslot, const float* ysh,
+                                                         const int32_t* slot_pos, const float* topk_w, int T,
+                                                         int k, int H, float* y) {
+  const int t = blockIdx.x;
+  int pos[kMaxK];
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    pos[j] = j < k ? slot_pos[(size_t)t * k + j] : -1;
+    wj[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
+  }
+  for (int h = 4 * threadIdx.x; h < H; h += 4 * blockDim.x) {
+    float4v v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      v[j] = pos[j] >= 0 ? *reinterpret_cast<const float4v*>(yslot + (size_t)pos[j] * H + h)
+                         : float4v{0.f, 0.f, 0.f, 0.f};
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (pos[j] >= 0)
+        for (int q = 0; q < 4; ++q) acc[q] += wj[j] * v[j][q];
+    if (ysh) {
+      const float4v sv = *reinterpret_cast<const float4v*>(ysh + (size_t)t * H + h);
+      for (int q = 0; q < 4; ++q) acc[q] += sv[q];
+    }
+    *reinterpret_cast<float4v*>(y + (size_t)t * H + h) = acc;
+  }
+}
 
 }  // namespace
 
 namespace qmoe {
 
-int pf_m_rows() { return kMTiles * 16; }
+int pf_m_rows() { return kMRows; }
 
 hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,
                           hipStream_t s) {
-  const int n_sh_chunks = a.Is > 0 ? (a.T + kMTiles * 16 - 1) / (kMTiles * 16) : 0;
-  const dim3 block(64 * kWaves);
+  const int n_sh = a.Is > 0 ? (a.T + kMRows - 1) / kMRows : 0;
+  const dim3 block(kThreads);
   {
     const int rows = a.Is > a.I ? a.Is : a.I;
-    const dim3 grid((rows + kRowsPerWg - 1) / kRowsPerWg, a.E + n_sh_chunks);
-    const size_t lds = kMTiles * 8192 + 2 * kCb2TableBytes;
-    void (*fn)(PfArgs) = fmt_ug == MOE_FMT_CB2 ? pf_upgate_kernel<MOE_FMT_CB2, kMTiles>
-                                               : pf_upgate_kernel<MOE_FMT_K4, kMTiles>;
+    const dim3 grid((rows + kUgRowsPerWg - 1) / kUgRowsPerWg, a.E + n_sh);
+    const size_t lds = (fmt_ug == MOE_FMT_CB2 ? kCb2CombBytes : 0) + kStageBytes;
+    void (*fn)(PfArgs) = fmt_ug == MOE_FMT_CB2 ? pf_upgate_kernel<MOE_FMT_CB2> : pf_upgate_kernel<MOE_FMT_K4>;
     hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
     err = launch_timed(MOE_KERNEL_PREFILL_UPGATE, s, [&] { hipLaunchKernelGGL(fn, grid, block, lds, s, a); });
     if (err != hipSuccess) return err;
   }
   {
-    const dim3 grid((a.H + kRowsPerWg - 1) / kRowsPerWg, a.E + n_sh_chunks);
-    const size_t lds = kMTiles * 8192;
-    void (*fn)(PfArgs) = fmt_dn == MOE_FMT_K2 ? pf_down_kernel<MOE_FMT_K2, kMTiles>
-                                              : pf_down_kernel<MOE_FMT_K4, kMTiles>;
+    const dim3 grid((a.H + kDnRowsPerWg - 1) / kDnRowsPerWg, a.E + n_sh);
+    void (*fn)(PfArgs) = fmt_dn == MOE_FMT_K2 ? pf_down_kernel<MOE_FMT_K2> : pf_down_kernel<MOE_FMT_K4>;
     hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
-    err = launch_timed(MOE_KERNEL_PREFILL_DOWN, s, [&] { hipLaunchKernelGGL(fn, grid, block, lds, s, a); });
+    err = launch_timed(MOE_KERNEL_PREFILL_DOWN, s,
+                       [&] { hipLaunchKernelGGL(fn, grid, block, (size_t)kStageBytes, s, a); });
     if (err != hipSuccess) return err;
   }
-  const int64_t n = (int64_t)a.T * a.H;
   return launch_timed(MOE_KERNEL_PREFILL_COMBINE, s, [&] {
-    hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.yslot,
+    hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)a.T), dim3(256), 0, s, a.yslot,
                        a.Is > 0 ? a.ysh : nullptr, a.slot_pos, topk_w, a.T, a.k, a.H, y);
   });
 }

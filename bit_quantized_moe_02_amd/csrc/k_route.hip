@@ -59,41 +59,73 @@ __global__ __launch_bounds__(256) void logits_small_kernel(const uint16_t* x, co
   }
 }
 
-// Many tokens: 64 tokens x 64 experts per workgroup, fp32 FMA on 4x4
-// register tiles, K staged through LDS 32 columns at a time.
+// Many tokens: fp32 matrix cores (v_mfma_f32_16x16x4_f32).  A workgroup of
+// 4 waves computes 64 tokens x 32 experts; wave w takes tokens 16w..16w+15
+// against two 16-expert tiles.  K is staged through LDS 64 columns at a time
+// (x converted bf16 -> fp32 exactly), the next chunk's loads in flight while
+// the current one is multiplied.
+constexpr int kLgT = 64, kLgE = 32, kLgK = 64;
+
+__device__ __forceinline__ float4v mfma_f32x4(float a, float b, const float4v& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(256) void logits_tiled_kernel(const uint16_t* x, const float* wr,
                                                            const float* bias, int T, int H, int E,
                                                            float* logits) {
-  __shared__ float xs[32][65];
-  __shared__ float ws[32][65];
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
-  float acc[4][4];
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    for (int i = tid; i < 64 * 32; i += 256) {
-      const int r = i >> 5, c = i & 31;
-      const int t = t0 + r, e = e0 + r, kk = k0 + c;
-      xs[c][r] = (t < T && kk < H) ? bf2f(x[(size_t)t * H + kk]) : 0.f;
-      ws[c][r] = (e < E && kk < H) ? wr[(size_t)e * H + kk] : 0.f;
+  __shared__ float xs[kLgT][kLgK + 1];
+  __shared__ float ws[kLgE][kLgK + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.y * kLgT, e0 = blockIdx.x * kLgE;
+  // loads of one chunk: x 64 rows x 8 pieces of 8 bf16, w 32 rows x 16 pieces of 4 fp32
+  u32x4 xr[2], wv[2];
+  auto load_chunk = [&](int k0) {
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + 256 * i;
+      const int r = p >> 3, c = k0 + (p & 7) * 8;
+      xr[i] = (t0 + r < T && c < H) ? load16(x + (size_t)(t0 + r) * H + c) : u32x4{0u, 0u, 0u, 0u};
+      const int re = p >> 4, ce = k0 + (p & 15) * 4;
+      wv[i] = (e0 + re < E && ce < H) ? load16(wr + (size_t)(e0 + re) * H + ce) : u32x4{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
-    for (int c = 0; c < 32; ++c) {
-      float xa[4], wb[4];
-      for (int i = 0; i < 4; ++i) xa[i] = xs[c][4 * ty + i];
-      for (int j = 0; j < 4; ++j) wb[j] = ws[c][4 * tx + j];
-      for (int i = 0; i < 4; ++i)
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], wb[j], acc[i][j]);
+  };
+  auto store_chunk = [&]() {
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + 256 * i;
+      const int r = p >> 3, c = (p & 7) * 8;
+      for (int q = 0; q < 4; ++q) {
+        xs[r][c + 2 * q] = bf2f(xr[i][q] & 0xFFFFu);
+        xs[r][c + 2 * q + 1] = bf2f(xr[i][q] >> 16);
+      }
+      const int re = p >> 4, ce = (p & 15) * 4;
+      // (bit-cast the whole vector: a bit-cast of a vector element here read
+      // element 0 for every element)
+      const float4v f = __builtin_bit_cast(float4v, wv[i]);
+      for (int q = 0; q < 4; ++q) ws[re][ce + q] = f[q];
     }
+  };
+  float4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  load_chunk(0);
+  for (int k0 = 0; k0 < H; k0 += kLgK) {
     __syncthreads();
+    store_chunk();
+    __syncthreads();
+    if (k0 + kLgK < H) load_chunk(k0 + kLgK);
+    const int kq = lane >> 4, ri = lane & 15;
+#pragma unroll 4
+    for (int ks = 0; ks < kLgK / 4; ++ks) {
+      const float av = xs[16 * wave + ri][4 * ks + kq];
+      acc0 = mfma_f32x4(av, ws[ri][4 * ks + kq], acc0);
+      acc1 = mfma_f32x4(av, ws[16 + ri][4 * ks + kq], acc1);
+    }
   }
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j) {
-      const int t = t0 + 4 * ty + i, e = e0 + 4 * tx + j;
-      if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
-    }
+  // C[4(lane/16) + i][lane%16]: token row, expert column
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 16 * wave + 4 * (lane >> 4) + i;
+    if (t >= T) continue;
+    const int ea = e0 + (lane & 15), eb = e0 + 16 + (lane & 15);
+    if (ea < E) logits[(size_t)t * E + ea] = acc0[i] + (bias ? bias[ea] : 0.f);
+    if (eb < E) logits[(size_t)t * E + eb] = acc1[i] + (bias ? bias[eb] : 0.f);
+  }
 }
 
 // Top-k by rank counting, one 1024-thread workgroup per token.  The logit of
@@ -188,8 +220,8 @@ hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, i
       hipLaunchKernelGGL(logits_small_kernel, dim3((E + 3) / 4, n_parts), dim3(256), 0, s, x, wr, bias, T,
                          H, E, logits);
     else
-      hipLaunchKernelGGL(logits_tiled_kernel, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x,
-                         wr, bias, T, H, E, logits);
+      hipLaunchKernelGGL(logits_tiled_kernel, dim3((E + kLgE - 1) / kLgE, (T + kLgT - 1) / kLgT), dim3(256), 0,
+                         s, x, wr, bias, T, H, E, logits);
   });
   if (err != hipSuccess) return err;
   return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
