@@ -34,6 +34,28 @@ METRIC = "MoE-layer tokens/s (decode b=1, prefill 2048) + % HBM BW / % MFMA peak
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per launch (read + written) of the dominant kernels, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the counts the same
+# counters gave for an elementwise pass of known size (FETCH x 2.0, WRITE x 1.0);
+# the summaries are profiles/<workload>_counters.md.  Each entry holds a digest
+# of the kernel sources it was measured on: when the sources differ, the figure
+# no longer describes the kernel and "traffic" is reported as null.
+MEASURED_TRAFFIC = {
+    ("decode_b1", "decode_upgate"): ("4730e0165db532f2:59c3bfc54c94cebc", 76.17e6 + 0.049e6),
+    ("decode_b1", "decode_down"): ("4730e0165db532f2:59c3bfc54c94cebc", 39.36e6 + 0.016e6),
+    ("prefill_2048", "prefill_upgate"): ("6718c2c857356488:59c3bfc54c94cebc", 2489.82e6 + 75.497e6),
+    ("prefill_2048", "prefill_down"): ("6718c2c857356488:59c3bfc54c94cebc", 1337.68e6 + 301.990e6),
+}
+TRAFFIC_SOURCES = {"decode": ["k_decode1.hip", "device_common.hpp"], "prefill": ["k_prefill.hip", "device_common.hpp"]}
+
+
+def source_digest(kind):
+    import hashlib
+    d = os.path.join(ROOT, "bit_quantized_moe_02_amd", "csrc")
+    return ":".join(hashlib.sha256(open(os.path.join(d, f), "rb").read()).hexdigest()[:16]
+                    for f in TRAFFIC_SOURCES[kind])
+
+
 DECODE = {"decode_b1", "decode_b16_hot", "k4_h7168_decode"}
 PREFILL = {"prefill_2048", "k4_h7168_prefill"}
 
@@ -301,8 +323,13 @@ def main():
             per_kernel[kn] = {"avg_us": round(float(durs[kn].mean()) * 1e6, 2), "achieved": round(ach, 1),
                               "frac": round(ach / peak, 4), "work_per_launch": float(w.mean())}
         dom = max(kernels, key=lambda kn: durs[kn].sum())
+        traffic = None
+        rec = MEASURED_TRAFFIC.get((wl.name, dom))
+        if rec is not None and rec[0] == source_digest("decode" if decode else "prefill"):
+            traffic = rec[1]
         roof = {"bound": bound, "achieved": per_kernel[dom]["achieved"], "peak": peak, "unit": unit,
-                "frac": per_kernel[dom]["frac"], "traffic": None, "kernel": dom,
+                "frac": per_kernel[dom]["frac"], "traffic": traffic, "traffic_unit": "bytes per launch",
+                "kernel": dom,
                 "avg_us": per_kernel[dom]["avg_us"],
                 ("bytes_per_launch" if decode else "flops_per_launch"): per_kernel[dom]["work_per_launch"]}
 
