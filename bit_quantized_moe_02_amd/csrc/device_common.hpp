@@ -110,22 +110,25 @@ __device__ __forceinline__ half8 cb2_group(uint32_t code, const uint8_t* val_lan
   return as_half8(v ^ m);
 }
 
-// CB2 combined table (64 KB, the kernels place it at LDS offset 0): entry
-// (idx, half, nib) at byte ((idx*2 + half)*16 + nib)*8 holds the 4 fp16
-// values T[idx][4*half+i]/4, negated where bit i of nib is set, so a group of
-// 8 weights is two 8-byte reads addressed straight from its 16-bit code
-// (idx | flip << 8): half 0 takes flip bits 0..3, half 1 bits 4..7.
+// CB2 combined table (REP x 64 KB, the kernels place it at LDS offset 0):
+// entry (idx, half, nib) holds the 4 fp16 values T[idx][4*half+i]/4, negated
+// where bit i of nib is set, so a group of 8 weights is two 8-byte reads
+// addressed straight from its 16-bit code (idx | flip << 8): half 0 takes flip
+// bits 0..3, half 1 bits 4..7.  Copy r of the entry sits at byte
+//   ((idx*2 + half)*16 + nib)*8*REP + 8*r,
+// and lane l reads copy l % REP: with REP = 2 even and odd lanes read
+// disjoint halves of the LDS banks, so random codes collide less.
 constexpr int kCb2CombBytes = 256 * 2 * 16 * 8;
 
-// Group of 8 weights from a dword holding the codes of k-blocks (kb, kb^1):
-// the low 16 bits for even kb (odd = 0), the high 16 bits for odd kb.
-__device__ __forceinline__ half8 cb2_comb(uint32_t w, int odd, const uint8_t* tab) {
+template <int REP>
+__device__ __forceinline__ half8 cb2_comb(uint32_t w, int odd, const uint8_t* tab_lane) {
+  static_assert(REP == 1 || REP == 2, "replication 1 or 2");
   const uint32_t c = odd ? (w >> 16) : (w & 0xFFFFu);
-  const uint32_t base = (c & 0xFFu) << 8;
-  const uint32_t a0 = base | ((c >> 5) & 0x78u);          // nib = flip & 15
-  const uint32_t a1 = base | ((c >> 9) & 0x78u);          // nib = flip >> 4
-  const uint2 lo = *reinterpret_cast<const uint2*>(tab + a0);
-  const uint2 hi = *reinterpret_cast<const uint2*>(tab + 128 + a1);
+  const uint32_t base = (c & 0xFFu) << (REP == 1 ? 8 : 9);
+  const uint32_t a0 = base | (REP == 1 ? ((c >> 5) & 0x78u) : ((c >> 4) & 0xF0u));   // nib = flip & 15
+  const uint32_t a1 = base | (REP == 1 ? ((c >> 9) & 0x78u) : ((c >> 8) & 0xF0u));   // nib = flip >> 4
+  const uint2 lo = *reinterpret_cast<const uint2*>(tab_lane + a0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(tab_lane + 128 * REP + a1);
   return as_half8(u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
@@ -140,11 +143,14 @@ __device__ __forceinline__ uint2 cb2_pair_values(const int8_t* v) {
   return make_uint2(w[0], w[1]);
 }
 
-// Entry i of the table from the values of its pair (val = cb2_pair_values).
-__device__ __forceinline__ void cb2_comb_put(uint8_t* tab, int i, uint2 val) {
-  const uint32_t nib = i & 15;
-  const uint32_t m01 = ((nib & 1u) << 15) | ((nib & 2u) << 30);
-  const uint32_t m23 = ((nib & 4u) << 13) | ((nib & 8u) << 28);
+// Slot i (0 .. 8192*REP - 1, in memory order) of the table, from the pair
+// values val4[pr] (cb2_pair_values).
+template <int REP>
+__device__ __forceinline__ void cb2_comb_put(uint8_t* tab, int i, const uint2* val4) {
+  const int pr = i / (16 * REP), nib = (i / REP) & 15;
+  const uint2 val = val4[pr];
+  const uint32_t m01 = ((uint32_t)(nib & 1) << 15) | ((uint32_t)(nib & 2) << 30);
+  const uint32_t m23 = ((uint32_t)(nib & 4) << 13) | ((uint32_t)(nib & 8) << 28);
   *reinterpret_cast<uint2*>(tab + (size_t)i * 8) = make_uint2(val.x ^ m01, val.y ^ m23);
 }
 
@@ -158,7 +164,7 @@ __device__ __forceinline__ void cb2_comb_fill(const int8_t* codebook, uint8_t* t
     val4[pr] = cb2_pair_values(v);
   }
   __syncthreads();
-  for (int i = tid; i < 512 * 16; i += nthreads) cb2_comb_put(tab, i, val4[i >> 4]);
+  for (int i = tid; i < 512 * 16; i += nthreads) cb2_comb_put<1>(tab, i, val4);
   __syncthreads();
 }
 

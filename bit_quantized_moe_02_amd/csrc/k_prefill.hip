@@ -155,7 +155,7 @@ __device__ __forceinline__ void b_load(K2B& b, const uint8_t* tile, int lane) {
 __device__ __forceinline__ half8 b_decode(const Cb2B& b, int kk, const uint8_t* tab) {
   const int kb = kk >> 1;
   const uint32_t w = (kk & 1) ? b.c1[kb >> 1] : b.c0[kb >> 1];
-  const half8 v = cb2_comb(w, kb & 1, tab);
+  const half8 v = cb2_comb<1>(w, kb & 1, tab);
   const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)((b.sc[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu));
   return v * s;
 }

@@ -144,68 +144,86 @@ __device__ __forceinline__ uint64_t route_key(float l, int e) {
   return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-constexpr int kTopkThreads = 1024;
+// Rank top-k of one token with NT threads (NT a multiple of 256): logit_of(e)
+// gives expert e's logit; NT/256 threads count each key's rank over a share
+// of the keys.  Shared scratch comes from the caller.
+struct TopkLds {
+  uint64_t key[1024];
+  float lg[1024];
+  int part_rank[4][256];
+  float kv[16];
+  int ki[16];
+};
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits, int n_parts, int T, int E, int k,
-                                                            int32_t* topk_idx, float* topk_w) {
-  __shared__ __align__(16) uint64_t key[1024];
-  __shared__ float lg[1024];
-  __shared__ int part_rank[4][256];
-  __shared__ float kv[16];
-  __shared__ int ki[16];
-  const int t = blockIdx.x, tid = threadIdx.x;
+template <int NT, typename LogitOf>
+__device__ __forceinline__ void rank_topk(TopkLds& sm, int E, int k, int32_t* topk_idx, float* topk_w,
+                                          LogitOf logit_of) {
+  constexpr int Q = NT / 256;
+  const int tid = threadIdx.x;
   const int Ep = (E + 7) & ~7;                 // keys padded with 0 (below every real key)
-  for (int e = tid; e < Ep; e += kTopkThreads) {
+  for (int e = tid; e < Ep; e += NT) {
     float s = 0.f;
     uint64_t kk = 0;
     if (e < E) {
-      float pv[kMaxLogitParts];                // all partial loads in flight together
-#pragma unroll
-      for (int p = 0; p < kMaxLogitParts; ++p)
-        pv[p] = p < n_parts ? logits[((size_t)p * T + t) * E + e] : 0.f;
-      s = pv[0];
-#pragma unroll
-      for (int p = 1; p < kMaxLogitParts; ++p)
-        if (p < n_parts) s += pv[p];
+      s = logit_of(e);
       kk = route_key(s, e);
     }
-    key[e] = kk;
-    lg[e] = s;
+    sm.key[e] = kk;
+    sm.lg[e] = s;
   }
   __syncthreads();
   const int q = tid >> 8, el = tid & 255;
-  const int span = Ep / 4;                      // multiple of 2
+  const int span = Ep / Q;                      // multiple of 2
   for (int e0 = 0; e0 < E; e0 += 256) {
     const int e = e0 + el;
     int cnt = 0;
     if (e < E) {
-      const uint64_t mine = key[e];
+      const uint64_t mine = sm.key[e];
       const int i_end = (q + 1) * span;
       for (int i = q * span; i < i_end; i += 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&key[i]);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.key[i]);
         const uint64_t k0 = (uint64_t)v.x | ((uint64_t)v.y << 32);
         const uint64_t k1 = (uint64_t)v.z | ((uint64_t)v.w << 32);
         cnt += (k0 > mine) + (k1 > mine);
       }
     }
-    part_rank[q][el] = cnt;
+    sm.part_rank[q][el] = cnt;
     __syncthreads();
     if (q == 0 && e < E) {
-      const int rank = part_rank[0][el] + part_rank[1][el] + part_rank[2][el] + part_rank[3][el];
+      int rank = 0;
+      for (int i = 0; i < Q; ++i) rank += sm.part_rank[i][el];
       if (rank < k) {
-        kv[rank] = lg[e];
-        ki[rank] = e;
+        sm.kv[rank] = sm.lg[e];
+        sm.ki[rank] = e;
       }
     }
     __syncthreads();
   }
   if (tid < k) {
-    const float top = kv[0];
+    const float top = sm.kv[0];
     float z = 0.f;
-    for (int j = 0; j < k; ++j) z += expf(kv[j] - top);
-    topk_idx[(size_t)t * k + tid] = ki[tid];
-    topk_w[(size_t)t * k + tid] = expf(kv[tid] - top) / z;
+    for (int j = 0; j < k; ++j) z += expf(sm.kv[j] - top);
+    topk_idx[tid] = sm.ki[tid];
+    topk_w[tid] = expf(sm.kv[tid] - top) / z;
   }
+}
+
+constexpr int kTopkThreads = 1024;
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits, int n_parts, int T, int E, int k,
+                                                            int32_t* topk_idx, float* topk_w) {
+  __shared__ __align__(16) TopkLds sm;
+  const int t = blockIdx.x;
+  rank_topk<kTopkThreads>(sm, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, [&](int e) {
+    float pv[kMaxLogitParts];                  // all partial loads in flight together
+#pragma unroll
+    for (int p = 0; p < kMaxLogitParts; ++p) pv[p] = p < n_parts ? logits[((size_t)p * T + t) * E + e] : 0.f;
+    float s = pv[0];
+#pragma unroll
+    for (int p = 1; p < kMaxLogitParts; ++p)
+      if (p < n_parts) s += pv[p];
+    return s;
+  });
 }
 
 }  // namespace

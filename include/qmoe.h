@@ -180,7 +180,8 @@ size_t moe_route_workspace_bytes(int32_t T, int32_t E);
  *   topk_idx device int32 [T, k]: experts by descending logit, ties to the
  *            lower index;  topk_w device fp32 [T, k]: exp(l_j - l_0) /
  *            sum_i exp(l_i - l_0) over the kept logits.
- * Logits are fp32 sums.  ws: device, >= moe_route_workspace_bytes(T, E).
+ * Logits are fp32 sums.  ws: device scratch, >= moe_route_workspace_bytes(T,
+ * E); its contents need no initialization.
  * Limits: 1 <= k <= min(E, 16), E <= 1024, H a multiple of 8. */
 int moe_route(const void* x_bf16, const float* w_router, const float* logit_bias,
               int32_t T, int32_t H, int32_t E, int32_t k, int32_t* topk_idx,

@@ -131,6 +131,70 @@ def test_route_matches_oracle(q, name, T):
     print(f"near-tie tokens exempted: {int(tie.sum())}")
 
 
+@pytest.mark.parametrize("name", ["decode_b1", "k4_h7168_decode", "tiny"])
+def test_route_single_token_calls(q, name):
+    """One-token routing, the decode case: many calls in a row on one
+    workspace that starts out holding garbage, each checked against the
+    oracle."""
+    import torch
+    print(f"route one token at a time: {name}", flush=True)
+    wl = synth.WORKLOADS[name]
+    layer = device_layer(wl, experts=[])
+    n = 12
+    xb, x64 = x_bits(wl, n)
+    E, H, k = wl.n_experts, wl.hidden, wl.top_k
+    ws = torch.randint(0, 256, (q.moe_route_workspace_bytes(1, E),), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((n, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((n, k), dtype=torch.float32, device="cuda")
+    for t in range(n):
+        q.moe_route(_bf16(xb[t:t + 1]), layer.router, layer.bias, 1, H, E, k, idx[t:t + 1], w[t:t + 1], ws)
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    o_idx, o_w, logits = O.route(x64, synth.router_weight(wl), synth.logit_bias(wl), k)
+    ok = ~near_tie_tokens(logits, k)
+    assert np.array_equal(idx[ok], o_idx[ok]), "routing indices differ"
+    assert np.allclose(w[ok], o_w[ok], rtol=1e-5, atol=0)
+    print(f"near-tie tokens exempted: {int((~ok).sum())}")
+
+
+def test_route_single_token_graph_replay(q):
+    """The one-token route captured once in a HIP graph (as the decode bench
+    does) and replayed on new inputs: every replay's result matches the oracle
+    and an eager call's."""
+    import torch
+    wl = synth.WORKLOADS["decode_b1"]
+    layer = device_layer(wl, experts=[])
+    E, H, k = wl.n_experts, wl.hidden, wl.top_k
+    n = 5
+    xb, x64 = x_bits(wl, n, step=7)
+    x_dev = _bf16(xb)
+    x_static = x_dev[0:1].clone()
+    ws = torch.empty(q.moe_route_workspace_bytes(1, E), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    q.moe_route(x_static, layer.router, layer.bias, 1, H, E, k, idx, w, ws)     # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.moe_route(x_static, layer.router, layer.bias, 1, H, E, k, idx, w, ws)
+    o_idx, o_w, logits = O.route(x64, synth.router_weight(wl), synth.logit_bias(wl), k)
+    ok = ~near_tie_tokens(logits, k)
+    e_idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    e_w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    e_ws = torch.empty_like(ws)
+    for t in range(n):
+        x_static.copy_(x_dev[t:t + 1])
+        g.replay()
+        torch.cuda.synchronize()
+        q.moe_route(x_dev[t:t + 1], layer.router, layer.bias, 1, H, E, k, e_idx, e_w, e_ws)
+        torch.cuda.synchronize()
+        gi, gw = idx.cpu().numpy()[0], w.cpu().numpy()[0]
+        assert np.array_equal(gi, e_idx.cpu().numpy()[0]) and np.array_equal(gw, e_w.cpu().numpy()[0]), \
+            f"replay {t} differs from the eager call"
+        if ok[t]:
+            assert np.array_equal(gi, o_idx[t]), f"replay {t}: routing indices differ"
+            assert np.allclose(gw, o_w[t], rtol=1e-5, atol=0)
+
+
 @pytest.mark.parametrize("T,k,E,skew", [(2048, 8, 256, False), (300, 3, 17, False), (16, 8, 256, True),
                                         (1, 2, 8, False), (8192, 8, 256, False)])
 def test_group_matches_oracle(q, T, k, E, skew):
