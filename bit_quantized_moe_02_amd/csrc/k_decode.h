@@ -43,5 +43,10 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const 
                        int cus, hipStream_t s);
 hipError_t launch_combine(const DecArgs& a, const int32_t* topk_idx, const float* topk_w, float* y,
                           hipStream_t s);
+// Batched path (k_decodem.hip): 2..16 tokens, CB2/CB2/K2, H/256 and
+// I_pad/256 at most 16 chunks each.
+size_t decm_upgate_lds(int nw);
+size_t decm_down_lds(const DecArgs& a, int nw);
+hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus, hipStream_t s);
 
 }  // namespace qmoe

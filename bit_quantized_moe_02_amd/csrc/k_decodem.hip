@@ -1,0 +1,446 @@
+// Batched decode (2..16 tokens, e.g. draft verification), CB2 up/gate and K2
+// down, H <= 4096:
+//   decm_upgate: h_{t,j} = SiLU(Wg_e x_t) * (Wu_e x_t) for every choice (t, j)
+//                of the batch and h_s,t for the shared expert;
+//   decm_down:   y_{t,j} = Wd_e h_{t,j} and the shared expert's down;
+//   decm_combine: y_t = sum_j w_{t,j} y_{t,j} + y_s,t in j order.
+//
+// Work items are (distinct expert, 16-row tile) -- its token set is the
+// bitmask of tokens that chose the expert -- plus the shared expert's row
+// tiles; items are split over the grid by the bytes they stream.  All tokens
+// of the batch sit in the 16 MFMA rows (v_mfma_f32_16x16x32_f16), so one
+// dequantized weight tile serves every token and the rows of tokens that did
+// not choose the expert are computed and dropped.  K is split over the waves
+// of a workgroup (one 256-column chunk each) and the partial sums meet in LDS
+// in wave order (fixed order, no atomics); the next item's weights are in
+// flight while the current one is multiplied.  Weights are dequantized to
+// fp16 B operands with their scales folded in (one fp16 rounding per
+// weight), as in the prefill kernels.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qmoe.h"
+#include "decode_common.hpp"
+#include "device_common.hpp"
+#include "k_decode.h"
+#include "launch_util.h"
+
+using namespace qmoe_dev;
+using namespace qmoe_dec;
+using qmoe::DecArgs;
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kMRB = 2;      // items per cross-wave reduction (up/gate)
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ float4v mfma_bf16(const u32x4& a, const u32x4& b, const float4v& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+
+// CB2 group for k-block kb with its fp16 scale folded in.
+__device__ __forceinline__ half8 cb2_scaled_b(const u32x4& codes, const u32x4& scl, int kb, const uint8_t* tab) {
+  const half8 v = cb2_comb<1>(codes[kb >> 1], kb & 1, tab);
+  const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu));
+  return v * s;
+}
+
+// K2 B operand of lane (qq, n) for k-block kb (sub-block 2 kb + qq/2): q
+// exactly from the magic value, then q * d*sc - dmin*m as one fp32 fma (d*sc
+// and dmin*m are exact in fp32) rounded to fp16: the fp16 value of the
+// dequantized weight.
+__device__ __forceinline__ half8 k2_scaled_b(const u32x4& qw, const u32x4& scm, uint32_t dd, int kb, int qq) {
+  const half8 mg = as_half8(k2_magic(qw, kb));
+  const int sb = 2 * kb + (qq >> 1);
+  const uint32_t byte = (scm[sb >> 2] >> (8 * (sb & 3))) & 0xFFu;
+  const float dsc = h2f(dd & 0xFFFFu) * (float)(byte & 15u);
+  const float ndm = -(h2f(dd >> 16) * (float)(byte >> 4));
+  half8 w;
+  for (int s = 0; s < 4; ++s) {
+    const int t = k2_slot_t(kb, s);
+    const _Float16 sc = (_Float16)__builtin_ldexpf(1.0f, -2 * t);
+    const _Float16 off = (_Float16)(-1024.0f * __builtin_ldexpf(1.0f, -2 * t));
+    const _Float16 q0 = mg[2 * s] * sc + off;
+    const _Float16 q1 = mg[2 * s + 1] * sc + off;
+    w[2 * s] = (_Float16)__builtin_fmaf((float)q0, dsc, ndm);
+    w[2 * s + 1] = (_Float16)__builtin_fmaf((float)q1, dsc, ndm);
+  }
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Up/gate.  Items: shared row tiles [0, n_rts), then (expert d, row tile rt).
+
+struct UgPayM {
+  u32x4 code[2], scl[2];     // up, gate: the lane's group codes, row n's scales
+  bool ok;
+};
+
+__global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* tab = smem;                                                      // CB2 table, LDS offset 0
+  const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float* red = reinterpret_cast<float*>(smem + kCb2CombBytes);             // [kMRB][NW][2][64][4]
+  ExpertList* L = reinterpret_cast<ExpertList*>(red + kMRB * NW * 2 * 256);
+
+  const int T = a.T, k = a.k, n_chunks = a.H / 256, n_rt = a.I / 16, n_rts = a.Is / 16;
+  const bool active = wave < n_chunks;        // idle waves (H < 1024) load chunk 0 and discard it
+  const int chunk = active ? wave : 0;
+  const int m = lane & 15, qq = lane >> 4, n = lane & 15;
+
+  // x of all tokens: A rows m < T (bf16 -> fp16), and the codebook bytes
+  u32x4 xr[8];
+  for (int kb = 0; kb < 8; ++kb)
+    xr[kb] = m < T ? load16(a.x + (size_t)m * a.H + chunk * 256 + kb * 32 + qq * 8) : u32x4{0u, 0u, 0u, 0u};
+  int8_t cbv[4] = {0, 0, 0, 0};
+  if (tid < 512)
+    for (int i = 0; i < 4; ++i) cbv[i] = a.codebook[(tid >> 1) * 8 + 4 * (tid & 1) + i];
+
+  build_expert_list(a.topk_idx, T * k, k, a.E, L, a.err_count);
+  const int64_t n_r = (int64_t)L->n * n_rt;
+  const int64_t w_r = (int64_t)2 * kCb2Tile * n_chunks, w_s = (int64_t)2 * kBf16Tile * n_chunks;
+  const int64_t lo = item_start(blockIdx.x, gridDim.x, n_rts, w_s, n_r, w_r);
+  const int64_t hi = item_start(blockIdx.x + 1, gridDim.x, n_rts, w_s, n_r, w_r);
+
+  // routed payload prefetch: item r = (d, rt)
+  int64_t r_ld = max(lo, (int64_t)n_rts) - n_rts;
+  int d_ld = (int)(r_ld / n_rt), rt_ld = (int)(r_ld - (int64_t)d_ld * n_rt);
+  const int64_t r_end = hi - n_rts;
+  auto issue = [&](UgPayM& P) {
+    const bool ok = r_ld < r_end && active;
+    const int e = ok ? L->expert[d_ld] : 0;
+    const int rt = ok ? rt_ld : 0;
+    const size_t t_off = (size_t)e * a.expert_bytes + ((size_t)rt * n_chunks + chunk) * kCb2Tile;
+    for (int mat = 0; mat < 2; ++mat) {
+      const uint8_t* tile = (mat ? a.gate : a.up) + t_off;
+      P.code[mat] = load16(tile + 16 * lane);
+      P.scl[mat] = load16(tile + 1024 + 16 * n);
+    }
+    P.ok = ok;
+    ++r_ld;
+    if (++rt_ld == n_rt) {
+      rt_ld = 0;
+      ++d_ld;
+    }
+  };
+  UgPayM P0, P1;
+  if (hi > n_rts) issue(P0);
+
+  half8 A[8];
+  for (int kb = 0; kb < 8; ++kb) A[kb] = active ? bf16x8_to_half8(xr[kb]) : as_half8(u32x4{0u, 0u, 0u, 0u});
+
+  // CB2 table (the pair values staged in the reduction area)
+  uint2* val4 = reinterpret_cast<uint2*>(red);
+  if (tid < 512) val4[tid] = cb2_pair_values(cbv);
+  for (int pr = tid + (int)blockDim.x; pr < 512; pr += blockDim.x) {
+    int8_t v[4];
+    for (int i = 0; i < 4; ++i) v[i] = a.codebook[(pr >> 1) * 8 + 4 * (pr & 1) + i];
+    val4[pr] = cb2_pair_values(v);
+  }
+  __syncthreads();
+  for (int i = tid; i < 512 * 16; i += blockDim.x) cb2_comb_put<1>(tab, i, val4);
+  __syncthreads();
+
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+  // cross-wave sums of a batch of items -> h (routed: every slot (t, j) whose
+  // token chose the item's expert), h_s (shared)
+  auto flush = [&](int64_t first, int nb) {
+    __syncthreads();
+    if (tid < nb * 256) {
+      const int b = tid >> 8, mm = (tid >> 4) & 15, nn = tid & 15;
+      const int cl = 16 * (mm >> 2) + nn, ci = mm & 3;
+      float u = 0.f, g = 0.f;
+      for (int w = 0; w < n_chunks; ++w) {
+        u += red[(((b * NW + w) * 2 + 0) * 64 + cl) * 4 + ci];
+        g += red[(((b * NW + w) * 2 + 1) * 64 + cl) * 4 + ci];
+      }
+      const _Float16 h16 = (_Float16)(silu(g) * u);
+      const int64_t item = first + b;
+      if (mm < T) {
+        if (item < n_rts) {
+          a.hs[(size_t)mm * a.Is + item * 16 + nn] = h16;
+        } else {
+          const int64_t r = item - n_rts;
+          const int dd = (int)(r / n_rt), rt = (int)(r - (int64_t)dd * n_rt);
+          const int e = L->expert[dd];
+          if ((L->mask[dd] >> mm) & 1u)
+            for (int j = 0; j < k; ++j)
+              if (L->slot_e[mm * k + j] == e) a.h[(size_t)(mm * k + j) * a.I + rt * 16 + nn] = h16;
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  int nb = 0;
+  int64_t first = lo;
+  auto done_item = [&](int64_t item, const float4v& cu, const float4v& cg) {
+    if (active) {
+      *reinterpret_cast<float4v*>(red + (((nb * NW + wave) * 2 + 0) * 64 + lane) * 4) = cu;
+      *reinterpret_cast<float4v*>(red + (((nb * NW + wave) * 2 + 1) * 64 + lane) * 4) = cg;
+    }
+    if (++nb == kMRB || item + 1 == hi) {
+      flush(first, nb);
+      first = item + 1;
+      nb = 0;
+    }
+  };
+
+  // shared row tiles: x (bf16) x bf16 weights on bf16 matrix cores, one
+  // matrix at a time
+  const int64_t s_hi = min(hi, (int64_t)n_rts);
+  for (int64_t item = lo; item < s_hi; ++item) {
+    float4v c[2] = {zero, zero};
+    for (int mat = 0; mat < 2; ++mat) {
+      const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)item * n_chunks + chunk) * kBf16Tile;
+      u32x4 raw[8];
+      for (int kb = 0; kb < 8; ++kb) raw[kb] = load16(tile + 1024 * kb + 16 * lane);
+      for (int kb = 0; kb < 8; ++kb) c[mat] = mfma_bf16(active ? xr[kb] : u32x4{0u, 0u, 0u, 0u}, raw[kb], c[mat]);
+    }
+    done_item(item, c[0], c[1]);
+  }
+  // routed items, the next one's weights in flight
+  for (int64_t item = max(lo, (int64_t)n_rts); item < hi; item += 2) {
+    if (item + 1 < hi) issue(P1);
+    {
+      float4v cu = zero, cg = zero;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        cu = mfma_f16(A[kb], cb2_scaled_b(P0.code[0], P0.scl[0], kb, tab), cu);
+        cg = mfma_f16(A[kb], cb2_scaled_b(P0.code[1], P0.scl[1], kb, tab), cg);
+      }
+      if (!P0.ok) cu = cg = zero;
+      done_item(item, cu, cg);
+    }
+    if (item + 1 >= hi) break;
+    if (item + 2 < hi) issue(P0);
+    {
+      float4v cu = zero, cg = zero;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        cu = mfma_f16(A[kb], cb2_scaled_b(P1.code[0], P1.scl[0], kb, tab), cu);
+        cg = mfma_f16(A[kb], cb2_scaled_b(P1.code[1], P1.scl[1], kb, tab), cg);
+      }
+      if (!P1.ok) cu = cg = zero;
+      done_item(item + 1, cu, cg);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down.  Items: shared row tiles of H [0, n_rts), then (expert d, row tile of
+// H).  A = the 16 token rows of h for the current expert (or of h_s), staged
+// in LDS as fp16 when the workgroup reaches a new expert.
+
+struct DnPayM {
+  u32x4 q, scm;
+  uint32_t dd;
+  bool ok;
+};
+
+__global__ __launch_bounds__(1024) void decm_down_kernel(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = a.T, k = a.k;
+  const int n_ck = a.I_pad / 256, n_cks = a.Is > 0 ? a.Is_pad / 256 : 0;
+  const int kmax = max(a.I_pad, a.Is_pad);                                  // staged columns
+  _Float16* hA = reinterpret_cast<_Float16*>(smem);                           // [16][kmax]
+  float* red = reinterpret_cast<float*>(smem + (size_t)16 * kmax * 2);       // [NW][64][4]
+  ExpertList* L = reinterpret_cast<ExpertList*>(red + NW * 256);
+  int* slot_of = reinterpret_cast<int*>(L + 1);                              // [16] slot of token m (or -1)
+
+  const int n_rt = a.H / 16, n_rts = a.Is > 0 ? a.H / 16 : 0;
+  const int m = lane & 15, qq = lane >> 4, n = lane & 15;
+  build_expert_list(a.topk_idx, T * k, k, a.E, L, nullptr);
+  const int64_t n_r = (int64_t)L->n * n_rt;
+  const int64_t w_r = (int64_t)kK2Tile * n_ck, w_s = (int64_t)kBf16Tile * n_cks;
+  const int64_t lo = item_start(blockIdx.x, gridDim.x, n_rts, w_s, n_r, w_r);
+  const int64_t hi = item_start(blockIdx.x + 1, gridDim.x, n_rts, w_s, n_r, w_r);
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+
+  // stage the A rows: shared (d = -1: h_s of every token) or expert d
+  auto stage = [&](int d) {
+    __syncthreads();
+    const int K = d < 0 ? a.Is : a.I, Kp = d < 0 ? a.Is_pad : a.I_pad;
+    if (tid < 16) {
+      int sl = -1;
+      if (tid < T) {
+        if (d < 0) {
+          sl = tid;
+        } else if ((L->mask[d] >> tid) & 1u) {
+          for (int j = 0; j < k; ++j)
+            if (L->slot_e[tid * k + j] == L->expert[d]) sl = tid * k + j;
+        }
+      }
+      slot_of[tid] = sl;
+    }
+    __syncthreads();
+    const _Float16* src = d < 0 ? a.hs : a.h;
+    const int vp = Kp / 8, vk = K / 8;
+    for (int i = tid; i < 16 * vp; i += blockDim.x) {
+      const int mm = i / vp, c = i - mm * vp;
+      const int sl = slot_of[mm];
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (sl >= 0 && c < vk) v = load16(src + (size_t)sl * K + 8 * c);
+      *reinterpret_cast<u32x4*>(hA + (size_t)mm * kmax + 8 * c) = v;
+    }
+    __syncthreads();
+  };
+
+  // reduce one item over the waves and write its rows
+  auto finish = [&](int64_t item, const float4v& acc, int n_waves) {
+    *reinterpret_cast<float4v*>(red + (wave * 64 + lane) * 4) = acc;
+    __syncthreads();
+    if (tid < 256) {
+      const int mm = tid >> 4, nn = tid & 15;
+      const int cl = 16 * (mm >> 2) + nn, ci = mm & 3;
+      float v = 0.f;
+      for (int w = 0; w < n_waves; ++w) v += red[(w * 64 + cl) * 4 + ci];
+      const int sl = slot_of[mm];
+      if (sl >= 0) {
+        if (item < n_rts) a.ysh[(size_t)mm * a.H + item * 16 + nn] = v;
+        else a.ybuf[(size_t)sl * a.H + ((item - n_rts) % n_rt) * 16 + nn] = v;
+      }
+    }
+    __syncthreads();
+  };
+
+  // shared row tiles: h_s (fp16) x bf16 weights converted to fp16
+  const int64_t s_hi = min(hi, (int64_t)n_rts);
+  if (lo < s_hi) stage(-1);
+  const bool s_active = wave < n_cks;
+  for (int64_t item = lo; item < s_hi; ++item) {
+    float4v acc = zero;
+    if (s_active) {
+      const uint8_t* tile = a.sdown + ((size_t)item * n_cks + wave) * kBf16Tile;
+      u32x4 raw[8];
+      for (int kb = 0; kb < 8; ++kb) raw[kb] = load16(tile + 1024 * kb + 16 * lane);
+      for (int kb = 0; kb < 8; ++kb) {
+        const half8 av = as_half8(*reinterpret_cast<const u32x4*>(hA + (size_t)m * kmax + wave * 256 + kb * 32 + qq * 8));
+        acc = mfma_f16(av, bf16x8_to_half8(raw[kb]), acc);
+      }
+    }
+    finish(item, acc, n_cks);
+  }
+
+  // routed items, the next one's weights in flight
+  const bool r_active = wave < n_ck;
+  const int chunk = r_active ? wave : 0;
+  int64_t r_ld = max(lo, (int64_t)n_rts) - n_rts;
+  int d_ld = (int)(r_ld / n_rt), rt_ld = (int)(r_ld - (int64_t)d_ld * n_rt);
+  const int64_t r_end = hi - n_rts;
+  auto issue = [&](DnPayM& P) {
+    const bool ok = r_ld < r_end && r_active;
+    const int e = ok ? L->expert[d_ld] : 0;
+    const int rt = ok ? rt_ld : 0;
+    const uint8_t* tile = a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + chunk) * kK2Tile;
+    P.q = load16(tile + 16 * lane);
+    P.scm = load16(tile + 1024 + 16 * n);
+    P.dd = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
+    P.ok = ok;
+    ++r_ld;
+    if (++rt_ld == n_rt) {
+      rt_ld = 0;
+      ++d_ld;
+    }
+  };
+  DnPayM P0, P1;
+  int cur_d = -1;
+  if (hi > n_rts) issue(P0);
+  auto compute = [&](const DnPayM& P, int64_t item) {
+    const int d = (int)((item - n_rts) / n_rt);
+    if (d != cur_d) {
+      stage(d);
+      cur_d = d;
+    }
+    float4v acc = zero;
+    if (P.ok) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const half8 av = as_half8(*reinterpret_cast<const u32x4*>(hA + (size_t)m * kmax + chunk * 256 + kb * 32 + qq * 8));
+        acc = mfma_f16(av, k2_scaled_b(P.q, P.scm, P.dd, kb, qq), acc);
+      }
+    }
+    finish(item, acc, n_ck);
+  };
+  for (int64_t item = max(lo, (int64_t)n_rts); item < hi; item += 2) {
+    if (item + 1 < hi) issue(P1);
+    compute(P0, item);
+    if (item + 1 >= hi) break;
+    if (item + 2 < hi) issue(P0);
+    compute(P1, item + 1);
+  }
+}
+
+// y[t][h] = sum_j w[t][j] * ybuf[t*k + j][h] + ysh[t][h] in j order (choices
+// with an invalid expert id skipped); one workgroup per token, 4 h per thread.
+__global__ __launch_bounds__(256) void decm_combine_kernel(const float* ybuf, const float* ysh, const int32_t* topk_idx,
+                                                           const float* topk_w, int k, int H, int E, float* y) {
+  const int t = blockIdx.x;
+  for (int h = 4 * threadIdx.x; h < H; h += 4 * blockDim.x) {
+    float4v v[16];
+    bool ok[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int e = j < k ? topk_idx[t * k + j] : -1;
+      ok[j] = e >= 0 && e < E;
+      v[j] = ok[j] ? *reinterpret_cast<const float4v*>(ybuf + (size_t)(t * k + j) * H + h) : float4v{0.f, 0.f, 0.f, 0.f};
+    }
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (ok[j]) {
+        const float wj = topk_w[t * k + j];
+        for (int q = 0; q < 4; ++q) acc[q] += wj * v[j][q];
+      }
+    if (ysh) {
+      const float4v sv = *reinterpret_cast<const float4v*>(ysh + (size_t)t * H + h);
+      for (int q = 0; q < 4; ++q) acc[q] += sv[q];
+    }
+    *reinterpret_cast<float4v*>(y + (size_t)t * H + h) = acc;
+  }
+}
+
+}  // namespace
+
+namespace qmoe {
+
+size_t decm_upgate_lds(int nw) {
+  return (size_t)kCb2CombBytes + (size_t)kMRB * nw * 2 * 256 * 4 + sizeof(ExpertList);
+}
+
+size_t decm_down_lds(const DecArgs& a, int nw) {
+  const size_t kmax = (size_t)(a.I_pad > a.Is_pad ? a.I_pad : a.Is_pad);
+  return 16 * kmax * 2 + (size_t)nw * 256 * 4 + sizeof(ExpertList) + 16 * 4;
+}
+
+hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus, hipStream_t s) {
+  const int n_chunks = a.H / 256, n_ck = a.I_pad / 256, n_cks = a.Is > 0 ? a.Is_pad / 256 : 0;
+  const int nw_ug = n_chunks < 4 ? 4 : n_chunks;
+  int nw_dn = n_ck > n_cks ? n_ck : n_cks;
+  if (nw_dn < 4) nw_dn = 4;
+  hipError_t err = ensure_dyn_lds((const void*)decm_upgate_kernel);
+  if (err != hipSuccess) return err;
+  err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
+    hipLaunchKernelGGL(decm_upgate_kernel, dim3(cus), dim3(64 * nw_ug), decm_upgate_lds(nw_ug), s, a);
+  });
+  if (err != hipSuccess) return err;
+  err = ensure_dyn_lds((const void*)decm_down_kernel);
+  if (err != hipSuccess) return err;
+  err = launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&] {
+    hipLaunchKernelGGL(decm_down_kernel, dim3(cus), dim3(64 * nw_dn), decm_down_lds(a, nw_dn), s, a);
+  });
+  if (err != hipSuccess) return err;
+  return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&] {
+    hipLaunchKernelGGL(decm_combine_kernel, dim3((unsigned)a.T), dim3(256), 0, s, a.ybuf, a.Is > 0 ? a.ysh : nullptr,
+                       a.topk_idx, topk_w, a.k, a.H, a.E, y);
+  });
+}
+
+}  // namespace qmoe

@@ -160,22 +160,24 @@ __device__ __forceinline__ half8 b_decode(const Cb2B& b, int kk, const uint8_t* 
   return v * s;
 }
 
-// K4: (magic - 1024) = q exactly, then q * fp16(d*sc) - fp16(dmin*m).
+// K4: (magic - 1024) = q exactly, then q * d*sc - dmin*m as one fp32 fma
+// (both products exact in fp32), rounded to fp16.
 __device__ __forceinline__ half8 b_decode(const K4B& b, int kk, const uint8_t*) {
   const int kb = kk >> 1;
   const uint32_t word = b.q[kk & 1][kb >> 2][kb & 3];
   const half8 mg = as_half8(k4_magic(word));
   const float d = h2f(b.dd & 0xFFFFu), dmin = h2f(b.dd >> 16);
-  const _Float16 dsc = (_Float16)(d * (float)k4_scale_value(b.s0, b.s1, b.s2, kb));
-  const _Float16 ndm = (_Float16)(-(dmin * (float)k4_scale_value(b.s0, b.s1, b.s2, 8 + kb)));
+  const float dsc = d * (float)k4_scale_value(b.s0, b.s1, b.s2, kb);
+  const float ndm = -(dmin * (float)k4_scale_value(b.s0, b.s1, b.s2, 8 + kb));
   const _Float16 m1024 = (_Float16)(-1024.0f);
   half8 w;
-  for (int j = 0; j < 8; ++j) w[j] = (mg[j] + m1024) * dsc + ndm;
+  for (int j = 0; j < 8; ++j) w[j] = (_Float16)__builtin_fmaf((float)(mg[j] + m1024), dsc, ndm);
   return w;
 }
 
 // K2: code pair of slot s decodes to 1024*4^-t + q exactly after scaling the
-// magic value by 4^-t; then q * fp16(d*sc) - fp16(dmin*m).  The lane's
+// magic value by 4^-t; then q * d*sc - dmin*m as one fp32 fma (both products
+// exact in fp32), rounded to fp16.  The lane's
 // sub-block is 2 kb + qq/2 = 2 kb + kk%2.
 __device__ __forceinline__ half8 b_decode(const K2B& b, int kk, const uint8_t*) {
   const int kb = kk >> 1;
@@ -183,8 +185,8 @@ __device__ __forceinline__ half8 b_decode(const K2B& b, int kk, const uint8_t*) 
   const int sb = 2 * kb + (kk & 1);
   const uint32_t byte = (b.scm[sb >> 2] >> (8 * (sb & 3))) & 0xFFu;
   const float d = h2f(b.dd & 0xFFFFu), dmin = h2f(b.dd >> 16);
-  const _Float16 dsc = (_Float16)(d * (float)(byte & 15u));
-  const _Float16 ndm = (_Float16)(-(dmin * (float)(byte >> 4)));
+  const float dsc = d * (float)(byte & 15u);
+  const float ndm = -(dmin * (float)(byte >> 4));
   half8 w;
   for (int s = 0; s < 4; ++s) {
     const int t = k2_slot_t(kb, s);
@@ -192,8 +194,8 @@ __device__ __forceinline__ half8 b_decode(const K2B& b, int kk, const uint8_t*) 
     const _Float16 off = (_Float16)(-1024.0f * __builtin_ldexpf(1.0f, -2 * t));
     const _Float16 q0 = mg[2 * s] * sc + off;
     const _Float16 q1 = mg[2 * s + 1] * sc + off;
-    w[2 * s] = q0 * dsc + ndm;
-    w[2 * s + 1] = q1 * dsc + ndm;
+    w[2 * s] = (_Float16)__builtin_fmaf((float)q0, dsc, ndm);
+    w[2 * s + 1] = (_Float16)__builtin_fmaf((float)q1, dsc, ndm);
   }
   return w;
 }
