@@ -244,7 +244,7 @@ extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, i
   }
   const int nck = g.I_pad / 256, ncks = g.Is > 0 ? g.Is_pad / 256 : 0;
   const int nw_m = (nck > ncks ? nck : ncks) < 4 ? 4 : (nck > ncks ? nck : ncks);
-  if (g.fmt_ug == MOE_FMT_CB2 && n_chunks <= 16 && nck <= 16 && ncks <= 16 &&
+  if (g.fmt_ug == MOE_FMT_CB2 && n_chunks <= 16 && nck <= 8 && ncks <= 8 &&
       decm_down_lds(a, nw_m) <= 160 * 1024) {
     hipError_t e = launch_decm(a, topk_w, y, cus, s);
     if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode", e);

@@ -128,11 +128,8 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
       ++d_ld;
     }
   };
-  UgPayM P0, P1;
+  UgPayM P0, P1, P2;
   if (hi > n_rts) issue(P0);
-
-  half8 A[8];
-  for (int kb = 0; kb < 8; ++kb) A[kb] = active ? bf16x8_to_half8(xr[kb]) : as_half8(u32x4{0u, 0u, 0u, 0u});
 
   // CB2 table (the pair values staged in the reduction area)
   uint2* val4 = reinterpret_cast<uint2*>(red);
@@ -204,31 +201,31 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
     }
     done_item(item, c[0], c[1]);
   }
-  // routed items, the next one's weights in flight
-  for (int64_t item = max(lo, (int64_t)n_rts); item < hi; item += 2) {
-    if (item + 1 < hi) issue(P1);
-    {
-      float4v cu = zero, cg = zero;
+  // routed items, the next two items' weights in flight
+  half8 A[8];
+  for (int kb = 0; kb < 8; ++kb) A[kb] = active ? bf16x8_to_half8(xr[kb]) : as_half8(u32x4{0u, 0u, 0u, 0u});
+  auto compute = [&](const UgPayM& P, int64_t item) {
+    float4v cu = zero, cg = zero;
+    if (P.ok) {
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        cu = mfma_f16(A[kb], cb2_scaled_b(P0.code[0], P0.scl[0], kb, tab), cu);
-        cg = mfma_f16(A[kb], cb2_scaled_b(P0.code[1], P0.scl[1], kb, tab), cg);
+        cu = mfma_f16(A[kb], cb2_scaled_b(P.code[0], P.scl[0], kb, tab), cu);
+        cg = mfma_f16(A[kb], cb2_scaled_b(P.code[1], P.scl[1], kb, tab), cg);
       }
-      if (!P0.ok) cu = cg = zero;
-      done_item(item, cu, cg);
     }
+    done_item(item, cu, cg);
+  };
+  const int64_t r0 = max(lo, (int64_t)n_rts);
+  if (r0 + 1 < hi) issue(P1);
+  for (int64_t item = r0; item < hi; item += 3) {
+    if (item + 2 < hi) issue(P2);
+    compute(P0, item);
     if (item + 1 >= hi) break;
-    if (item + 2 < hi) issue(P0);
-    {
-      float4v cu = zero, cg = zero;
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        cu = mfma_f16(A[kb], cb2_scaled_b(P1.code[0], P1.scl[0], kb, tab), cu);
-        cg = mfma_f16(A[kb], cb2_scaled_b(P1.code[1], P1.scl[1], kb, tab), cg);
-      }
-      if (!P1.ok) cu = cg = zero;
-      done_item(item + 1, cu, cg);
-    }
+    if (item + 3 < hi) issue(P0);
+    compute(P1, item + 1);
+    if (item + 2 >= hi) break;
+    if (item + 4 < hi) issue(P1);
+    compute(P2, item + 2);
   }
 }
 
@@ -237,13 +234,19 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
 // H).  A = the 16 token rows of h for the current expert (or of h_s), staged
 // in LDS as fp16 when the workgroup reaches a new expert.
 
-struct DnPayM {
-  u32x4 q, scm;
-  uint32_t dd;
-  bool ok;
+// Down: a round is up to kDnR consecutive row tiles of one expert (or one
+// shared row tile).  Wave w owns K chunk w; its slice of the staged A rows
+// stays in registers for the whole expert, the next round's weights are in
+// flight while the current one computes, and the waves' partial sums are
+// reduced once per round.
+constexpr int kDnR = 4;
+
+struct DnRound {
+  u32x4 q[kDnR], scm[kDnR];
+  uint32_t dd[kDnR];
 };
 
-__global__ __launch_bounds__(1024) void decm_down_kernel(DecArgs a) {
+__global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -251,8 +254,8 @@ __global__ __launch_bounds__(1024) void decm_down_kernel(DecArgs a) {
   const int n_ck = a.I_pad / 256, n_cks = a.Is > 0 ? a.Is_pad / 256 : 0;
   const int kmax = max(a.I_pad, a.Is_pad);                                  // staged columns
   _Float16* hA = reinterpret_cast<_Float16*>(smem);                           // [16][kmax]
-  float* red = reinterpret_cast<float*>(smem + (size_t)16 * kmax * 2);       // [NW][64][4]
-  ExpertList* L = reinterpret_cast<ExpertList*>(red + NW * 256);
+  float* red = reinterpret_cast<float*>(smem + (size_t)16 * kmax * 2);       // [kDnR][NW][64][4]
+  ExpertList* L = reinterpret_cast<ExpertList*>(red + kDnR * NW * 256);
   int* slot_of = reinterpret_cast<int*>(L + 1);                              // [16] slot of token m (or -1)
 
   const int n_rt = a.H / 16, n_rts = a.Is > 0 ? a.H / 16 : 0;
@@ -293,19 +296,22 @@ __global__ __launch_bounds__(1024) void decm_down_kernel(DecArgs a) {
     __syncthreads();
   };
 
-  // reduce one item over the waves and write its rows
-  auto finish = [&](int64_t item, const float4v& acc, int n_waves) {
-    *reinterpret_cast<float4v*>(red + (wave * 64 + lane) * 4) = acc;
+  // reduce `cnt` row tiles (first one rt0) over the first n_waves waves and
+  // write their rows: shared ones to ysh, routed ones to ybuf
+  auto finish = [&](const float4v* acc, int cnt, int64_t rt0, int n_waves, bool shared) {
+    for (int j = 0; j < kDnR; ++j)
+      if (j < cnt) *reinterpret_cast<float4v*>(red + ((j * NW + wave) * 64 + lane) * 4) = acc[j];
     __syncthreads();
-    if (tid < 256) {
-      const int mm = tid >> 4, nn = tid & 15;
+    for (int o = tid; o < cnt * 256; o += blockDim.x) {
+      const int j = o >> 8, mm = (o >> 4) & 15, nn = o & 15;
       const int cl = 16 * (mm >> 2) + nn, ci = mm & 3;
       float v = 0.f;
-      for (int w = 0; w < n_waves; ++w) v += red[(w * 64 + cl) * 4 + ci];
+      for (int w = 0; w < n_waves; ++w) v += red[((j * NW + w) * 64 + cl) * 4 + ci];
       const int sl = slot_of[mm];
       if (sl >= 0) {
-        if (item < n_rts) a.ysh[(size_t)mm * a.H + item * 16 + nn] = v;
-        else a.ybuf[(size_t)sl * a.H + ((item - n_rts) % n_rt) * 16 + nn] = v;
+        const size_t row = (size_t)(rt0 + j) * 16 + nn;
+        if (shared) a.ysh[(size_t)mm * a.H + row] = v;
+        else a.ybuf[(size_t)sl * a.H + row] = v;
       }
     }
     __syncthreads();
@@ -316,65 +322,71 @@ __global__ __launch_bounds__(1024) void decm_down_kernel(DecArgs a) {
   if (lo < s_hi) stage(-1);
   const bool s_active = wave < n_cks;
   for (int64_t item = lo; item < s_hi; ++item) {
-    float4v acc = zero;
+    float4v acc[1] = {zero};
     if (s_active) {
       const uint8_t* tile = a.sdown + ((size_t)item * n_cks + wave) * kBf16Tile;
       u32x4 raw[8];
       for (int kb = 0; kb < 8; ++kb) raw[kb] = load16(tile + 1024 * kb + 16 * lane);
       for (int kb = 0; kb < 8; ++kb) {
         const half8 av = as_half8(*reinterpret_cast<const u32x4*>(hA + (size_t)m * kmax + wave * 256 + kb * 32 + qq * 8));
-        acc = mfma_f16(av, bf16x8_to_half8(raw[kb]), acc);
+        acc[0] = mfma_f16(av, bf16x8_to_half8(raw[kb]), acc[0]);
       }
     }
-    finish(item, acc, n_cks);
+    finish(acc, 1, item, n_cks, true);
   }
 
-  // routed items, the next one's weights in flight
+  // routed rounds, the next round's weights in flight
   const bool r_active = wave < n_ck;
   const int chunk = r_active ? wave : 0;
-  int64_t r_ld = max(lo, (int64_t)n_rts) - n_rts;
-  int d_ld = (int)(r_ld / n_rt), rt_ld = (int)(r_ld - (int64_t)d_ld * n_rt);
+  int64_t r_next = max(lo, (int64_t)n_rts) - n_rts;       // next routed item to load
   const int64_t r_end = hi - n_rts;
-  auto issue = [&](DnPayM& P) {
-    const bool ok = r_ld < r_end && r_active;
-    const int e = ok ? L->expert[d_ld] : 0;
-    const int rt = ok ? rt_ld : 0;
-    const uint8_t* tile = a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + chunk) * kK2Tile;
-    P.q = load16(tile + 16 * lane);
-    P.scm = load16(tile + 1024 + 16 * n);
-    P.dd = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
-    P.ok = ok;
-    ++r_ld;
-    if (++rt_ld == n_rt) {
-      rt_ld = 0;
-      ++d_ld;
+  // issue the loads of the round starting at r_next; returns its size (0: none)
+  auto issue = [&](DnRound& P, int& d, int& rt0) {
+    if (r_next >= r_end) return 0;
+    d = (int)(r_next / n_rt);
+    rt0 = (int)(r_next - (int64_t)d * n_rt);
+    const int cnt = (int)min((int64_t)min(kDnR, n_rt - rt0), r_end - r_next);
+    const uint8_t* base = a.down + (size_t)L->expert[d] * a.expert_bytes_down + (size_t)chunk * kK2Tile;
+#pragma unroll
+    for (int j = 0; j < kDnR; ++j) {
+      const uint8_t* tile = base + (size_t)(rt0 + min(j, cnt - 1)) * n_ck * kK2Tile;
+      P.q[j] = load16(tile + 16 * lane);
+      P.scm[j] = load16(tile + 1024 + 16 * n);
+      P.dd[j] = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
     }
+    r_next += cnt;
+    return cnt;
   };
-  DnPayM P0, P1;
+  half8 A[8];
   int cur_d = -1;
-  if (hi > n_rts) issue(P0);
-  auto compute = [&](const DnPayM& P, int64_t item) {
-    const int d = (int)((item - n_rts) / n_rt);
+  auto compute = [&](const DnRound& P, int cnt, int d, int rt0) {
     if (d != cur_d) {
       stage(d);
       cur_d = d;
+      for (int kb = 0; kb < 8; ++kb)
+        A[kb] = as_half8(*reinterpret_cast<const u32x4*>(hA + (size_t)m * kmax + chunk * 256 + kb * 32 + qq * 8));
     }
-    float4v acc = zero;
-    if (P.ok) {
+    float4v acc[kDnR];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const half8 av = as_half8(*reinterpret_cast<const u32x4*>(hA + (size_t)m * kmax + chunk * 256 + kb * 32 + qq * 8));
-        acc = mfma_f16(av, k2_scaled_b(P.q, P.scm, P.dd, kb, qq), acc);
-      }
+    for (int j = 0; j < kDnR; ++j) acc[j] = zero;
+    if (r_active) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int j = 0; j < kDnR; ++j)
+          if (j < cnt) acc[j] = mfma_f16(A[kb], k2_scaled_b(P.q[j], P.scm[j], P.dd[j], kb, qq), acc[j]);
     }
-    finish(item, acc, n_ck);
+    finish(acc, cnt, rt0, n_ck, false);
   };
-  for (int64_t item = max(lo, (int64_t)n_rts); item < hi; item += 2) {
-    if (item + 1 < hi) issue(P1);
-    compute(P0, item);
-    if (item + 1 >= hi) break;
-    if (item + 2 < hi) issue(P0);
-    compute(P1, item + 1);
+  DnRound P0, P1;
+  int d0 = 0, rt0 = 0, d1 = 0, rt1 = 0;
+  int c0 = issue(P0, d0, rt0);
+  while (c0 > 0) {
+    const int c1 = issue(P1, d1, rt1);
+    compute(P0, c0, d0, rt0);
+    if (c1 == 0) break;
+    c0 = issue(P0, d0, rt0);
+    compute(P1, c1, d1, rt1);
   }
 }
 
@@ -417,7 +429,7 @@ size_t decm_upgate_lds(int nw) {
 
 size_t decm_down_lds(const DecArgs& a, int nw) {
   const size_t kmax = (size_t)(a.I_pad > a.Is_pad ? a.I_pad : a.Is_pad);
-  return 16 * kmax * 2 + (size_t)nw * 256 * 4 + sizeof(ExpertList) + 16 * 4;
+  return 16 * kmax * 2 + (size_t)kDnR * nw * 256 * 4 + sizeof(ExpertList) + 16 * 4;
 }
 
 hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus, hipStream_t s) {
@@ -425,6 +437,7 @@ hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus,
   const int nw_ug = n_chunks < 4 ? 4 : n_chunks;
   int nw_dn = n_ck > n_cks ? n_ck : n_cks;
   if (nw_dn < 4) nw_dn = 4;
+  if (nw_ug > 16 || nw_dn > 8) return hipErrorInvalidValue;   // H <= 4096, I and I_s <= 2048
   hipError_t err = ensure_dyn_lds((const void*)decm_upgate_kernel);
   if (err != hipSuccess) return err;
   err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {

@@ -225,8 +225,25 @@ __device__ __forceinline__ void stage_rows(int* rows, int64_t m0, int64_t p_end,
 // ---------------------------------------------------------------------------
 // Up/gate, routed experts (CB2 or K4).  blockIdx.x = 256-row N-tile of I.
 
+// 16 k-steps of one staged chunk over the first mta M-tiles.
+template <int FMT, typename B>
+__device__ __forceinline__ void ug_steps(float16v (&acc)[2][kMT], const B& cu, const B& cg, const uint8_t* tab,
+                                         const uint8_t* a_lds, int mta, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const half8 bu = b_decode(cu, kk, tab), bg = b_decode(cg, kk, tab);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+      if (mt < mta) {
+        const half8 av = a_read(a_lds, mt, kk, lane);
+        acc[0][mt] = mfma32(av, bu, acc[0][mt]);
+        acc[1][mt] = mfma32(av, bg, acc[1][mt]);
+      }
+  }
+}
+
 template <int FMT>
-__device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e) {
+__device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e, int nt) {
   const int64_t p_begin = a.offsets[e], p_end = a.offsets[e + 1];
   if (p_begin >= p_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -234,7 +251,7 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e)
   uint8_t* a_lds = smem + (FMT == MOE_FMT_CB2 ? kCb2CombBytes : 0);
   if (FMT == MOE_FMT_CB2) cb2_comb_fill(a.codebook, tab, reinterpret_cast<uint2*>(a_lds), tid, blockDim.x);
   const int n_rt = a.I / 16, n_chunks = a.H / 256, k = a.k;
-  const int rt0 = (blockIdx.x * kUgRowsPerWg + wave * 32) / 16;
+  const int rt0 = (nt * kUgRowsPerWg + wave * 32) / 16;
   const bool active = rt0 < n_rt;
   const int rt_l = min(rt0 + ((lane & 31) >> 4), n_rt - 1);            // clamped: loads stay in the matrix
   const int tb = FMT == MOE_FMT_CB2 ? kCb2Tile : kK4Tile;
@@ -263,17 +280,7 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e)
         b_load(ng, tg + (size_t)(chunk + 1) * tb, lane);
       }
       if (active) {
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const half8 bu = b_decode(cu, kk, tab), bg = b_decode(cg, kk, tab);
-#pragma unroll
-          for (int mt = 0; mt < kMT; ++mt)
-            if (mt < mta) {
-              const half8 av = a_read(a_lds, mt, kk, lane);
-              acc[0][mt] = mfma32(av, bu, acc[0][mt]);
-              acc[1][mt] = mfma32(av, bg, acc[1][mt]);
-            }
-        }
+        ug_steps<FMT>(acc, cu, cg, tab, a_lds, mta, lane);
       }
       cu = nu;
       cg = ng;
@@ -292,13 +299,26 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e)
 // Up/gate, shared expert (bf16 x bf16 on bf16 matrix cores).  blockIdx.y - E
 // = 96-token chunk.  Weights stream a quarter chunk (4 steps) at a time, the
 // next quarter's loads in flight during the current one.
-__device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc) {
+__device__ __forceinline__ void ug_shared_steps(float16v (&acc)[2][kMT], const u32x4 (&cu)[4], const u32x4 (&cg)[4],
+                                                const uint8_t* a_lds, int q0, int mta, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+      if (mt < mta) {
+        const u32x4 av = as_u32x4(a_read(a_lds, mt, q0 + q, lane));
+        acc[0][mt] = mfma32_bf(av, cu[q], acc[0][mt]);
+        acc[1][mt] = mfma32_bf(av, cg[q], acc[1][mt]);
+      }
+}
+
+__device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc, int nt) {
   const int64_t p_begin = (int64_t)mc * kMRows, p_end = min((int64_t)a.T, p_begin + kMRows);
   if (p_begin >= p_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint8_t* a_lds = smem;
   const int n_rt = a.Is / 16, n_chunks = a.H / 256;
-  const int rt0 = (blockIdx.x * kUgRowsPerWg + wave * 32) / 16;
+  const int rt0 = (nt * kUgRowsPerWg + wave * 32) / 16;
   const bool active = rt0 < n_rt;
   const int rt_l = min(rt0 + ((lane & 31) >> 4), n_rt - 1);
   const uint8_t* tu = a.sup + (size_t)rt_l * n_chunks * kBf16Tile;
@@ -332,15 +352,7 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
       }
     }
     if (active) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-          if (mt < mta) {
-            const u32x4 av = as_u32x4(a_read(a_lds, mt, q0 + q, lane));
-            acc[0][mt] = mfma32_bf(av, cu[q], acc[0][mt]);
-            acc[1][mt] = mfma32_bf(av, cg[q], acc[1][mt]);
-          }
+      ug_shared_steps(acc, cu, cg, a_lds, q0, mta, lane);
     }
     for (int q = 0; q < 4; ++q) {
       cu[q] = nu[q];
@@ -356,15 +368,34 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
       }
 }
 
+// Workgroup -> (N-tile nt, group g) over a 1-D grid of n_nt * roundup(G, 8)
+// workgroups.  Consecutive workgroups go to the 8 XCDs in turn, so workgroup
+// L runs on XCD L % 8; all n_nt N-tiles of a group are given to the same XCD
+// back to back, and the token rows they all stage come through one L2.
+// Groups [0, n_sh) are the shared expert's token chunks (the heaviest
+// workgroups, dispatched first), then the routed experts.
+__device__ __forceinline__ bool pf_tile(int n_nt, int n_groups, int& nt, int& g) {
+  const int L = (int)blockIdx.x, x = L & 7, j = L >> 3;
+  nt = j % n_nt;
+  g = (j / n_nt) * 8 + x;
+  return g < n_groups;
+}
+
+__host__ __device__ inline int pf_shared_chunks(const PfArgs& a) { return a.Is > 0 ? (a.T + kMRows - 1) / kMRows : 0; }
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void pf_upgate_kernel(PfArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  if (blockIdx.y < (unsigned)a.E) {
-    if ((int)blockIdx.x * kUgRowsPerWg >= a.I) return;
-    ug_routed<FMT>(a, smem, (int)blockIdx.y);
+  const int n_sh = pf_shared_chunks(a);
+  const int n_nt = ((a.Is > a.I ? a.Is : a.I) + kUgRowsPerWg - 1) / kUgRowsPerWg;
+  int nt, g;
+  if (!pf_tile(n_nt, a.E + n_sh, nt, g)) return;
+  if (g >= n_sh) {
+    if (nt * kUgRowsPerWg >= a.I) return;
+    ug_routed<FMT>(a, smem, g - n_sh, nt);
   } else {
-    if ((int)blockIdx.x * kUgRowsPerWg >= a.Is) return;
-    ug_shared(a, smem, (int)blockIdx.y - a.E);
+    if (nt * kUgRowsPerWg >= a.Is) return;
+    ug_shared(a, smem, g, nt);
   }
 }
 
@@ -372,8 +403,23 @@ __global__ __launch_bounds__(kThreads) void pf_upgate_kernel(PfArgs a) {
 // Down.  blockIdx.x = 256-row N-tile of H (one 32-row B tile per wave).
 // Routed outputs go to yslot[position], shared outputs to ysh[token].
 
+template <int FMT, int MTA, typename B>
+__device__ __forceinline__ void dn_steps(float16v (&acc)[kDnTiles][kMT], const B (&cur)[kDnTiles], const uint8_t* a_lds,
+                                         int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    half8 bw[kDnTiles];
+    for (int b = 0; b < kDnTiles; ++b) bw[b] = b_decode(cur[b], kk, nullptr);
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt) {
+      const half8 av = a_read(a_lds, mt, kk, lane);
+      for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
+    }
+  }
+}
+
 template <int FMT>
-__device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e) {
+__device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e, int nt) {
   const int64_t p_begin = a.offsets[e], p_end = a.offsets[e + 1];
   if (p_begin >= p_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -383,7 +429,7 @@ __device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e)
   int rt0[kDnTiles];
   const uint8_t* tp[kDnTiles];
   for (int b = 0; b < kDnTiles; ++b) {
-    rt0[b] = (blockIdx.x * kDnRowsPerWg + wave * 32 * kDnTiles + 32 * b) / 16;
+    rt0[b] = (nt * kDnRowsPerWg + wave * 32 * kDnTiles + 32 * b) / 16;
     const int rt_l = min(rt0[b] + ((lane & 31) >> 4), n_rt - 1);
     tp[b] = a.down + (size_t)e * a.expert_bytes_down + (size_t)rt_l * n_chunks * tb;
   }
@@ -407,17 +453,9 @@ __device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e)
         a_load(st, reinterpret_cast<const uint16_t*>(a.h), a.I, rows, (chunk + 1) * 256, a.I);
         for (int b = 0; b < kDnTiles; ++b) b_load(nxt[b], tp[b] + (size_t)(chunk + 1) * tb, lane);
       }
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        half8 bw[kDnTiles];
-        for (int b = 0; b < kDnTiles; ++b) bw[b] = b_decode(cur[b], kk, nullptr);
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-          if (mt < mta) {
-            const half8 av = a_read(a_lds, mt, kk, lane);
-            for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
-          }
-      }
+      if (mta >= 3) dn_steps<FMT, 3>(acc, cur, a_lds, lane);
+      else if (mta == 2) dn_steps<FMT, 2>(acc, cur, a_lds, lane);
+      else dn_steps<FMT, 1>(acc, cur, a_lds, lane);
       for (int b = 0; b < kDnTiles; ++b) cur[b] = nxt[b];
     }
     for (int b = 0; b < kDnTiles; ++b) {
@@ -434,7 +472,22 @@ __device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e)
 
 // Shared expert down: hs (fp16) x bf16 weights converted to fp16 in
 // registers, weights streamed a quarter chunk at a time.
-__device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc) {
+template <int MTA>
+__device__ __forceinline__ void dn_shared_steps(float16v (&acc)[kDnTiles][kMT], const u32x4 (&cw)[kDnTiles][4],
+                                                const uint8_t* a_lds, int q0, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    half8 bw[kDnTiles];
+    for (int b = 0; b < kDnTiles; ++b) bw[b] = bf16x8_to_half8(cw[b][q]);
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt) {
+      const half8 av = a_read(a_lds, mt, q0 + q, lane);
+      for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
+    }
+  }
+}
+
+__device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc, int nt) {
   const int64_t p_begin = (int64_t)mc * kMRows, p_end = min((int64_t)a.T, p_begin + kMRows);
   if (p_begin >= p_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -443,7 +496,7 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
   int rt0[kDnTiles];
   const uint8_t* tp[kDnTiles];
   for (int b = 0; b < kDnTiles; ++b) {
-    rt0[b] = (blockIdx.x * kDnRowsPerWg + wave * 32 * kDnTiles + 32 * b) / 16;
+    rt0[b] = (nt * kDnRowsPerWg + wave * 32 * kDnTiles + 32 * b) / 16;
     const int rt_l = min(rt0[b] + ((lane & 31) >> 4), n_rt - 1);
     tp[b] = a.sdown + (size_t)rt_l * n_chunks * kBf16Tile;
   }
@@ -473,17 +526,9 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
       for (int b = 0; b < kDnTiles; ++b)
         for (int q = 0; q < 4; ++q) nw[b][q] = bf16_piece(tp[b] + (size_t)c1 * kBf16Tile, k1 + q, lane);
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      half8 bw[kDnTiles];
-      for (int b = 0; b < kDnTiles; ++b) bw[b] = bf16x8_to_half8(cw[b][q]);
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
-        if (mt < mta) {
-          const half8 av = a_read(a_lds, mt, q0 + q, lane);
-          for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
-        }
-    }
+    if (mta >= 3) dn_shared_steps<3>(acc, cw, a_lds, q0, lane);
+    else if (mta == 2) dn_shared_steps<2>(acc, cw, a_lds, q0, lane);
+    else dn_shared_steps<1>(acc, cw, a_lds, q0, lane);
     for (int b = 0; b < kDnTiles; ++b)
       for (int q = 0; q < 4; ++q) cw[b][q] = nw[b][q];
   }
@@ -501,9 +546,12 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void pf_down_kernel(PfArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  if ((int)blockIdx.x * kDnRowsPerWg >= a.H) return;
-  if (blockIdx.y < (unsigned)a.E) dn_routed<FMT>(a, smem, (int)blockIdx.y);
-  else dn_shared(a, smem, (int)blockIdx.y - a.E);
+  const int n_sh = pf_shared_chunks(a);
+  const int n_nt = (a.H + kDnRowsPerWg - 1) / kDnRowsPerWg;
+  int nt, g;
+  if (!pf_tile(n_nt, a.E + n_sh, nt, g)) return;
+  if (g >= n_sh) dn_routed<FMT>(a, smem, g - n_sh, nt);
+  else dn_shared(a, smem, g, nt);
 }
 
 // y[t][h] = sum_j w[t][j] * yslot[slot_pos[t*k + j]][h] + ysh[t][h], summed in
@@ -549,11 +597,11 @@ int pf_m_rows() { return kMRows; }
 
 hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,
                           hipStream_t s) {
-  const int n_sh = a.Is > 0 ? (a.T + kMRows - 1) / kMRows : 0;
+  const int n_groups8 = (a.E + pf_shared_chunks(a) + 7) / 8 * 8;
   const dim3 block(kThreads);
   {
     const int rows = a.Is > a.I ? a.Is : a.I;
-    const dim3 grid((rows + kUgRowsPerWg - 1) / kUgRowsPerWg, a.E + n_sh);
+    const dim3 grid((unsigned)(((rows + kUgRowsPerWg - 1) / kUgRowsPerWg) * n_groups8));
     const size_t lds = (fmt_ug == MOE_FMT_CB2 ? kCb2CombBytes : 0) + kStageBytes;
     void (*fn)(PfArgs) = fmt_ug == MOE_FMT_CB2 ? pf_upgate_kernel<MOE_FMT_CB2> : pf_upgate_kernel<MOE_FMT_K4>;
     hipError_t err = ensure_dyn_lds((const void*)fn);
@@ -562,7 +610,7 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
     if (err != hipSuccess) return err;
   }
   {
-    const dim3 grid((a.H + kDnRowsPerWg - 1) / kDnRowsPerWg, a.E + n_sh);
+    const dim3 grid((unsigned)(((a.H + kDnRowsPerWg - 1) / kDnRowsPerWg) * n_groups8));
     void (*fn)(PfArgs) = fmt_dn == MOE_FMT_K2 ? pf_down_kernel<MOE_FMT_K2> : pf_down_kernel<MOE_FMT_K4>;
     hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
