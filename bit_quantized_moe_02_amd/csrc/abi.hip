@@ -310,6 +310,7 @@ extern "C" int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, 
   a.hs = (_Float16*)(wsb + L.hs);
   a.yslot = (float*)(wsb + L.yslot);
   a.ysh = (float*)(wsb + L.ysh);
+  a.x16 = (const uint16_t*)(wsb + L.yslot);   // T*H fp16 fits in yslot, which only the down kernel writes
   hipError_t e = launch_prefill(a, g.fmt_ug, g.fmt_dn, topk_w, y, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("moe_expert_ffn_prefill", e);
   return MOE_OK;

@@ -9,6 +9,7 @@ namespace qmoe {
 
 struct PfArgs {
   const uint16_t* x;              // bf16 [T][H]
+  const uint16_t* x16;            // fp16 [T][H] copy of x (workspace; written by the launch)
   int T, H, I, Is, I_pad, Is_pad, k, E;
   const int32_t* offsets;         // [E+1]
   const int32_t* sorted_slots;    // [T*k]

@@ -39,8 +39,6 @@ constexpr int kMRows = 32 * kMT;                         // 96 tokens per pass
 constexpr int kUgRowsPerWg = kWaves * 32;                // up/gate: 256 rows of I
 constexpr int kDnTiles = 1;                              // down: 32-row B tiles per wave
 constexpr int kDnRowsPerWg = kWaves * 32 * kDnTiles;     // 256 rows of H
-constexpr int kStageBytes = kMRows * 256 * 2;            // one staged 256-column chunk (48 KB)
-constexpr int kPieces = kMRows * 32 / kThreads;          // 16-byte pieces per thread per chunk (6)
 
 __device__ __forceinline__ float16v mfma32(const half8& a, const half8& b, const float16v& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -53,43 +51,61 @@ __device__ __forceinline__ float16v mfma32_bf(const u32x4& a, const u32x4& b, co
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ---------------------------------------------------------------------------
-// A staging.  MFMA 32x32x16: lane l of M-tile mt, 16-column step kk reads the
-// 8 values of row 32 mt + l%32, columns 16 kk + 8 (l/32) .. +7.  In LDS the
-// 16-byte piece (row r, step kk, half hf) sits at slot
-//   (r/32 * 16 + kk) * 64 + 32 hf + ((r%32 + kk) & 31)
-// (a rotation by kk within each half), so that both the row-wise stores of
-// the staging and the MFMA reads are free of bank conflicts.
-__device__ __forceinline__ int a_slot(int r, int kk, int hf) {
-  return ((r >> 5) * 16 + kk) * 64 + 32 * hf + (((r & 31) + kk) & 31);
-}
-__device__ __forceinline__ half8 a_read(const uint8_t* lds, int mt, int kk, int lane) {
-  const int slot = (mt * 16 + kk) * 64 + (lane & 32) + ((lane + kk) & 31);
-  return as_half8(*reinterpret_cast<const u32x4*>(lds + slot * 16));
+// A staging.  A 256-column chunk of kMRows token rows goes from global memory
+// straight into LDS through global_load_lds_dwordx4: one instruction writes
+// 1 KB, lane l's 16 bytes at byte 16 l of the wave's LDS destination.  In LDS
+// row r keeps its 32 pieces of 8 columns rotated by r: piece c8 at slot
+// r*32 + ((c8 + r) & 31).  One instruction fills two rows (lane l: row
+// r0 + l/32, slot l%32, i.e. piece (l%32 - r) & 31), and the MFMA reads of a
+// step (32 consecutive rows, one piece column) hit 32 distinct 16-byte bank
+// groups.  Chunks alternate between two buffers, the next chunk in flight
+// while the current one is multiplied; no registers hold staged data.
+
+constexpr int kChunkBytes = kMRows * 512;                // one staged chunk (48 KB)
+constexpr int kStageBytes = 2 * kChunkBytes;             // double buffer (96 KB)
+constexpr int kDmaPerWave = kMRows / 2 / kWaves;         // two-row DMA instructions per wave per chunk (6)
+
+__device__ __forceinline__ half8 a_read(const uint8_t* buf, int mt, int kk, int lane) {
+  const int r = 32 * mt + (lane & 31), c8 = 2 * kk + (lane >> 5);
+  return as_half8(*reinterpret_cast<const u32x4*>(buf + 16 * (r * 32 + ((c8 + r) & 31))));
 }
 
-// Thread tid stages pieces p = tid + kThreads*i: row r = p/32 = tid/32 + 16 i,
-// 8-column group c8 = tid%32.  rows[i] = source row (or -1: zero row).
-struct AStage {
-  u32x4 v[kPieces];
-};
-
-__device__ __forceinline__ void a_load(AStage& st, const uint16_t* src, int64_t ld, const int* rows, int col0,
-                                       int col_valid) {
-  const int col = col0 + 8 * (threadIdx.x & 31);
+// Source rows of this lane's DMA instructions for the pass starting at m0
+// (instruction i of wave w stages rows 2 (w kDmaPerWave + i) + {0, 1}).  Rows
+// past the pass's end repeat its last row: they only feed accumulator rows
+// that are never stored.
+template <typename RowOf>
+__device__ __forceinline__ void stage_rows(int* rows, int64_t m0, int64_t p_end, RowOf row_of) {
+  const int wave = threadIdx.x >> 6, hl = (threadIdx.x >> 5) & 1;
 #pragma unroll
-  for (int i = 0; i < kPieces; ++i)
-    st.v[i] = (rows[i] >= 0 && col < col_valid) ? load16(src + (int64_t)rows[i] * ld + col) : u32x4{0u, 0u, 0u, 0u};
-}
-
-template <bool BF16_TO_F16>
-__device__ __forceinline__ void a_store(const AStage& st, uint8_t* lds) {
-  const int c8 = threadIdx.x & 31, kk = c8 >> 1, hf = c8 & 1;
-#pragma unroll
-  for (int i = 0; i < kPieces; ++i) {
-    const int r = (threadIdx.x >> 5) + 16 * i;
-    const u32x4 v = BF16_TO_F16 ? as_u32x4(bf16x8_to_half8(st.v[i])) : st.v[i];
-    *reinterpret_cast<u32x4*>(lds + a_slot(r, kk, hf) * 16) = v;
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int64_t p = m0 + 2 * (wave * kDmaPerWave + i) + hl;
+    rows[i] = (int)row_of(p < p_end ? p : p_end - 1);
   }
+}
+
+// Issues the DMA of columns [col0, col0 + 256) of rows[] (2-byte elements,
+// row stride ld) into buf.  Columns at or past col_valid read column
+// col_valid - 8 instead: the packed weights there are zero.
+__device__ __forceinline__ void a_dma(uint8_t* buf, const uint16_t* src, int64_t ld, const int* rows, int col0,
+                                      int col_valid) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int r0 = 2 * (wave * kDmaPerWave + i), r = r0 + (lane >> 5);
+    int col = col0 + 8 * (((lane & 31) - r) & 31);
+    if (col >= col_valid) col = col_valid - 8;
+    __builtin_amdgcn_global_load_lds(src + (int64_t)rows[i] * ld + col,
+                                     (__attribute__((address_space(3))) void*)(buf + 512 * r0), 16, 0, 0);
+  }
+}
+
+// Start of a chunk: this wave's loads (its DMA of the chunk, its registers of
+// the chunk's weights) are complete, and after the barrier every wave's are,
+// and every wave is done with the chunk before.
+__device__ __forceinline__ void chunk_sync() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -212,33 +228,23 @@ __device__ __forceinline__ float16v zero16v() {
   return z;
 }
 
-// Rows of this thread's staging pieces for the pass starting at m0.
-template <typename RowOf>
-__device__ __forceinline__ void stage_rows(int* rows, int64_t m0, int64_t p_end, RowOf row_of) {
-#pragma unroll
-  for (int i = 0; i < kPieces; ++i) {
-    const int64_t p = m0 + (threadIdx.x >> 5) + 16 * i;
-    rows[i] = p < p_end ? (int)row_of(p) : -1;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Up/gate, routed experts (CB2 or K4).  blockIdx.x = 256-row N-tile of I.
+// Up/gate, routed experts (CB2 or K4): one (expert, 256-row N-tile of I) per
+// workgroup, A = the expert's token rows of x (fp16 copy).
 
-// 16 k-steps of one staged chunk over the first mta M-tiles.
-template <int FMT, typename B>
+// The 16 k-steps of one staged chunk over MTA live M-tiles.
+template <int MTA, typename B>
 __device__ __forceinline__ void ug_steps(float16v (&acc)[2][kMT], const B& cu, const B& cg, const uint8_t* tab,
-                                         const uint8_t* a_lds, int mta, int lane) {
+                                         const uint8_t* buf, int lane) {
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
     const half8 bu = b_decode(cu, kk, tab), bg = b_decode(cg, kk, tab);
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-      if (mt < mta) {
-        const half8 av = a_read(a_lds, mt, kk, lane);
-        acc[0][mt] = mfma32(av, bu, acc[0][mt]);
-        acc[1][mt] = mfma32(av, bg, acc[1][mt]);
-      }
+    for (int mt = 0; mt < MTA; ++mt) {
+      const half8 av = a_read(buf, mt, kk, lane);
+      acc[0][mt] = mfma32(av, bu, acc[0][mt]);
+      acc[1][mt] = mfma32(av, bg, acc[1][mt]);
+    }
   }
 }
 
@@ -248,8 +254,8 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
   if (p_begin >= p_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint8_t* tab = smem;                                                 // CB2 table at offset 0
-  uint8_t* a_lds = smem + (FMT == MOE_FMT_CB2 ? kCb2CombBytes : 0);
-  if (FMT == MOE_FMT_CB2) cb2_comb_fill(a.codebook, tab, reinterpret_cast<uint2*>(a_lds), tid, blockDim.x);
+  uint8_t* stage = smem + (FMT == MOE_FMT_CB2 ? kCb2CombBytes : 0);
+  if (FMT == MOE_FMT_CB2) cb2_comb_fill(a.codebook, tab, reinterpret_cast<uint2*>(stage), tid, blockDim.x);
   const int n_rt = a.I / 16, n_chunks = a.H / 256, k = a.k;
   const int rt0 = (nt * kUgRowsPerWg + wave * 32) / 16;
   const bool active = rt0 < n_rt;
@@ -261,26 +267,25 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
 
   for (int64_t m0 = p_begin; m0 < p_end; m0 += kMRows) {
     const int mta = (int)min((int64_t)kMT, (p_end - m0 + 31) / 32);
-    int rows[kPieces];
+    int rows[kDmaPerWave];
     stage_rows(rows, m0, p_end, [&](int64_t p) { return (int64_t)(a.sorted_slots[p] / k); });
     float16v acc[2][kMT];
     for (int mt = 0; mt < kMT; ++mt) acc[0][mt] = acc[1][mt] = zero16v();
-    AStage st;
     B cu, cg, nu, ng;
-    a_load(st, a.x, a.H, rows, 0, a.H);
+    __syncthreads();                                                   // the last pass is done with the buffers
+    a_dma(stage, a.x16, a.H, rows, 0, a.H);
     b_load(cu, tu, lane);
     b_load(cg, tg, lane);
     for (int chunk = 0; chunk < n_chunks; ++chunk) {
-      __syncthreads();
-      a_store<true>(st, a_lds);
-      __syncthreads();
+      const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
+      chunk_sync();
       if (chunk + 1 < n_chunks) {
-        a_load(st, a.x, a.H, rows, (chunk + 1) * 256, a.H);
+        a_dma(stage + ((chunk + 1) & 1) * kChunkBytes, a.x16, a.H, rows, (chunk + 1) * 256, a.H);
         b_load(nu, tu + (size_t)(chunk + 1) * tb, lane);
         b_load(ng, tg + (size_t)(chunk + 1) * tb, lane);
       }
       if (active) {
-        ug_steps<FMT>(acc, cu, cg, tab, a_lds, mta, lane);
+        ug_steps<kMT>(acc, cu, cg, tab, buf, lane);
       }
       cu = nu;
       cg = ng;
@@ -296,27 +301,27 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
   }
 }
 
-// Up/gate, shared expert (bf16 x bf16 on bf16 matrix cores).  blockIdx.y - E
-// = 96-token chunk.  Weights stream a quarter chunk (4 steps) at a time, the
-// next quarter's loads in flight during the current one.
+// Up/gate, shared expert (bf16 x bf16 on bf16 matrix cores): one (96-token
+// chunk, 256-row N-tile of I_s) per workgroup.  Weights stream a quarter
+// chunk (4 steps) at a time, the next quarter's loads in flight.
+template <int MTA>
 __device__ __forceinline__ void ug_shared_steps(float16v (&acc)[2][kMT], const u32x4 (&cu)[4], const u32x4 (&cg)[4],
-                                                const uint8_t* a_lds, int q0, int mta, int lane) {
+                                                const uint8_t* buf, int q0, int lane) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-      if (mt < mta) {
-        const u32x4 av = as_u32x4(a_read(a_lds, mt, q0 + q, lane));
-        acc[0][mt] = mfma32_bf(av, cu[q], acc[0][mt]);
-        acc[1][mt] = mfma32_bf(av, cg[q], acc[1][mt]);
-      }
+    for (int mt = 0; mt < MTA; ++mt) {
+      const u32x4 av = as_u32x4(a_read(buf, mt, q0 + q, lane));
+      acc[0][mt] = mfma32_bf(av, cu[q], acc[0][mt]);
+      acc[1][mt] = mfma32_bf(av, cg[q], acc[1][mt]);
+    }
 }
 
 __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc, int nt) {
   const int64_t p_begin = (int64_t)mc * kMRows, p_end = min((int64_t)a.T, p_begin + kMRows);
   if (p_begin >= p_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint8_t* a_lds = smem;
+  uint8_t* stage = smem;
   const int n_rt = a.Is / 16, n_chunks = a.H / 256;
   const int rt0 = (nt * kUgRowsPerWg + wave * 32) / 16;
   const bool active = rt0 < n_rt;
@@ -324,13 +329,12 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
   const uint8_t* tu = a.sup + (size_t)rt_l * n_chunks * kBf16Tile;
   const uint8_t* tg = a.sgate + (size_t)rt_l * n_chunks * kBf16Tile;
   const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
-  int rows[kPieces];
+  int rows[kDmaPerWave];
   stage_rows(rows, p_begin, p_end, [](int64_t p) { return p; });
   float16v acc[2][kMT];
   for (int mt = 0; mt < kMT; ++mt) acc[0][mt] = acc[1][mt] = zero16v();
-  AStage st;
-  a_load(st, a.x, a.H, rows, 0, a.H);
   u32x4 cu[4], cg[4], nu[4], ng[4];
+  a_dma(stage, a.x, a.H, rows, 0, a.H);
   for (int q = 0; q < 4; ++q) {
     cu[q] = bf16_piece(tu, q, lane);
     cg[q] = bf16_piece(tg, q, lane);
@@ -338,11 +342,10 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
   const int n_quarters = 4 * n_chunks;
   for (int gq = 0; gq < n_quarters; ++gq) {
     const int chunk = gq >> 2, q0 = 4 * (gq & 3);
+    const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
     if ((gq & 3) == 0) {
-      __syncthreads();
-      a_store<false>(st, a_lds);
-      __syncthreads();
-      if (chunk + 1 < n_chunks) a_load(st, a.x, a.H, rows, (chunk + 1) * 256, a.H);
+      chunk_sync();
+      if (chunk + 1 < n_chunks) a_dma(stage + ((chunk + 1) & 1) * kChunkBytes, a.x, a.H, rows, (chunk + 1) * 256, a.H);
     }
     if (gq + 1 < n_quarters) {
       const int c1 = (gq + 1) >> 2, k1 = 4 * ((gq + 1) & 3);
@@ -352,7 +355,9 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
       }
     }
     if (active) {
-      ug_shared_steps(acc, cu, cg, a_lds, q0, mta, lane);
+      if (mta >= 3) ug_shared_steps<3>(acc, cu, cg, buf, q0, lane);
+      else if (mta == 2) ug_shared_steps<2>(acc, cu, cg, buf, q0, lane);
+      else ug_shared_steps<1>(acc, cu, cg, buf, q0, lane);
     }
     for (int q = 0; q < 4; ++q) {
       cu[q] = nu[q];
@@ -399,12 +404,20 @@ __global__ __launch_bounds__(kThreads) void pf_upgate_kernel(PfArgs a) {
   }
 }
 
+// x (bf16) -> x16 (fp16), 8 values per thread: the routed experts' A operand.
+__global__ __launch_bounds__(256) void pf_x16_kernel(const uint16_t* x, uint16_t* x16, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n8)
+    *reinterpret_cast<u32x4*>(x16 + 8 * i) = as_u32x4(bf16x8_to_half8(load16(x + 8 * i)));
+}
+
 // ---------------------------------------------------------------------------
-// Down.  blockIdx.x = 256-row N-tile of H (one 32-row B tile per wave).
-// Routed outputs go to yslot[position], shared outputs to ysh[token].
+// Down: one (expert, 256-row N-tile of H) per workgroup, one 32-row B tile
+// per wave, A = the expert's rows of h (positions in grouped order).  Routed
+// outputs go to yslot[position], shared outputs to ysh[token].
 
 template <int FMT, int MTA, typename B>
-__device__ __forceinline__ void dn_steps(float16v (&acc)[kDnTiles][kMT], const B (&cur)[kDnTiles], const uint8_t* a_lds,
+__device__ __forceinline__ void dn_steps(float16v (&acc)[kDnTiles][kMT], const B (&cur)[kDnTiles], const uint8_t* buf,
                                          int lane) {
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
@@ -412,7 +425,7 @@ __device__ __forceinline__ void dn_steps(float16v (&acc)[kDnTiles][kMT], const B
     for (int b = 0; b < kDnTiles; ++b) bw[b] = b_decode(cur[b], kk, nullptr);
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt) {
-      const half8 av = a_read(a_lds, mt, kk, lane);
+      const half8 av = a_read(buf, mt, kk, lane);
       for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
     }
   }
@@ -423,7 +436,7 @@ __device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e,
   const int64_t p_begin = a.offsets[e], p_end = a.offsets[e + 1];
   if (p_begin >= p_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint8_t* a_lds = smem;
+  uint8_t* stage = smem;
   const int n_rt = a.H / 16, n_chunks = a.I_pad / 256;
   const int tb = FMT == MOE_FMT_K2 ? kK2Tile : kK4Tile;
   int rt0[kDnTiles];
@@ -433,29 +446,29 @@ __device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e,
     const int rt_l = min(rt0[b] + ((lane & 31) >> 4), n_rt - 1);
     tp[b] = a.down + (size_t)e * a.expert_bytes_down + (size_t)rt_l * n_chunks * tb;
   }
+  const uint16_t* hsrc = reinterpret_cast<const uint16_t*>(a.h);
   using B = typename BRegs<FMT>::T;
   for (int64_t m0 = p_begin; m0 < p_end; m0 += kMRows) {
     const int mta = (int)min((int64_t)kMT, (p_end - m0 + 31) / 32);
-    int rows[kPieces];
+    int rows[kDmaPerWave];
     stage_rows(rows, m0, p_end, [](int64_t p) { return p; });
     float16v acc[kDnTiles][kMT];
     for (int b = 0; b < kDnTiles; ++b)
       for (int mt = 0; mt < kMT; ++mt) acc[b][mt] = zero16v();
-    AStage st;
     B cur[kDnTiles], nxt[kDnTiles];
-    a_load(st, reinterpret_cast<const uint16_t*>(a.h), a.I, rows, 0, a.I);
+    __syncthreads();
+    a_dma(stage, hsrc, a.I, rows, 0, a.I);
     for (int b = 0; b < kDnTiles; ++b) b_load(cur[b], tp[b], lane);
     for (int chunk = 0; chunk < n_chunks; ++chunk) {
-      __syncthreads();
-      a_store<false>(st, a_lds);
-      __syncthreads();
+      const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
+      chunk_sync();
       if (chunk + 1 < n_chunks) {
-        a_load(st, reinterpret_cast<const uint16_t*>(a.h), a.I, rows, (chunk + 1) * 256, a.I);
+        a_dma(stage + ((chunk + 1) & 1) * kChunkBytes, hsrc, a.I, rows, (chunk + 1) * 256, a.I);
         for (int b = 0; b < kDnTiles; ++b) b_load(nxt[b], tp[b] + (size_t)(chunk + 1) * tb, lane);
       }
-      if (mta >= 3) dn_steps<FMT, 3>(acc, cur, a_lds, lane);
-      else if (mta == 2) dn_steps<FMT, 2>(acc, cur, a_lds, lane);
-      else dn_steps<FMT, 1>(acc, cur, a_lds, lane);
+      if (mta >= 3) dn_steps<FMT, 3>(acc, cur, buf, lane);
+      else if (mta == 2) dn_steps<FMT, 2>(acc, cur, buf, lane);
+      else dn_steps<FMT, 1>(acc, cur, buf, lane);
       for (int b = 0; b < kDnTiles; ++b) cur[b] = nxt[b];
     }
     for (int b = 0; b < kDnTiles; ++b) {
@@ -474,14 +487,14 @@ __device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e,
 // registers, weights streamed a quarter chunk at a time.
 template <int MTA>
 __device__ __forceinline__ void dn_shared_steps(float16v (&acc)[kDnTiles][kMT], const u32x4 (&cw)[kDnTiles][4],
-                                                const uint8_t* a_lds, int q0, int lane) {
+                                                const uint8_t* buf, int q0, int lane) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     half8 bw[kDnTiles];
     for (int b = 0; b < kDnTiles; ++b) bw[b] = bf16x8_to_half8(cw[b][q]);
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt) {
-      const half8 av = a_read(a_lds, mt, q0 + q, lane);
+      const half8 av = a_read(buf, mt, q0 + q, lane);
       for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
     }
   }
@@ -491,7 +504,7 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
   const int64_t p_begin = (int64_t)mc * kMRows, p_end = min((int64_t)a.T, p_begin + kMRows);
   if (p_begin >= p_end) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint8_t* a_lds = smem;
+  uint8_t* stage = smem;
   const int n_rt = a.H / 16, n_chunks = a.Is_pad / 256;
   int rt0[kDnTiles];
   const uint8_t* tp[kDnTiles];
@@ -500,35 +513,33 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
     const int rt_l = min(rt0[b] + ((lane & 31) >> 4), n_rt - 1);
     tp[b] = a.sdown + (size_t)rt_l * n_chunks * kBf16Tile;
   }
+  const uint16_t* hsrc = reinterpret_cast<const uint16_t*>(a.hs);
   const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
-  int rows[kPieces];
+  int rows[kDmaPerWave];
   stage_rows(rows, p_begin, p_end, [](int64_t p) { return p; });
   float16v acc[kDnTiles][kMT];
   for (int b = 0; b < kDnTiles; ++b)
     for (int mt = 0; mt < kMT; ++mt) acc[b][mt] = zero16v();
-  AStage st;
-  a_load(st, reinterpret_cast<const uint16_t*>(a.hs), a.Is, rows, 0, a.Is);
+  a_dma(stage, hsrc, a.Is, rows, 0, a.Is);
   u32x4 cw[kDnTiles][4], nw[kDnTiles][4];
   for (int b = 0; b < kDnTiles; ++b)
     for (int q = 0; q < 4; ++q) cw[b][q] = bf16_piece(tp[b], q, lane);
   const int n_quarters = 4 * n_chunks;
   for (int gq = 0; gq < n_quarters; ++gq) {
     const int chunk = gq >> 2, q0 = 4 * (gq & 3);
+    const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
     if ((gq & 3) == 0) {
-      __syncthreads();
-      a_store<false>(st, a_lds);
-      __syncthreads();
-      if (chunk + 1 < n_chunks)
-        a_load(st, reinterpret_cast<const uint16_t*>(a.hs), a.Is, rows, (chunk + 1) * 256, a.Is);
+      chunk_sync();
+      if (chunk + 1 < n_chunks) a_dma(stage + ((chunk + 1) & 1) * kChunkBytes, hsrc, a.Is, rows, (chunk + 1) * 256, a.Is);
     }
     if (gq + 1 < n_quarters) {
       const int c1 = (gq + 1) >> 2, k1 = 4 * ((gq + 1) & 3);
       for (int b = 0; b < kDnTiles; ++b)
         for (int q = 0; q < 4; ++q) nw[b][q] = bf16_piece(tp[b] + (size_t)c1 * kBf16Tile, k1 + q, lane);
     }
-    if (mta >= 3) dn_shared_steps<3>(acc, cw, a_lds, q0, lane);
-    else if (mta == 2) dn_shared_steps<2>(acc, cw, a_lds, q0, lane);
-    else dn_shared_steps<1>(acc, cw, a_lds, q0, lane);
+    if (mta >= 3) dn_shared_steps<3>(acc, cw, buf, q0, lane);
+    else if (mta == 2) dn_shared_steps<2>(acc, cw, buf, q0, lane);
+    else dn_shared_steps<1>(acc, cw, buf, q0, lane);
     for (int b = 0; b < kDnTiles; ++b)
       for (int q = 0; q < 4; ++q) cw[b][q] = nw[b][q];
   }
@@ -599,6 +610,13 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
                           hipStream_t s) {
   const int n_groups8 = (a.E + pf_shared_chunks(a) + 7) / 8 * 8;
   const dim3 block(kThreads);
+  {
+    const int64_t n8 = (int64_t)a.T * a.H / 8;
+    hipLaunchKernelGGL(pf_x16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a.x,
+                       const_cast<uint16_t*>(a.x16), n8);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   {
     const int rows = a.Is > a.I ? a.Is : a.I;
     const dim3 grid((unsigned)(((rows + kUgRowsPerWg - 1) / kUgRowsPerWg) * n_groups8));
