@@ -419,14 +419,31 @@ __global__ __launch_bounds__(256) void pf_x16_kernel(const uint16_t* x, uint16_t
 template <int FMT, int MTA, typename B>
 __device__ __forceinline__ void dn_steps(float16v (&acc)[kDnTiles][kMT], const B (&cur)[kDnTiles], const uint8_t* buf,
                                          int lane) {
+  // A of step kk + 1 is read while step kk decodes and multiplies
+  half8 av[MTA];
+#pragma unroll
+  for (int mt = 0; mt < MTA; ++mt) av[mt] = a_read(buf, mt, 0, lane);
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
+    half8 an[MTA];
+    if (kk + 1 < 16)
+#pragma unroll
+      for (int mt = 0; mt < MTA; ++mt) an[mt] = a_read(buf, mt, kk + 1, lane);
     half8 bw[kDnTiles];
     for (int b = 0; b < kDnTiles; ++b) bw[b] = b_decode(cur[b], kk, nullptr);
 #pragma unroll
+    for (int mt = 0; mt < MTA; ++mt)
+      for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av[mt], bw[b], acc[b][mt]);
+    if (kk + 1 < 16)
+#pragma unroll
+      for (int mt = 0; mt < MTA; ++mt) av[mt] = an[mt];
+    // issue order per step: the next step's A reads, then the MFMAs
+    // interleaved with the decode arithmetic
+    __builtin_amdgcn_sched_group_barrier(0x100, MTA, 0);
+#pragma unroll
     for (int mt = 0; mt < MTA; ++mt) {
-      const half8 av = a_read(buf, mt, kk, lane);
-      for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av, bw[b], acc[b][mt]);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 24 / MTA, 0);
     }
   }
 }

@@ -242,8 +242,8 @@ def test_group_counts_invalid_ids(q):
 def _multi_token_rounds_weights(wl, T):
     """True where the multi-token decode kernels take this layer: they fold the
     block scales into fp16 weights (one rounding per weight), as prefill does."""
-    return (T >= 2 and wl.fmt_up == "cb2" and wl.hidden <= 4096 and wl.inter <= 4096
-            and wl.shared_inter <= 4096)
+    return (T >= 2 and wl.fmt_up == "cb2" and wl.hidden <= 4096 and wl.inter <= 2048
+            and wl.shared_inter <= 2048)
 
 
 def _check_layer(y, wl, x64, expect_idx=None, mirror_tol=None, round_w=False):
