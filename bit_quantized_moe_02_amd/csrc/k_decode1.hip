@@ -512,6 +512,245 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// K4 up/gate at one token, H up to 8192.
+//
+// A unit is one item (a routed 16-row tile or a shared 8-row half tile)
+// restricted to a K-part of up to 16 chunks: wave w takes chunk 16 kp + w of
+// part kp, and the parts of an item are consecutive units whose per-wave
+// sums accumulate until the item's last part.  Routed units are loaded two
+// ahead.  x sits in LDS as fp16, followed by a zero block: the
+// block-diagonal A operand of k-block kb is one LDS read per lane (the lanes
+// of row kb read x's block, the others the zero block), so no registers hold
+// activations.  K4 codes go into the MFMA as 1024 + q (exact), and the
+// 6-bit scales and mins are applied per k-block to the block dots C_kb with
+// the block sums X_kb of x:
+//   sum_k x_k w_k = sum_kb [d sc_kb C_kb - (1024 d sc_kb + dmin m_kb) X_kb].
+
+struct K4Pay {
+  u32x4 q[2][2];       // up, gate: the lane's words of k-blocks 0-3 and 4-7
+  uint32_t s[2][3];    // up, gate: row n's packed 6-bit scales (0-7) and mins (8-15)
+  uint32_t dd[2];      // up, gate: row n's fp16 d | dmin << 16
+  bool ok;             // false: a stand-in tile, contributes 0
+};
+
+__device__ __forceinline__ void k4_pay_load(K4Pay& p, const DecArgs& a, int e, int rt, int chunk, int lane,
+                                            int n_chunks, bool ok) {
+  const int n = lane & 15;
+  const size_t t_off = (size_t)e * a.expert_bytes + ((size_t)rt * n_chunks + chunk) * kK4Tile;
+  for (int mat = 0; mat < 2; ++mat) {
+    const uint8_t* tile = (mat ? a.gate : a.up) + t_off;
+    p.q[mat][0] = load16(tile + 16 * lane);
+    p.q[mat][1] = load16(tile + 1024 + 16 * lane);
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(tile + 2048 + 12 * n);
+    p.s[mat][0] = sp[0];
+    p.s[mat][1] = sp[1];
+    p.s[mat][2] = sp[2];
+    p.dd[mat] = *reinterpret_cast<const uint32_t*>(tile + 2240 + 4 * n);
+  }
+  p.ok = ok;
+}
+
+// Scaled sum of lane (g, n)'s four block dots (k-blocks 4g .. 4g+3, g < 2).
+__device__ __forceinline__ float k4_scaled(const float4v& c, const uint32_t s[3], uint32_t dd, const float* xs, int g) {
+  const float d = h2f(dd & 0xFFFFu), dmin = h2f(dd >> 16);
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kb = 4 * g + i;
+    const float dsc = d * (float)k4_scale_value(s[0], s[1], s[2], kb);
+    const float mn = dmin * (float)k4_scale_value(s[0], s[1], s[2], 8 + kb);
+    v = fmaf(dsc, c[i], v);
+    v = fmaf(-fmaf(1024.0f, dsc, mn), xs[kb], v);
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H, k = a.k, n_chunks = H / 256, n_kp = (n_chunks + 15) / 16;
+  const int n_rt = a.I / 16, n_rts = a.Is / 16;
+  _Float16* xs16 = reinterpret_cast<_Float16*>(smem);                      // [H] then a 16-byte zero block
+  const int zero_off = 2 * H;
+  float* xsum = reinterpret_cast<float*>(smem + zero_off + 16);            // [H / 32]
+  float* red_r = xsum + H / 32;                                            // [kRedBatch][2][NW][32]
+  float* red_s = red_r + kRedBatch * 2 * NW * 32;                          // [NW][2][8]
+
+  const int G = gridDim.x, gi = blockIdx.x;
+  const int U_s = 2 * n_rts, U_r = k * n_rt;
+  const int s_lo = (int)((int64_t)gi * U_s / G), s_hi = (int)((int64_t)(gi + 1) * U_s / G);
+  const int r_lo = (int)((int64_t)gi * U_r / G), r_hi = (int)((int64_t)(gi + 1) * U_r / G);
+  const int n = lane & 15, g = lane >> 4, m = lane & 15, qq = lane >> 4;
+
+  // routed units u = item * n_kp + kp, loaded kPrefetch3 ahead
+  const int u_lo = r_lo * n_kp, u_hi = r_hi * n_kp;
+  auto issue = [&](K4Pay& P, int u) {
+    int e = -1, rt = 0, chunk = 0;
+    if (u < u_hi) {
+      const int item = u / n_kp, kp = u - item * n_kp;
+      const int j = item / n_rt;
+      rt = item - j * n_rt;
+      chunk = kp * 16 + wave;
+      e = a.topk_idx[j];
+      if (e >= a.E || chunk >= n_chunks) e = -1;
+    }
+    const bool ok = e >= 0;
+    k4_pay_load(P, a, ok ? e : 0, ok ? rt : 0, ok ? chunk : 0, lane, n_chunks, ok);
+  };
+  K4Pay P0, P1;
+  issue(P0, u_lo);
+  issue(P1, u_lo + 1);
+
+  // x -> LDS (fp16) and its 32-column block sums
+  for (int i = tid; i < H / 8; i += blockDim.x)
+    *reinterpret_cast<u32x4*>(xs16 + 8 * i) = as_u32x4(bf16x8_to_half8(load16(a.x + 8 * i)));
+  if (tid == 0) *reinterpret_cast<u32x4*>(smem + zero_off) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  for (int b = tid; b < H / 32; b += blockDim.x) {
+    float v = 0.f;
+    for (int j = 0; j < 32; ++j) v += (float)xs16[32 * b + j];
+    xsum[b] = v;
+  }
+  __syncthreads();
+
+  // A of k-block kb for chunk c: row kb = x block kb (lanes m == kb), else 0
+  auto a_kb = [&](int c, int kb) {
+    const int off = (m == kb) ? c * 512 + kb * 64 + qq * 16 : zero_off;
+    return *reinterpret_cast<const half8*>(smem + off);
+  };
+  // A of k-block pair p (rows 2p and 2p+1) for the shared half tiles
+  auto a_pair = [&](int c, int p) {
+    const int off = (m < 8 && (m >> 1) == p) ? c * 512 + m * 64 + qq * 16 : zero_off;
+    return *reinterpret_cast<const half8*>(smem + off);
+  };
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- shared expert half tiles, K-part by K-part
+  for (int su = s_lo; su < s_hi; ++su) {
+    const int rt = su >> 1, hr = su & 1;
+    const int r = 8 * hr + (n & 7);
+    float v[2] = {0.f, 0.f};
+    for (int kp = 0; kp < n_kp; ++kp) {
+      const int chunk = kp * 16 + wave;
+      if (chunk >= n_chunks) continue;
+      u32x4 sraw[2][4];
+      for (int mat = 0; mat < 2; ++mat) {
+        const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kBf16Tile;
+        for (int p = 0; p < 4; ++p) sraw[mat][p] = load16(tile + 1024 * (2 * p + (n >> 3)) + 16 * (16 * qq + r));
+      }
+      half8 Ap[4];
+      for (int p = 0; p < 4; ++p) Ap[p] = a_pair(chunk, p);
+      for (int mat = 0; mat < 2; ++mat) {
+        float4v c = zero;
+        for (int p = 0; p < 4; ++p) c = mfma_f16(Ap[p], bf16x8_to_half8(sraw[mat][p]), c);
+        float t = (n < 8) ? c[0] + c[2] : c[1] + c[3];
+        if (g >= 2) t = 0.f;
+        t += __shfl_xor(t, 8);
+        t += __shfl_xor(t, 16);
+        v[mat] += t;
+      }
+    }
+    if (lane < 8) {
+      red_s[(wave * 2 + 0) * 8 + lane] = v[0];
+      red_s[(wave * 2 + 1) * 8 + lane] = v[1];
+    }
+    __syncthreads();
+    if (tid < 8) {
+      float u = 0.f, gg = 0.f;
+      for (int w = 0; w < NW; ++w) {
+        u += red_s[(w * 2 + 0) * 8 + tid];
+        gg += red_s[(w * 2 + 1) * 8 + tid];
+      }
+      a.hs[rt * 16 + 8 * hr + tid] = (_Float16)(silu(gg) * u);
+    }
+    __syncthreads();
+  }
+
+  // ---- routed units
+  auto compute = [&](const K4Pay& P, int u, int b) {
+    const int item = u / n_kp, kp = u - item * n_kp;
+    const int chunk = min(kp * 16 + wave, n_chunks - 1);
+    float4v cu = zero, cg = zero;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const half8 av = a_kb(chunk, kb);
+      cu = mfma_f16(av, as_half8(k4_magic(P.q[0][kb >> 2][kb & 3])), cu);
+      cg = mfma_f16(av, as_half8(k4_magic(P.q[1][kb >> 2][kb & 3])), cg);
+    }
+    if (lane < 32) {
+      const float* xs = xsum + chunk * 8;
+      const float vu = P.ok ? k4_scaled(cu, P.s[0], P.dd[0], xs, g) : 0.f;
+      const float vg = P.ok ? k4_scaled(cg, P.s[1], P.dd[1], xs, g) : 0.f;
+      float* ru = &red_r[((b * 2 + 0) * NW + wave) * 32 + lane];
+      float* rg = &red_r[((b * 2 + 1) * NW + wave) * 32 + lane];
+      if (kp == 0) {
+        *ru = vu;
+        *rg = vg;
+      } else {
+        *ru += vu;
+        *rg += vg;
+      }
+    }
+  };
+  auto flush = [&](int first, int nb) {
+    __syncthreads();
+    if (tid < nb * 16) {
+      const int b = tid >> 4, item = first + b;
+      float u = 0.f, gg = 0.f;
+      for (int w = 0; w < NW; ++w) {
+        u += red_r[((b * 2 + 0) * NW + w) * 32 + n];
+        u += red_r[((b * 2 + 0) * NW + w) * 32 + 16 + n];
+        gg += red_r[((b * 2 + 1) * NW + w) * 32 + n];
+        gg += red_r[((b * 2 + 1) * NW + w) * 32 + 16 + n];
+      }
+      const _Float16 h16 = (_Float16)(silu(gg) * u);
+      const float hv = (float)h16;
+      const int j = item / n_rt, rt = item - j * n_rt;
+      a.h[(size_t)j * a.I + rt * 16 + n] = h16;
+      const int kk = (rt * 16 + n) & 255;
+      const int t = k2_slot_t(kk >> 5, (kk & 7) >> 1);
+      float X = hv, O = 1024.0f * (float)(_Float16)(hv * __builtin_ldexpf(1.0f, -2 * t));
+      for (int o = 8; o >= 1; o >>= 1) {
+        X += __shfl_xor(X, o);
+        O += __shfl_xor(O, o);
+      }
+      if (n == 0) {
+        float* hsm = a.hsum + ((size_t)j * (a.I_pad / 16) + rt) * 2;
+        hsm[0] = X;
+        hsm[1] = O;
+      }
+    }
+    __syncthreads();
+  };
+  // every wave writes its reduction slot (zeros when idle), so the flush can
+  // sum all NW waves
+  int nb = 0, first = r_lo;
+  auto done_unit = [&](int u) {
+    const int item = u / n_kp, kp = u - item * n_kp;
+    if (kp + 1 < n_kp) return;
+    if (++nb == kRedBatch || item + 1 == r_hi) {
+      flush(first, nb);
+      first = item + 1;
+      nb = 0;
+    }
+  };
+  for (int u = u_lo; u < u_hi; u += 2) {
+    compute(P0, u, nb);
+    issue(P0, u + 2);
+    done_unit(u);
+    if (u + 1 >= u_hi) break;
+    compute(P1, u + 1, nb);
+    issue(P1, u + 3);
+    done_unit(u + 1);
+  }
+}
+
+size_t dec1_k4_upgate_lds(int H, int nw) {
+  return (size_t)2 * H + 16 + (size_t)(H / 32) * 4 + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4;
+}
+
+// ---------------------------------------------------------------------------
 // Per-wave payload of one routed down unit (one K-chunk of one 16-row tile).
 
 template <int FMT>
@@ -752,7 +991,18 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const 
                        int cus, hipStream_t s) {
   hipError_t err;
   const int n_chunks = a.H / 256;
-  if (fmt_ug == MOE_FMT_CB2 && n_chunks <= 16) {
+  if (fmt_ug == MOE_FMT_K4) {
+    const int nw = n_chunks < 4 ? 4 : (n_chunks > 16 ? 16 : n_chunks);
+    const int U_s = 2 * (a.Is / 16), U_r = a.k * (a.I / 16);
+    const int most = U_s > U_r ? U_s : U_r;
+    const int grid = most < cus ? most : cus;
+    err = ensure_dyn_lds((const void*)dec1_k4_upgate_kernel);
+    if (err != hipSuccess) return err;
+    const size_t lds = dec1_k4_upgate_lds(a.H, nw);
+    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
+      hipLaunchKernelGGL(dec1_k4_upgate_kernel, dim3(grid), dim3(64 * nw), lds, s, a);
+    });
+  } else if (fmt_ug == MOE_FMT_CB2 && n_chunks <= 16) {
     const int nw = n_chunks < 4 ? 4 : n_chunks;
     const int U_s = 2 * (a.Is / 16), U_r = a.k * (a.I / 16);
     const int most = U_s > U_r ? U_s : U_r;

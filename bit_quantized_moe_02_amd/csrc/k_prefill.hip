@@ -32,13 +32,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kUgWaves = 8;                              // up/gate workgroup: waves
+constexpr int kDnWaves = 8;                              // down workgroup: waves
 constexpr int kMT = 3;                                   // 32-token M-tiles per pass
 constexpr int kMRows = 32 * kMT;                         // 96 tokens per pass
-constexpr int kUgRowsPerWg = kWaves * 32;                // up/gate: 256 rows of I
+constexpr int kUgTiles = 1;                              // up/gate: 32-row B tiles per wave and matrix
+constexpr int kUgRowsPerWg = kUgWaves * 32 * kUgTiles;     // 256 rows of I
 constexpr int kDnTiles = 1;                              // down: 32-row B tiles per wave
-constexpr int kDnRowsPerWg = kWaves * 32 * kDnTiles;     // 256 rows of H
+constexpr int kDnRowsPerWg = kDnWaves * 32 * kDnTiles;     // 256 rows of H
 
 __device__ __forceinline__ float16v mfma32(const half8& a, const half8& b, const float16v& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -63,7 +64,8 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 constexpr int kChunkBytes = kMRows * 512;                // one staged chunk (48 KB)
 constexpr int kStageBytes = 2 * kChunkBytes;             // double buffer (96 KB)
-constexpr int kDmaPerWave = kMRows / 2 / kWaves;         // two-row DMA instructions per wave per chunk (6)
+template <int NW>
+constexpr int dma_per_wave() { return kMRows / 2 / NW; }   // two-row DMA instructions per wave per chunk
 
 __device__ __forceinline__ half8 a_read(const uint8_t* buf, int mt, int kk, int lane) {
   const int r = 32 * mt + (lane & 31), c8 = 2 * kk + (lane >> 5);
@@ -71,11 +73,12 @@ __device__ __forceinline__ half8 a_read(const uint8_t* buf, int mt, int kk, int 
 }
 
 // Source rows of this lane's DMA instructions for the pass starting at m0
-// (instruction i of wave w stages rows 2 (w kDmaPerWave + i) + {0, 1}).  Rows
+// (instruction i of wave w stages rows 2 (w D + i) + {0, 1}, D = kMRows / 2 / NW).  Rows
 // past the pass's end repeat its last row: they only feed accumulator rows
 // that are never stored.
-template <typename RowOf>
+template <int NW, typename RowOf>
 __device__ __forceinline__ void stage_rows(int* rows, int64_t m0, int64_t p_end, RowOf row_of) {
+  constexpr int kDmaPerWave = dma_per_wave<NW>();
   const int wave = threadIdx.x >> 6, hl = (threadIdx.x >> 5) & 1;
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) {
@@ -87,8 +90,10 @@ __device__ __forceinline__ void stage_rows(int* rows, int64_t m0, int64_t p_end,
 // Issues the DMA of columns [col0, col0 + 256) of rows[] (2-byte elements,
 // row stride ld) into buf.  Columns at or past col_valid read column
 // col_valid - 8 instead: the packed weights there are zero.
+template <int NW>
 __device__ __forceinline__ void a_dma(uint8_t* buf, const uint16_t* src, int64_t ld, const int* rows, int col0,
                                       int col_valid) {
+  constexpr int kDmaPerWave = dma_per_wave<NW>();
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) {
@@ -234,17 +239,33 @@ __device__ __forceinline__ float16v zero16v() {
 
 // The 16 k-steps of one staged chunk over MTA live M-tiles.
 template <int MTA, typename B>
-__device__ __forceinline__ void ug_steps(float16v (&acc)[2][kMT], const B& cu, const B& cg, const uint8_t* tab,
-                                         const uint8_t* buf, int lane) {
+__device__ __forceinline__ void ug_steps(float16v (&acc)[2][kUgTiles][kMT], const B (&cu)[kUgTiles],
+                                         const B (&cg)[kUgTiles], const uint8_t* tab, const uint8_t* buf, int lane) {
+  half8 av[MTA];
+#pragma unroll
+  for (int mt = 0; mt < MTA; ++mt) av[mt] = a_read(buf, mt, 0, lane);
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
-    const half8 bu = b_decode(cu, kk, tab), bg = b_decode(cg, kk, tab);
+    half8 an[MTA];
+    if (kk + 1 < 16)
 #pragma unroll
-    for (int mt = 0; mt < MTA; ++mt) {
-      const half8 av = a_read(buf, mt, kk, lane);
-      acc[0][mt] = mfma32(av, bu, acc[0][mt]);
-      acc[1][mt] = mfma32(av, bg, acc[1][mt]);
+      for (int mt = 0; mt < MTA; ++mt) an[mt] = a_read(buf, mt, kk + 1, lane);
+    half8 bu[kUgTiles], bg[kUgTiles];
+#pragma unroll
+    for (int b = 0; b < kUgTiles; ++b) {
+      bu[b] = b_decode(cu[b], kk, tab);
+      bg[b] = b_decode(cg[b], kk, tab);
     }
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+      for (int b = 0; b < kUgTiles; ++b) {
+        acc[0][b][mt] = mfma32(av[mt], bu[b], acc[0][b][mt]);
+        acc[1][b][mt] = mfma32(av[mt], bg[b], acc[1][b][mt]);
+      }
+    if (kk + 1 < 16)
+#pragma unroll
+      for (int mt = 0; mt < MTA; ++mt) av[mt] = an[mt];
   }
 }
 
@@ -257,63 +278,76 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
   uint8_t* stage = smem + (FMT == MOE_FMT_CB2 ? kCb2CombBytes : 0);
   if (FMT == MOE_FMT_CB2) cb2_comb_fill(a.codebook, tab, reinterpret_cast<uint2*>(stage), tid, blockDim.x);
   const int n_rt = a.I / 16, n_chunks = a.H / 256, k = a.k;
-  const int rt0 = (nt * kUgRowsPerWg + wave * 32) / 16;
-  const bool active = rt0 < n_rt;
-  const int rt_l = min(rt0 + ((lane & 31) >> 4), n_rt - 1);            // clamped: loads stay in the matrix
+  const int row0 = nt * kUgRowsPerWg + wave * 32 * kUgTiles;          // the wave's first weight row
+  const bool active = row0 < a.I;
   const int tb = FMT == MOE_FMT_CB2 ? kCb2Tile : kK4Tile;
-  const uint8_t* tu = a.up + (size_t)e * a.expert_bytes + (size_t)rt_l * n_chunks * tb;
-  const uint8_t* tg = a.gate + (size_t)e * a.expert_bytes + (size_t)rt_l * n_chunks * tb;
+  const uint8_t* tu[kUgTiles];
+  const uint8_t* tg[kUgTiles];
+  for (int b = 0; b < kUgTiles; ++b) {
+    const int rt_l = min((row0 + 32 * b) / 16 + ((lane & 31) >> 4), n_rt - 1);   // clamped: loads stay in the matrix
+    tu[b] = a.up + (size_t)e * a.expert_bytes + (size_t)rt_l * n_chunks * tb;
+    tg[b] = a.gate + (size_t)e * a.expert_bytes + (size_t)rt_l * n_chunks * tb;
+  }
   using B = typename BRegs<FMT>::T;
 
   for (int64_t m0 = p_begin; m0 < p_end; m0 += kMRows) {
-    const int mta = (int)min((int64_t)kMT, (p_end - m0 + 31) / 32);
-    int rows[kDmaPerWave];
-    stage_rows(rows, m0, p_end, [&](int64_t p) { return (int64_t)(a.sorted_slots[p] / k); });
-    float16v acc[2][kMT];
-    for (int mt = 0; mt < kMT; ++mt) acc[0][mt] = acc[1][mt] = zero16v();
-    B cu, cg, nu, ng;
+    int rows[dma_per_wave<kUgWaves>()];
+    stage_rows<kUgWaves>(rows, m0, p_end, [&](int64_t p) { return (int64_t)(a.sorted_slots[p] / k); });
+    float16v acc[2][kUgTiles][kMT];
+    for (int b = 0; b < kUgTiles; ++b)
+      for (int mt = 0; mt < kMT; ++mt) acc[0][b][mt] = acc[1][b][mt] = zero16v();
+    B cu[kUgTiles], cg[kUgTiles], nu[kUgTiles], ng[kUgTiles];
     __syncthreads();                                                   // the last pass is done with the buffers
-    a_dma(stage, a.x16, a.H, rows, 0, a.H);
-    b_load(cu, tu, lane);
-    b_load(cg, tg, lane);
+    a_dma<kUgWaves>(stage, a.x16, a.H, rows, 0, a.H);
+    for (int b = 0; b < kUgTiles; ++b) {
+      b_load(cu[b], tu[b], lane);
+      b_load(cg[b], tg[b], lane);
+    }
     for (int chunk = 0; chunk < n_chunks; ++chunk) {
       const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
       chunk_sync();
       if (chunk + 1 < n_chunks) {
-        a_dma(stage + ((chunk + 1) & 1) * kChunkBytes, a.x16, a.H, rows, (chunk + 1) * 256, a.H);
-        b_load(nu, tu + (size_t)(chunk + 1) * tb, lane);
-        b_load(ng, tg + (size_t)(chunk + 1) * tb, lane);
+        a_dma<kUgWaves>(stage + ((chunk + 1) & 1) * kChunkBytes, a.x16, a.H, rows, (chunk + 1) * 256, a.H);
+        for (int b = 0; b < kUgTiles; ++b) {
+          b_load(nu[b], tu[b] + (size_t)(chunk + 1) * tb, lane);
+          b_load(ng[b], tg[b] + (size_t)(chunk + 1) * tb, lane);
+        }
       }
-      if (active) {
-        ug_steps<kMT>(acc, cu, cg, tab, buf, lane);
+      if (active) ug_steps<kMT>(acc, cu, cg, tab, buf, lane);
+      for (int b = 0; b < kUgTiles; ++b) {
+        cu[b] = nu[b];
+        cg[b] = ng[b];
       }
-      cu = nu;
-      cg = ng;
     }
     // epilogue: C[m][n], m = 8(i/4) + 4(l/32) + i%4, n = l%32
-    const int row = rt0 * 16 + (lane & 31);
-    if (active && row < a.I)
+    for (int b = 0; b < kUgTiles; ++b) {
+      const int row = row0 + 32 * b + (lane & 31);
+      if (row >= a.I) continue;
       for (int mt = 0; mt < kMT; ++mt)
         for (int i = 0; i < 16; ++i) {
           const int64_t p = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (p < p_end) a.h[p * a.I + row] = (_Float16)(silu(acc[1][mt][i]) * acc[0][mt][i]);
+          if (p < p_end) a.h[p * a.I + row] = (_Float16)(silu(acc[1][b][mt][i]) * acc[0][b][mt][i]);
         }
+    }
   }
 }
 
 // Up/gate, shared expert (bf16 x bf16 on bf16 matrix cores): one (96-token
-// chunk, 256-row N-tile of I_s) per workgroup.  Weights stream a quarter
-// chunk (4 steps) at a time, the next quarter's loads in flight.
+// chunk, 256-row N-tile of I_s) per workgroup.  Weights stream two steps at
+// a time, the next two steps' loads in flight.
 template <int MTA>
-__device__ __forceinline__ void ug_shared_steps(float16v (&acc)[2][kMT], const u32x4 (&cu)[4], const u32x4 (&cg)[4],
-                                                const uint8_t* buf, int q0, int lane) {
+__device__ __forceinline__ void ug_shared_steps(float16v (&acc)[2][kUgTiles][kMT], const u32x4 (&cu)[kUgTiles][2],
+                                                const u32x4 (&cg)[kUgTiles][2], const uint8_t* buf, int k0, int lane) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt) {
-      const u32x4 av = as_u32x4(a_read(buf, mt, q0 + q, lane));
-      acc[0][mt] = mfma32_bf(av, cu[q], acc[0][mt]);
-      acc[1][mt] = mfma32_bf(av, cg[q], acc[1][mt]);
+      const u32x4 av = as_u32x4(a_read(buf, mt, k0 + q, lane));
+#pragma unroll
+      for (int b = 0; b < kUgTiles; ++b) {
+        acc[0][b][mt] = mfma32_bf(av, cu[b][q], acc[0][b][mt]);
+        acc[1][b][mt] = mfma32_bf(av, cg[b][q], acc[1][b][mt]);
+      }
     }
 }
 
@@ -323,54 +357,65 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint8_t* stage = smem;
   const int n_rt = a.Is / 16, n_chunks = a.H / 256;
-  const int rt0 = (nt * kUgRowsPerWg + wave * 32) / 16;
-  const bool active = rt0 < n_rt;
-  const int rt_l = min(rt0 + ((lane & 31) >> 4), n_rt - 1);
-  const uint8_t* tu = a.sup + (size_t)rt_l * n_chunks * kBf16Tile;
-  const uint8_t* tg = a.sgate + (size_t)rt_l * n_chunks * kBf16Tile;
-  const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
-  int rows[kDmaPerWave];
-  stage_rows(rows, p_begin, p_end, [](int64_t p) { return p; });
-  float16v acc[2][kMT];
-  for (int mt = 0; mt < kMT; ++mt) acc[0][mt] = acc[1][mt] = zero16v();
-  u32x4 cu[4], cg[4], nu[4], ng[4];
-  a_dma(stage, a.x, a.H, rows, 0, a.H);
-  for (int q = 0; q < 4; ++q) {
-    cu[q] = bf16_piece(tu, q, lane);
-    cg[q] = bf16_piece(tg, q, lane);
+  const int row0 = nt * kUgRowsPerWg + wave * 32 * kUgTiles;
+  const bool active = row0 < a.Is;
+  const uint8_t* tu[kUgTiles];
+  const uint8_t* tg[kUgTiles];
+  for (int b = 0; b < kUgTiles; ++b) {
+    const int rt_l = min((row0 + 32 * b) / 16 + ((lane & 31) >> 4), n_rt - 1);
+    tu[b] = a.sup + (size_t)rt_l * n_chunks * kBf16Tile;
+    tg[b] = a.sgate + (size_t)rt_l * n_chunks * kBf16Tile;
   }
-  const int n_quarters = 4 * n_chunks;
-  for (int gq = 0; gq < n_quarters; ++gq) {
-    const int chunk = gq >> 2, q0 = 4 * (gq & 3);
-    const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
-    if ((gq & 3) == 0) {
-      chunk_sync();
-      if (chunk + 1 < n_chunks) a_dma(stage + ((chunk + 1) & 1) * kChunkBytes, a.x, a.H, rows, (chunk + 1) * 256, a.H);
+  const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
+  int rows[dma_per_wave<kUgWaves>()];
+  stage_rows<kUgWaves>(rows, p_begin, p_end, [](int64_t p) { return p; });
+  float16v acc[2][kUgTiles][kMT];
+  for (int b = 0; b < kUgTiles; ++b)
+    for (int mt = 0; mt < kMT; ++mt) acc[0][b][mt] = acc[1][b][mt] = zero16v();
+  u32x4 cu[kUgTiles][2], cg[kUgTiles][2], nu[kUgTiles][2], ng[kUgTiles][2];
+  __syncthreads();
+  a_dma<kUgWaves>(stage, a.x, a.H, rows, 0, a.H);
+  for (int b = 0; b < kUgTiles; ++b)
+    for (int q = 0; q < 2; ++q) {
+      cu[b][q] = bf16_piece(tu[b], q, lane);
+      cg[b][q] = bf16_piece(tg[b], q, lane);
     }
-    if (gq + 1 < n_quarters) {
-      const int c1 = (gq + 1) >> 2, k1 = 4 * ((gq + 1) & 3);
-      for (int q = 0; q < 4; ++q) {
-        nu[q] = bf16_piece(tu + (size_t)c1 * kBf16Tile, k1 + q, lane);
-        ng[q] = bf16_piece(tg + (size_t)c1 * kBf16Tile, k1 + q, lane);
-      }
+  const int n_pairs = 8 * n_chunks;
+  for (int gp = 0; gp < n_pairs; ++gp) {
+    const int chunk = gp >> 3, k0 = 2 * (gp & 7);
+    const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
+    if ((gp & 7) == 0) {
+      chunk_sync();
+      if (chunk + 1 < n_chunks) a_dma<kUgWaves>(stage + ((chunk + 1) & 1) * kChunkBytes, a.x, a.H, rows, (chunk + 1) * 256, a.H);
+    }
+    if (gp + 1 < n_pairs) {
+      const int c1 = (gp + 1) >> 3, k1 = 2 * ((gp + 1) & 7);
+      for (int b = 0; b < kUgTiles; ++b)
+        for (int q = 0; q < 2; ++q) {
+          nu[b][q] = bf16_piece(tu[b] + (size_t)c1 * kBf16Tile, k1 + q, lane);
+          ng[b][q] = bf16_piece(tg[b] + (size_t)c1 * kBf16Tile, k1 + q, lane);
+        }
     }
     if (active) {
-      if (mta >= 3) ug_shared_steps<3>(acc, cu, cg, buf, q0, lane);
-      else if (mta == 2) ug_shared_steps<2>(acc, cu, cg, buf, q0, lane);
-      else ug_shared_steps<1>(acc, cu, cg, buf, q0, lane);
+      if (mta >= 3) ug_shared_steps<3>(acc, cu, cg, buf, k0, lane);
+      else if (mta == 2) ug_shared_steps<2>(acc, cu, cg, buf, k0, lane);
+      else ug_shared_steps<1>(acc, cu, cg, buf, k0, lane);
     }
-    for (int q = 0; q < 4; ++q) {
-      cu[q] = nu[q];
-      cg[q] = ng[q];
-    }
+    for (int b = 0; b < kUgTiles; ++b)
+      for (int q = 0; q < 2; ++q) {
+        cu[b][q] = nu[b][q];
+        cg[b][q] = ng[b][q];
+      }
   }
-  const int row = rt0 * 16 + (lane & 31);
-  if (active && row < a.Is)
+  for (int b = 0; b < kUgTiles; ++b) {
+    const int row = row0 + 32 * b + (lane & 31);
+    if (row >= a.Is) continue;
     for (int mt = 0; mt < kMT; ++mt)
       for (int i = 0; i < 16; ++i) {
         const int64_t p = p_begin + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (p < p_end) a.hs[p * a.Is + row] = (_Float16)(silu(acc[1][mt][i]) * acc[0][mt][i]);
+        if (p < p_end) a.hs[p * a.Is + row] = (_Float16)(silu(acc[1][b][mt][i]) * acc[0][b][mt][i]);
       }
+  }
 }
 
 // Workgroup -> (N-tile nt, group g) over a 1-D grid of n_nt * roundup(G, 8)
@@ -389,7 +434,7 @@ __device__ __forceinline__ bool pf_tile(int n_nt, int n_groups, int& nt, int& g)
 __host__ __device__ inline int pf_shared_chunks(const PfArgs& a) { return a.Is > 0 ? (a.T + kMRows - 1) / kMRows : 0; }
 
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void pf_upgate_kernel(PfArgs a) {
+__global__ __launch_bounds__(64 * kUgWaves) void pf_upgate_kernel(PfArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int n_sh = pf_shared_chunks(a);
   const int n_nt = ((a.Is > a.I ? a.Is : a.I) + kUgRowsPerWg - 1) / kUgRowsPerWg;
@@ -467,20 +512,20 @@ __device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e,
   using B = typename BRegs<FMT>::T;
   for (int64_t m0 = p_begin; m0 < p_end; m0 += kMRows) {
     const int mta = (int)min((int64_t)kMT, (p_end - m0 + 31) / 32);
-    int rows[kDmaPerWave];
-    stage_rows(rows, m0, p_end, [](int64_t p) { return p; });
+    int rows[dma_per_wave<kDnWaves>()];
+    stage_rows<kDnWaves>(rows, m0, p_end, [](int64_t p) { return p; });
     float16v acc[kDnTiles][kMT];
     for (int b = 0; b < kDnTiles; ++b)
       for (int mt = 0; mt < kMT; ++mt) acc[b][mt] = zero16v();
     B cur[kDnTiles], nxt[kDnTiles];
     __syncthreads();
-    a_dma(stage, hsrc, a.I, rows, 0, a.I);
+    a_dma<kDnWaves>(stage, hsrc, a.I, rows, 0, a.I);
     for (int b = 0; b < kDnTiles; ++b) b_load(cur[b], tp[b], lane);
     for (int chunk = 0; chunk < n_chunks; ++chunk) {
       const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
       chunk_sync();
       if (chunk + 1 < n_chunks) {
-        a_dma(stage + ((chunk + 1) & 1) * kChunkBytes, hsrc, a.I, rows, (chunk + 1) * 256, a.I);
+        a_dma<kDnWaves>(stage + ((chunk + 1) & 1) * kChunkBytes, hsrc, a.I, rows, (chunk + 1) * 256, a.I);
         for (int b = 0; b < kDnTiles; ++b) b_load(nxt[b], tp[b] + (size_t)(chunk + 1) * tb, lane);
       }
       if (mta >= 3) dn_steps<FMT, 3>(acc, cur, buf, lane);
@@ -532,12 +577,12 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
   }
   const uint16_t* hsrc = reinterpret_cast<const uint16_t*>(a.hs);
   const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
-  int rows[kDmaPerWave];
-  stage_rows(rows, p_begin, p_end, [](int64_t p) { return p; });
+  int rows[dma_per_wave<kDnWaves>()];
+  stage_rows<kDnWaves>(rows, p_begin, p_end, [](int64_t p) { return p; });
   float16v acc[kDnTiles][kMT];
   for (int b = 0; b < kDnTiles; ++b)
     for (int mt = 0; mt < kMT; ++mt) acc[b][mt] = zero16v();
-  a_dma(stage, hsrc, a.Is, rows, 0, a.Is);
+  a_dma<kDnWaves>(stage, hsrc, a.Is, rows, 0, a.Is);
   u32x4 cw[kDnTiles][4], nw[kDnTiles][4];
   for (int b = 0; b < kDnTiles; ++b)
     for (int q = 0; q < 4; ++q) cw[b][q] = bf16_piece(tp[b], q, lane);
@@ -547,7 +592,7 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
     const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
     if ((gq & 3) == 0) {
       chunk_sync();
-      if (chunk + 1 < n_chunks) a_dma(stage + ((chunk + 1) & 1) * kChunkBytes, hsrc, a.Is, rows, (chunk + 1) * 256, a.Is);
+      if (chunk + 1 < n_chunks) a_dma<kDnWaves>(stage + ((chunk + 1) & 1) * kChunkBytes, hsrc, a.Is, rows, (chunk + 1) * 256, a.Is);
     }
     if (gq + 1 < n_quarters) {
       const int c1 = (gq + 1) >> 2, k1 = 4 * ((gq + 1) & 3);
@@ -572,7 +617,7 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void pf_down_kernel(PfArgs a) {
+__global__ __launch_bounds__(64 * kDnWaves) void pf_down_kernel(PfArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int n_sh = pf_shared_chunks(a);
   const int n_nt = (a.H + kDnRowsPerWg - 1) / kDnRowsPerWg;
@@ -626,7 +671,6 @@ int pf_m_rows() { return kMRows; }
 hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,
                           hipStream_t s) {
   const int n_groups8 = (a.E + pf_shared_chunks(a) + 7) / 8 * 8;
-  const dim3 block(kThreads);
   {
     const int64_t n8 = (int64_t)a.T * a.H / 8;
     hipLaunchKernelGGL(pf_x16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a.x,
@@ -641,7 +685,8 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
     void (*fn)(PfArgs) = fmt_ug == MOE_FMT_CB2 ? pf_upgate_kernel<MOE_FMT_CB2> : pf_upgate_kernel<MOE_FMT_K4>;
     hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
-    err = launch_timed(MOE_KERNEL_PREFILL_UPGATE, s, [&] { hipLaunchKernelGGL(fn, grid, block, lds, s, a); });
+    err = launch_timed(MOE_KERNEL_PREFILL_UPGATE, s,
+                       [&] { hipLaunchKernelGGL(fn, grid, dim3(64 * kUgWaves), lds, s, a); });
     if (err != hipSuccess) return err;
   }
   {
@@ -650,7 +695,7 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
     hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
     err = launch_timed(MOE_KERNEL_PREFILL_DOWN, s,
-                       [&] { hipLaunchKernelGGL(fn, grid, block, (size_t)kStageBytes, s, a); });
+                       [&] { hipLaunchKernelGGL(fn, grid, dim3(64 * kDnWaves), (size_t)kStageBytes, s, a); });
     if (err != hipSuccess) return err;
   }
   return launch_timed(MOE_KERNEL_PREFILL_COMBINE, s, [&] {
