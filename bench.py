@@ -41,10 +41,10 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # of the kernel sources it was measured on: when the sources differ, the figure
 # no longer describes the kernel and "traffic" is reported as null.
 MEASURED_TRAFFIC = {
-    ("decode_b1", "decode_upgate"): ("4730e0165db532f2:59c3bfc54c94cebc", 76.17e6 + 0.049e6),
-    ("decode_b1", "decode_down"): ("4730e0165db532f2:59c3bfc54c94cebc", 39.36e6 + 0.016e6),
-    ("prefill_2048", "prefill_upgate"): ("6718c2c857356488:59c3bfc54c94cebc", 2489.82e6 + 75.497e6),
-    ("prefill_2048", "prefill_down"): ("6718c2c857356488:59c3bfc54c94cebc", 1337.68e6 + 301.990e6),
+    ("decode_b1", "decode_upgate"): ("03bd242191549005:66c6882cc36e9a40", 76.18e6 + 0.049e6),
+    ("decode_b1", "decode_down"): ("03bd242191549005:66c6882cc36e9a40", 39.36e6 + 0.016e6),
+    ("prefill_2048", "prefill_upgate"): ("c4406cda7635d819:66c6882cc36e9a40", 1761.91e6 + 75.497e6),
+    ("prefill_2048", "prefill_down"): ("c4406cda7635d819:66c6882cc36e9a40", 1015.62e6 + 301.990e6),
 }
 TRAFFIC_SOURCES = {"decode": ["k_decode1.hip", "device_common.hpp"], "prefill": ["k_prefill.hip", "device_common.hpp"]}
 
