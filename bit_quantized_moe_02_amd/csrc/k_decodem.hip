@@ -257,6 +257,7 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
   float* red = reinterpret_cast<float*>(smem + (size_t)16 * kmax * 2);       // [kDnR][NW][64][4]
   ExpertList* L = reinterpret_cast<ExpertList*>(red + kDnR * NW * 256);
   int* slot_of = reinterpret_cast<int*>(L + 1);                              // [16] slot of token m (or -1)
+  uint32_t* slot_bits = reinterpret_cast<uint32_t*>(slot_of + 16);           // [16] choices j of token m
 
   const int n_rt = a.H / 16, n_rts = a.Is > 0 ? a.H / 16 : 0;
   const int m = lane & 15, qq = lane >> 4, n = lane & 15;
@@ -273,15 +274,20 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
     const int K = d < 0 ? a.Is : a.I, Kp = d < 0 ? a.Is_pad : a.I_pad;
     if (tid < 16) {
       int sl = -1;
+      uint32_t bits = 0;
       if (tid < T) {
         if (d < 0) {
           sl = tid;
         } else if ((L->mask[d] >> tid) & 1u) {
           for (int j = 0; j < k; ++j)
-            if (L->slot_e[tid * k + j] == L->expert[d]) sl = tid * k + j;
+            if (L->slot_e[tid * k + j] == L->expert[d]) {
+              sl = tid * k + j;
+              bits |= 1u << j;
+            }
         }
       }
       slot_of[tid] = sl;
+      slot_bits[tid] = bits;
     }
     __syncthreads();
     const _Float16* src = d < 0 ? a.hs : a.h;
@@ -297,8 +303,9 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
   };
 
   // reduce `cnt` row tiles (first one rt0) over the first n_waves waves and
-  // write their rows: shared ones to ysh, routed ones to ybuf
-  auto finish = [&](const float4v* acc, int cnt, int64_t rt0, int n_waves, bool shared) {
+  // write their rows: shared ones (e < 0) to ysh, routed ones of expert e to
+  // ybuf at every slot of the token that chose the staged expert
+  auto finish = [&](const float4v* acc, int cnt, int64_t rt0, int n_waves, int e) {
     for (int j = 0; j < kDnR; ++j)
       if (j < cnt) *reinterpret_cast<float4v*>(red + ((j * NW + wave) * 64 + lane) * 4) = acc[j];
     __syncthreads();
@@ -310,8 +317,12 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
       const int sl = slot_of[mm];
       if (sl >= 0) {
         const size_t row = (size_t)(rt0 + j) * 16 + nn;
-        if (shared) a.ysh[(size_t)mm * a.H + row] = v;
-        else a.ybuf[(size_t)sl * a.H + row] = v;
+        if (e < 0) {
+          a.ysh[(size_t)mm * a.H + row] = v;
+        } else {
+          for (uint32_t bits = slot_bits[mm]; bits; bits &= bits - 1u)
+            a.ybuf[(size_t)(mm * k + __builtin_ctz(bits)) * a.H + row] = v;
+        }
       }
     }
     __syncthreads();
@@ -332,7 +343,7 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
         acc[0] = mfma_f16(av, bf16x8_to_half8(raw[kb]), acc[0]);
       }
     }
-    finish(acc, 1, item, n_cks, true);
+    finish(acc, 1, item, n_cks, -1);
   }
 
   // routed rounds, the next round's weights in flight
@@ -376,7 +387,7 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
         for (int j = 0; j < kDnR; ++j)
           if (j < cnt) acc[j] = mfma_f16(A[kb], k2_scaled_b(P.q[j], P.scm[j], P.dd[j], kb, qq), acc[j]);
     }
-    finish(acc, cnt, rt0, n_ck, false);
+    finish(acc, cnt, rt0, n_ck, L->expert[d]);
   };
   DnRound P0, P1;
   int d0 = 0, rt0 = 0, d1 = 0, rt1 = 0;
@@ -429,7 +440,7 @@ size_t decm_upgate_lds(int nw) {
 
 size_t decm_down_lds(const DecArgs& a, int nw) {
   const size_t kmax = (size_t)(a.I_pad > a.Is_pad ? a.I_pad : a.Is_pad);
-  return 16 * kmax * 2 + (size_t)kDnR * nw * 256 * 4 + sizeof(ExpertList) + 16 * 4;
+  return 16 * kmax * 2 + (size_t)kDnR * nw * 256 * 4 + sizeof(ExpertList) + 16 * 4 + 16 * 4;
 }
 
 hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus, hipStream_t s) {

@@ -213,8 +213,10 @@ size_t moe_ffn_workspace_bytes(const moe_weights* w, int32_t T, int32_t k, int p
  *   decodes the weights exactly (scales applied to fp32 block sums); for
  *   T >= 2 a layer with CB2 up/gate, hidden <= 4096 and inter, shared_inter
  *   <= 2048 takes kernels that fold the scales into fp16 weights (one
- *   rounding per weight, as moe_expert_ffn_prefill does).  The first bytes
- *   of ws hold h as fp16 [T*k, inter] (slot order) after the call.  Limits:
+ *   rounding per weight, as moe_expert_ffn_prefill does).  A choice whose
+ *   expert id lies outside [0, E) contributes nothing; a token may name one
+ *   expert in several choices (each contributes).  The first bytes of ws
+ *   hold h as fp16 [T*k, inter] (slot order) after the call.  Limits:
  *   1 <= T <= 16, 1 <= k <= 16. */
 int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
                           const int32_t* topk_idx, const float* topk_w, float* y,

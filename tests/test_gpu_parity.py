@@ -335,6 +335,46 @@ def test_decode_single_token_odd_shapes(q, wl):
         assert rel_err(y1.cpu().numpy(), y2.cpu().numpy()[t:t + 1]).max() <= tol
 
 
+@pytest.mark.parametrize("wl,T", [(synth.WORKLOADS["tiny"], 4), (synth.WORKLOADS["tiny"], 1), (ODD_K4, 1),
+                                  (ODD_CB2, 3)], ids=["tiny_T4", "tiny_T1", "odd_k4_T1", "odd_cb2_T3"])
+def test_decode_invalid_and_repeated_ids(q, wl, T):
+    """Choices with an expert id outside [0, E) contribute nothing; a token
+    that names one expert twice gets both contributions."""
+    import torch
+    from layer_fixture import oracle_expert, oracle_shared
+    print(f"decode ids {wl.name} T={T}", flush=True)
+    layer = device_layer(wl)
+    xb, x64 = x_bits(wl, T, step=11)
+    idx, w = _route(q, layer, xb, wl.top_k)
+    ih = idx.cpu().numpy().copy()
+    wh = w.cpu().numpy()
+    ih[0, -1] = -1
+    if T > 1:
+        ih[T - 1, 0] = wl.n_experts
+        ih[1, 1] = ih[1, 0]
+    else:
+        ih[0, 1] = ih[0, 0]
+    idx2 = torch.from_numpy(ih).cuda()
+    y, _ = _decode(q, layer, xb, idx2, w, wl.top_k)
+    sh = oracle_shared(wl)
+    y_ref = np.zeros((T, wl.hidden))
+    for t in range(T):
+        for j in range(wl.top_k):
+            e = int(ih[t, j])
+            if 0 <= e < wl.n_experts:
+                y_ref[t] += float(wh[t, j]) * O.expert_ffn(x64[t:t + 1], *oracle_expert(wl, e))[0]
+        if sh is not None:
+            y_ref[t] += O.expert_ffn(x64[t:t + 1], *sh)[0]
+    err = rel_err(y.cpu().numpy(), y_ref)
+    print(f"max rel err: {err.max():.3e}")
+    assert err.max() <= TOL_LAYER, err
+    # the same choices through grouping and the prefill kernels
+    yp, _, _ = _prefill(q, layer, xb, idx2, w, wl.top_k)
+    errp = rel_err(yp.cpu().numpy(), y_ref)
+    print(f"prefill max rel err: {errp.max():.3e}")
+    assert errp.max() <= TOL_LAYER, errp
+
+
 def test_decode_16_tokens_skewed(q):
     print("decode_b16_hot", flush=True)
     wl = synth.WORKLOADS["decode_b16_hot"]
