@@ -121,31 +121,45 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* topk_idx, in
     tot[e] = run;
   }
   __syncthreads();
-  // exclusive scan of the totals, in expert order
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
+  // exclusive scan of the totals in expert order, by wave 0: lane l sums
+  // experts [l*P, l*P + P), the lane sums are scanned across the wave
+  if (wave == 0) {
+    const int P = (E + 63) / 64, e0 = lane * P, e1 = min(E, e0 + P);
+    int part = 0;
+    for (int e = e0; e < e1; ++e) part += tot[e];
+    int incl = part;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - part;
+    for (int e = e0; e < e1; ++e) {
       const int c = tot[e];
       tot[e] = run;
       offsets[e] = run;
       run += c;
     }
-    tot[E] = run;
-    offsets[E] = run;
+    if (lane == 63) {
+      tot[E] = incl;
+      offsets[E] = incl;
+    }
   }
   __syncthreads();
+  const int id_bits = 32 - __builtin_clz((unsigned)(E > 1 ? E - 1 : 1));   // bits of an id in [0, E)
   for (int c0 = s0; c0 < s1; c0 += 64) {
     const int s = c0 + lane;
     const int e = (s < s1) ? topk_idx[s] : -1;
     const bool valid = e >= 0 && e < E;
-    int rank = 0, same = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __shfl(e, j);
-      if (ej == e) {
-        if (j < lane) ++rank;
-        ++same;
-      }
+    // lanes holding the same id: intersect, bit by bit, the ballots of the
+    // lanes that agree with this lane's id bit
+    uint64_t match = ~0ull;
+    for (int b = 0; b < id_bits; ++b) {
+      const uint64_t ones = __ballot((e >> b) & 1);
+      match &= ((e >> b) & 1) ? ones : ~ones;
     }
+    match &= __ballot(valid);
+    const int rank = __popcll(match & ((1ull << lane) - 1ull));
+    const int same = __popcll(match);
     int cursor = 0;
     if (valid) cursor = cnt[wave * E + e];
     if (valid) {
