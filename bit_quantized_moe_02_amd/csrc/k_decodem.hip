@@ -13,9 +13,12 @@
 // not choose the expert are computed and dropped.  K is split over the waves
 // of a workgroup (one 256-column chunk each) and the partial sums meet in LDS
 // in wave order (fixed order, no atomics); the next item's weights are in
-// flight while the current one is multiplied.  Weights are dequantized to
+// flight while the current one is multiplied.  CB2 up/gate weights become
 // fp16 B operands with their scales folded in (one fp16 rounding per
-// weight), as in the prefill kernels.
+// weight), as in the prefill kernels.  K2 down weights stay exact: the B
+// operands are the integers q * sc, and per item and chunk the result is
+// d * (h . q sc) - dmin * (sum over sub-blocks of m * X), X being the
+// sub-block sums of the staged h rows (as fp16 hi + lo).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,6 +35,7 @@ using qmoe::DecArgs;
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMRB = 2;      // items per cross-wave reduction (up/gate)
 
@@ -49,27 +53,42 @@ __device__ __forceinline__ half8 cb2_scaled_b(const u32x4& codes, const u32x4& s
   return v * s;
 }
 
-// K2 B operand of lane (qq, n) for k-block kb (sub-block 2 kb + qq/2): q
-// exactly from the magic value, then q * d*sc - dmin*m as one fp32 fma (d*sc
-// and dmin*m are exact in fp32) rounded to fp16: the fp16 value of the
-// dequantized weight.
-__device__ __forceinline__ half8 k2_scaled_b(const u32x4& qw, const u32x4& scm, uint32_t dd, int kb, int qq) {
+// K2 B operand of lane (qq, n) for k-block kb as the exact integers q * sc
+// (sc = the 4-bit scale of the lane's sub-block 2 kb + qq/2): the magic value
+// 1024 * 4^t + q * 4^t times sc * 4^-t, minus 1024 * sc * 4^-t, in one fp16
+// fma whose exact result is an integer <= 45.
+__device__ __forceinline__ half8 k2_qsc_b(const u32x4& qw, const u32x4& scm, int kb, int qq) {
   const half8 mg = as_half8(k2_magic(qw, kb));
   const int sb = 2 * kb + (qq >> 1);
-  const uint32_t byte = (scm[sb >> 2] >> (8 * (sb & 3))) & 0xFFu;
-  const float dsc = h2f(dd & 0xFFFFu) * (float)(byte & 15u);
-  const float ndm = -(h2f(dd >> 16) * (float)(byte >> 4));
+  const _Float16 sc = (_Float16)(float)((scm[sb >> 2] >> (8 * (sb & 3))) & 15u);
+  // per slot pair: a = sc * 4^-t, b = -1024 a (packed two slots at a time)
+  half2v a[2], b[2];
+  for (int p = 0; p < 2; ++p) {
+    const half2v pw = {(_Float16)__builtin_ldexpf(1.0f, -2 * k2_slot_t(kb, 2 * p)),
+                       (_Float16)__builtin_ldexpf(1.0f, -2 * k2_slot_t(kb, 2 * p + 1))};
+    a[p] = half2v{sc, sc} * pw;
+    b[p] = a[p] * half2v{(_Float16)(-1024.0f), (_Float16)(-1024.0f)};
+  }
   half8 w;
   for (int s = 0; s < 4; ++s) {
-    const int t = k2_slot_t(kb, s);
-    const _Float16 sc = (_Float16)__builtin_ldexpf(1.0f, -2 * t);
-    const _Float16 off = (_Float16)(-1024.0f * __builtin_ldexpf(1.0f, -2 * t));
-    const _Float16 q0 = mg[2 * s] * sc + off;
-    const _Float16 q1 = mg[2 * s + 1] * sc + off;
-    w[2 * s] = (_Float16)__builtin_fmaf((float)q0, dsc, ndm);
-    w[2 * s + 1] = (_Float16)__builtin_fmaf((float)q1, dsc, ndm);
+    const half2v as = {a[s >> 1][s & 1], a[s >> 1][s & 1]}, bs = {b[s >> 1][s & 1], b[s >> 1][s & 1]};
+    const half2v r = half2v{mg[2 * s], mg[2 * s + 1]} * as + bs;
+    w[2 * s] = r[0];
+    w[2 * s + 1] = r[1];
   }
   return w;
+}
+
+// Min-term B operand of a 16x16x16 MFMA over the 16 sub-blocks of a chunk:
+// lane (g, n) holds the 4-bit mins m of sub-blocks 4g .. 4g+3 of row n.
+__device__ __forceinline__ half4 k2_min_b(const u32x4& scm, int g) {
+  const uint32_t w = scm[g];                       // bytes sc | m << 4 of sub-blocks 4g .. 4g+3
+  const uint32_t lo = ((w >> 4) & 0xFu) | ((w >> 12) & 0xFu) << 16;
+  const uint32_t hi = ((w >> 20) & 0xFu) | ((w >> 28) & 0xFu) << 16;
+  const half2v off = {(_Float16)(-1024.0f), (_Float16)(-1024.0f)};
+  const half2v m01 = __builtin_bit_cast(half2v, lo | 0x64006400u) + off;
+  const half2v m23 = __builtin_bit_cast(half2v, hi | 0x64006400u) + off;
+  return half4{m01[0], m01[1], m23[0], m23[1]};
 }
 
 // ---------------------------------------------------------------------------
@@ -258,6 +277,9 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
   ExpertList* L = reinterpret_cast<ExpertList*>(red + kDnR * NW * 256);
   int* slot_of = reinterpret_cast<int*>(L + 1);                              // [16] slot of token m (or -1)
   uint32_t* slot_bits = reinterpret_cast<uint32_t*>(slot_of + 16);           // [16] choices j of token m
+  _Float16* xsb = reinterpret_cast<_Float16*>((reinterpret_cast<uintptr_t>(slot_bits + 16) + 15) &
+                                               ~(uintptr_t)15);               // [2][16][kmax/16] hi, lo
+  const int nsb = kmax / 16;                                                  // sub-blocks per staged row
 
   const int n_rt = a.H / 16, n_rts = a.Is > 0 ? a.H / 16 : 0;
   const int m = lane & 15, qq = lane >> 4, n = lane & 15;
@@ -300,6 +322,21 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
       *reinterpret_cast<u32x4*>(hA + (size_t)mm * kmax + 8 * c) = v;
     }
     __syncthreads();
+    if (d >= 0) {
+      // sums X of each row over each 16-column sub-block, as fp16 hi + lo
+      for (int i = tid; i < 16 * (Kp / 16); i += blockDim.x) {
+        const int mm = i / (Kp / 16), sb = i - mm * (Kp / 16);
+        const half8 v0 = *reinterpret_cast<const half8*>(hA + (size_t)mm * kmax + 16 * sb);
+        const half8 v1 = *reinterpret_cast<const half8*>(hA + (size_t)mm * kmax + 16 * sb + 8);
+        float x = 0.f;
+        for (int j = 0; j < 8; ++j) x += (float)v0[j];
+        for (int j = 0; j < 8; ++j) x += (float)v1[j];
+        const _Float16 xh = (_Float16)x;
+        xsb[(size_t)mm * nsb + sb] = xh;
+        xsb[(size_t)(16 + mm) * nsb + sb] = (_Float16)(x - (float)xh);
+      }
+      __syncthreads();
+    }
   };
 
   // reduce `cnt` row tiles (first one rt0) over the first n_waves waves and
@@ -381,11 +418,26 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
 #pragma unroll
     for (int j = 0; j < kDnR; ++j) acc[j] = zero;
     if (r_active) {
+      // sum_k h w = d sum_k h (q sc) - dmin sum_sb m X_sb: the q sc dots on
+      // the f16 matrix cores (exact operands), the min term as one
+      // 16x16x16 product of the sub-block sums (hi + lo) with the mins
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
         for (int j = 0; j < kDnR; ++j)
-          if (j < cnt) acc[j] = mfma_f16(A[kb], k2_scaled_b(P.q[j], P.scm[j], P.dd[j], kb, qq), acc[j]);
+          if (j < cnt) acc[j] = mfma_f16(A[kb], k2_qsc_b(P.q[j], P.scm[j], kb, qq), acc[j]);
+      const int g = lane >> 4;
+      const half4 xh = *reinterpret_cast<const half4*>(xsb + (size_t)m * nsb + 16 * chunk + 4 * g);
+      const half4 xl = *reinterpret_cast<const half4*>(xsb + (size_t)(16 + m) * nsb + 16 * chunk + 4 * g);
+#pragma unroll
+      for (int j = 0; j < kDnR; ++j)
+        if (j < cnt) {
+          const half4 mb = k2_min_b(P.scm[j], g);
+          float4v cm = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, mb, zero, 0, 0, 0);
+          cm = __builtin_amdgcn_mfma_f32_16x16x16f16(xl, mb, cm, 0, 0, 0);
+          const float dd = h2f(P.dd[j] & 0xFFFFu), dm = h2f(P.dd[j] >> 16);
+          for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(dd, acc[j][i], -dm * cm[i]);
+        }
     }
     finish(acc, cnt, rt0, n_ck, L->expert[d]);
   };
@@ -440,7 +492,8 @@ size_t decm_upgate_lds(int nw) {
 
 size_t decm_down_lds(const DecArgs& a, int nw) {
   const size_t kmax = (size_t)(a.I_pad > a.Is_pad ? a.I_pad : a.Is_pad);
-  return 16 * kmax * 2 + (size_t)kDnR * nw * 256 * 4 + sizeof(ExpertList) + 16 * 4 + 16 * 4;
+  return 16 * kmax * 2 + (size_t)kDnR * nw * 256 * 4 + sizeof(ExpertList) + 16 * 4 + 16 * 4 +
+         16 + 2 * 16 * (kmax / 16) * 2;
 }
 
 hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus, hipStream_t s) {

@@ -240,23 +240,27 @@ def test_group_counts_invalid_ids(q):
 
 
 def _multi_token_rounds_weights(wl, T):
-    """True where the multi-token decode kernels take this layer: they fold the
-    block scales into fp16 weights (one rounding per weight), as prefill does."""
-    return (T >= 2 and wl.fmt_up == "cb2" and wl.hidden <= 4096 and wl.inter <= 2048
-            and wl.shared_inter <= 2048)
+    """The matrices whose weights the multi-token decode kernels round to fp16
+    for this layer: the CB2 up/gate of the batched kernels (scales folded in,
+    one rounding per weight); their K2 down keeps exact weights."""
+    batched = (T >= 2 and wl.fmt_up == "cb2" and wl.hidden <= 4096 and wl.inter <= 2048
+               and wl.shared_inter <= 2048)
+    return (0, 1) if batched else ()
 
 
-def _check_layer(y, wl, x64, expect_idx=None, mirror_tol=None, round_w=False):
+def _check_layer(y, wl, x64, expect_idx=None, mirror_tol=None, round_w=()):
     y_ref, o_idx, _ = oracle_layer(wl, x64)
     err = rel_err(y, y_ref)
     print(f"max rel err vs fp64 oracle: {err.max():.3e} (tokens {len(err)})")
     assert err.max() <= TOL_LAYER, err
     if mirror_tol is not None:
         if round_w:
-            # routed weights rounded to fp16 as the kernels hold them; the
-            # shared expert's bf16 weights are exact in either form
+            # routed weights (matrices round_w: 0 up, 1 gate, 2 down) rounded
+            # to fp16 as the kernels hold them; the shared expert's bf16
+            # weights are exact in either form
             y_m, _, _ = O.moe_layer(x64, synth.router_weight(wl), synth.logit_bias(wl), wl.top_k,
-                                    lambda e: tuple(O.f16(m) for m in oracle_expert(wl, e)),
+                                    lambda e: tuple(O.f16(m) if i in round_w else m
+                                                    for i, m in enumerate(oracle_expert(wl, e))),
                                     shared=oracle_shared(wl), round_h=_mirror_h)
         else:
             y_m, _, _ = oracle_layer(wl, x64, round_h=_mirror_h)
@@ -417,7 +421,7 @@ def test_prefill_full_layer(q, name):
     xb, x64 = x_bits(wl, wl.tokens)
     idx, w = _route(q, layer, xb, wl.top_k)
     y, _, _ = _prefill(q, layer, xb, idx, w, wl.top_k)
-    _check_layer(y.cpu().numpy(), wl, x64, mirror_tol=2e-4, round_w=True)
+    _check_layer(y.cpu().numpy(), wl, x64, mirror_tol=2e-4, round_w=(0, 1, 2))
     # the same tokens through the decode path, 16 at a time
     if wl.tokens <= 16:
         yd, _ = _decode(q, layer, xb, idx, w, wl.top_k)
@@ -438,7 +442,7 @@ def test_prefill_full_size_sampled(q, name, n_sample):
     y, _, _ = _prefill(q, layer, xb, idx, w, wl.top_k)
     ys = y.cpu().numpy()
     assert np.all(np.isfinite(ys))
-    _check_layer(ys[sample], wl, x64[sample], mirror_tol=2e-4, round_w=True)
+    _check_layer(ys[sample], wl, x64[sample], mirror_tol=2e-4, round_w=(0, 1, 2))
 
 
 def test_prefill_is_deterministic(q):
