@@ -56,7 +56,10 @@ def source_digest(kind):
                     for f in TRAFFIC_SOURCES[kind])
 
 
-DECODE = {"decode_b1", "decode_b16_hot", "k4_h7168_decode"}
+# The decode call runs the single-token kernels once per token up to this
+# many tokens (kDecPerTokenMax in csrc/abi.hip).
+DEC_PER_TOKEN_MAX = 3
+DECODE = {"decode_b1", "decode_b16_hot", "k4_h7168_decode", "decode_b1_noshared", "draft_verify_t3"}
 PREFILL = {"prefill_2048", "k4_h7168_prefill"}
 
 
@@ -306,11 +309,15 @@ def main():
         if decode:
             work = {kn: [] for kn in kernels}
             for s in range(steps):
-                d = len(np.unique(idx_h[s]))
+                # up to DEC_PER_TOKEN_MAX tokens the library runs the single-token
+                # kernels once per token and the events time the first token's
+                # launch; beyond, one launch covers the whole batch
+                Tl = 1 if T <= DEC_PER_TOKEN_MAX else T
+                d = len(np.unique(idx_h[s][:Tl]))
                 # up/gate: both matrices of the distinct routed experts + shared, x in, h out
-                work["decode_upgate"].append(d * 2 * nb_up + 2 * Is * H * 2 + T * H * 2 + T * k * I * 2 + T * Is * 2)
+                work["decode_upgate"].append(d * 2 * nb_up + 2 * Is * H * 2 + Tl * H * 2 + Tl * k * I * 2 + Tl * Is * 2)
                 # down: the distinct routed down matrices + shared, h in, y out
-                work["decode_down"].append(d * nb_dn + H * Is * 2 + T * k * I * 2 + T * Is * 2 + T * H * 4)
+                work["decode_down"].append(d * nb_dn + H * Is * 2 + Tl * k * I * 2 + Tl * Is * 2 + Tl * H * 4)
             unit, peak, bound, scale = "GB/s", HBM_PEAK_GBS, "hbm", 1e9
         else:
             work = {"prefill_upgate": [2.0 * 2 * (T * k) * I * H + 2.0 * 2 * T * Is * H] * steps,
@@ -339,7 +346,9 @@ def main():
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": wl.name, "hidden": H, "inter": I, "experts": E, "top_k": k, "shared_inter": Is,
                    "tokens_per_step": T, "formats": "/".join(f.upper() for f in wl.fmts),
-                   "layer_instances": instances, "launch": "hip_graph" if use_graph else "eager"},
+                   "layer_instances": instances, "launch": "hip_graph" if use_graph else "eager",
+                   **({"decode_kernels": "single-token, once per token" if T <= DEC_PER_TOKEN_MAX else "batched"}
+                      if decode else {})},
         "roofline": roof,
         "kernels": per_kernel,
         "kernel_events_pass": None if per_kernel is None else {

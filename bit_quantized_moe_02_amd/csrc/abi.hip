@@ -82,6 +82,10 @@ int check_weights(const moe_weights* w, Geometry* g, const char* fn) {
   return MOE_OK;
 }
 
+// Up to this many tokens the decode call runs the single-token kernels once
+// per token; beyond, the batched kernels that read each distinct expert once.
+constexpr int kDecPerTokenMax = 3;
+
 struct DecLayout {
   size_t h, hs, hsum, ybuf, ysh, err, total;
 };
@@ -237,9 +241,19 @@ extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, i
   a.err_count = (int*)(wsb + L.err);
   const int cus = n_cus();
   hipStream_t s = (hipStream_t)stream;
-  if (T == 1 && dec1_down_lds(a, 16) <= 160 * 1024) {
-    hipError_t e = launch_dec1(a, g.fmt_ug, g.fmt_dn, cpw, topk_w, y, cus, s);
-    if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode", e);
+  if (T <= kDecPerTokenMax && dec1_down_lds(a, 16) <= 160 * 1024) {
+    // few tokens: the single-token kernels once per token (exact weights)
+    for (int t = 0; t < T; ++t) {
+      DecArgs at = a;
+      at.T = 1;
+      at.x = a.x + (size_t)t * g.H;
+      at.topk_idx = topk_idx + (size_t)t * k;
+      at.h = a.h + (size_t)t * k * g.I;
+      at.hs = a.hs + (size_t)t * g.Is;
+      at.hsum = a.hsum + (size_t)t * k * (g.I_pad / 16) * 2;
+      hipError_t e = launch_dec1(at, g.fmt_ug, g.fmt_dn, cpw, topk_w + (size_t)t * k, y + (size_t)t * g.H, cus, s);
+      if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode", e);
+    }
     return MOE_OK;
   }
   const int nck = g.I_pad / 256, ncks = g.Is > 0 ? g.Is_pad / 256 : 0;

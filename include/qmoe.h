@@ -209,11 +209,13 @@ size_t moe_ffn_workspace_bytes(const moe_weights* w, int32_t T, int32_t k, int p
  *   y[t] = sum_j topk_w[t,j] * FFN_{topk_idx[t,j]}(x[t]) + FFN_shared(x[t]),
  *   FFN(x) = W_down (SiLU(W_gate x) * (W_up x)), summed j = 0..k-1 then the
  *   shared expert.  x_bf16 device bf16 [T, H]; y device fp32 [T, H]
- *   (overwritten).  The intermediate h is fp16; sums are fp32.  T = 1
- *   decodes the weights exactly (scales applied to fp32 block sums); for
- *   T >= 2 a layer with CB2 up/gate, hidden <= 4096 and inter, shared_inter
- *   <= 2048 takes kernels that fold the scales into fp16 weights (one
- *   rounding per weight, as moe_expert_ffn_prefill does).  A choice whose
+ *   (overwritten).  The intermediate h is fp16; sums are fp32.  Up to 3
+ *   tokens run the single-token kernels once per token, which decode the
+ *   weights exactly (scales applied to fp32 block sums); for T >= 4 a layer
+ *   with CB2 up/gate, hidden <= 4096 and inter, shared_inter <= 2048 takes
+ *   batched kernels that read each distinct expert once and fold the CB2
+ *   scales into fp16 weights (one rounding per weight, as
+ *   moe_expert_ffn_prefill does); their K2 down weights stay exact.  A choice whose
  *   expert id lies outside [0, E) contributes nothing; a token may name one
  *   expert in several choices (each contributes).  The first bytes of ws
  *   hold h as fp16 [T*k, inter] (slot order) after the call.  Limits:

@@ -43,6 +43,7 @@ TAG_X = 8
 TAG_HOT_SET = 9
 TAG_BIAS_CALIB = 10
 TAG_X_DECODE = 11
+TAG_X_DRAFT = 12
 
 WEIGHT_STD = 0.02
 
@@ -93,6 +94,14 @@ WORKLOADS = {
     "k4_h7168_decode": Workload("k4_h7168_decode", 7168, 2048, 256, 8, 2048,
                                 "k4", "k4", "k4", seed=4, tokens=1,
                                 steps=1000, x_tag=TAG_X_DECODE),
+    # decode_b1's layer (same seed, same weights) without its shared expert:
+    # the quantized expert bytes alone
+    "decode_b1_noshared": Workload("decode_b1_noshared", 4096, 2048, 256, 8, 0,
+                                   "cb2", "cb2", "k2", seed=1, tokens=1, steps=1000),
+    # draft verification: decode_b1's layer, 1 + 2 drafted tokens per step
+    "draft_verify_t3": Workload("draft_verify_t3", 4096, 2048, 256, 8, 2048,
+                                "cb2", "cb2", "k2", seed=1, tokens=3, steps=1000,
+                                x_tag=TAG_X_DRAFT),
 }
 
 
