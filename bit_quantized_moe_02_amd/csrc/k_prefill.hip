@@ -238,18 +238,36 @@ __device__ __forceinline__ float16v zero16v() {
 // workgroup, A = the expert's token rows of x (fp16 copy).
 
 // The 16 k-steps of one staged chunk over MTA live M-tiles.
+// A of M-tile mt at step kk: row 32 mt + l%32 sits at byte 16384 mt +
+// 512 (l%32), piece rotation (2 kk + l/32 + l%32) & 31 does not depend on mt,
+// so one address per step serves every M-tile (the empty asm keeps the
+// compiler from hoisting the 16 step addresses into registers).
+__device__ __forceinline__ const uint8_t* a_step_addr(const uint8_t* buf, int kk, int lane) {
+  int q = (lane >> 5) + (lane & 31);
+  asm volatile("" : "+v"(q));
+  return buf + 512 * (lane & 31) + 16 * ((2 * kk + q) & 31);
+}
+__device__ __forceinline__ half8 a_at(const uint8_t* p, int mt) {
+  return as_half8(*reinterpret_cast<const u32x4*>(p + 16384 * mt));
+}
+
 template <int MTA, typename B>
 __device__ __forceinline__ void ug_steps(float16v (&acc)[2][kUgTiles][kMT], const B (&cu)[kUgTiles],
                                          const B (&cg)[kUgTiles], const uint8_t* tab, const uint8_t* buf, int lane) {
   half8 av[MTA];
+  {
+    const uint8_t* p0 = a_step_addr(buf, 0, lane);
 #pragma unroll
-  for (int mt = 0; mt < MTA; ++mt) av[mt] = a_read(buf, mt, 0, lane);
+    for (int mt = 0; mt < MTA; ++mt) av[mt] = a_at(p0, mt);
+  }
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
     half8 an[MTA];
-    if (kk + 1 < 16)
+    if (kk + 1 < 16) {
+      const uint8_t* pn = a_step_addr(buf, kk + 1, lane);
 #pragma unroll
-      for (int mt = 0; mt < MTA; ++mt) an[mt] = a_read(buf, mt, kk + 1, lane);
+      for (int mt = 0; mt < MTA; ++mt) an[mt] = a_at(pn, mt);
+    }
     half8 bu[kUgTiles], bg[kUgTiles];
 #pragma unroll
     for (int b = 0; b < kUgTiles; ++b) {
