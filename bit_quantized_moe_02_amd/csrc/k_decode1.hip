@@ -29,6 +29,32 @@ using qmoe::DecArgs;
 
 namespace {
 
+// Expert id of choice j (j uniform over the wave), read as a scalar load:
+// its wait counts scalar loads only, so taking an id never waits for the
+// weight tiles in flight (a wave's vector loads complete in issue order and
+// a vector wait is a count of loads still outstanding).
+__device__ __forceinline__ int expert_id(const int32_t* topk_idx, int j) {
+  return ((const __attribute__((address_space(4))) int32_t*)topk_idx)[j];
+}
+__device__ __forceinline__ float choice_weight(const float* topk_w, int j) {
+  return ((const __attribute__((address_space(4))) float*)topk_w)[j];
+}
+
+// Raw buffer loads of a tile that may not exist: a load whose offset lies
+// past the descriptor's byte count returns zeros and touches no memory, so
+// such a tile needs no branch around its loads (a load inside a branch makes
+// the compiler wait for every earlier load where the paths join).  base must
+// be wave-uniform; word 3 is the untyped-dword setting of this family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 constexpr int kBatch = 8;        // row tiles reduced per barrier (up/gate)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -339,34 +365,40 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   const int n = lane & 15, g = lane >> 4, m = lane & 15, qq = lane >> 4;
 
   // ---- prologue.  Loads are issued oldest-first in the order they are
-  // needed (codebook and x, then the shared tile, then a routed tile), so
-  // the table can be built while the weights are still in flight.
-  int8_t cbv[4] = {0, 0, 0, 0};
-  if (tid < 512) {
-    const int8_t* cbp = a.codebook + (tid >> 1) * 8 + 4 * (tid & 1);
+  // needed (expert ids, codebook and x, then the shared tile, then a routed
+  // tile), so the table can be built while the weights are still in flight.
+  // A wave's loads complete in issue order and a wait is a count of loads
+  // still in flight, so these loads are unconditional (lanes that need none
+  // load a copy and ignore it): a load inside a divergent branch makes the
+  // compiler wait for every earlier load at the join.
+  int8_t cbv[4];
+  {
+    const int8_t* cbp = a.codebook + ((tid & 511) >> 1) * 8 + 4 * (tid & 1);
     for (int i = 0; i < 4; ++i) cbv[i] = cbp[i];
   }
-  u32x4 xr = {0u, 0u, 0u, 0u};
-  if (m < 8) xr = load16(a.x + chunk * 256 + m * 32 + qq * 8);
+  const u32x4 xr = load16(a.x + chunk * 256 + (m & 7) * 32 + qq * 8);    // used by lanes m < 8
 
-  // shared half tile loads: 2 matrices x 4 k-block pairs
+  // shared half tile loads: 2 matrices x 4 k-block pairs (zeros when the
+  // workgroup has no shared item)
   u32x4 sraw[2][4];
-  auto issue_shared = [&](int su) {
+  auto issue_shared = [&](int su, bool valid) {
     const int rt = su >> 1, hr = su & 1;
     const int r = 8 * hr + (n & 7);
     for (int mat = 0; mat < 2; ++mat) {
-      const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kBf16Tile;
-      for (int p = 0; p < 4; ++p) sraw[mat][p] = load16(tile + 1024 * (2 * p + (n >> 3)) + 16 * (16 * qq + r));
+      const uint8_t* tile = valid ? (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kBf16Tile
+                                  : reinterpret_cast<const uint8_t*>(a.x);
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kBf16Tile : 0);
+      for (int p = 0; p < 4; ++p) sraw[mat][p] = bload16(rs, 1024 * (2 * p + (n >> 3)) + 16 * (16 * qq + r));
     }
   };
-  if (s_lo < s_hi) issue_shared(s_lo);
+  issue_shared(s_lo, s_lo < s_hi);
 
   int j_ld = r_lo / n_rt, rt_ld = r_lo - j_ld * n_rt;      // next routed item to load
   Cb2Pay P0, P1, P2;
   auto issue = [&](Cb2Pay& P, int r) {
     int e = -1;
     if (r < r_hi) {
-      e = a.topk_idx[j_ld];
+      e = expert_id(a.topk_idx, j_ld);
       if (e >= a.E) e = -1;
     }
     const bool ok = e >= 0 && active;
@@ -404,7 +436,7 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
 
   // ---- shared expert half tiles
   for (int su = s_lo; su < s_hi; ++su) {
-    if (su != s_lo) issue_shared(su);
+    if (su != s_lo) issue_shared(su, true);
     float v[2];
     for (int mat = 0; mat < 2; ++mat) {
       float4v c = zero;
@@ -592,7 +624,7 @@ __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
       const int j = item / n_rt;
       rt = item - j * n_rt;
       chunk = kp * 16 + wave;
-      e = a.topk_idx[j];
+      e = expert_id(a.topk_idx, j);
       if (e >= a.E || chunk >= n_chunks) e = -1;
     }
     const bool ok = e >= 0;
@@ -767,20 +799,19 @@ struct DnPay<MOE_FMT_K4> {
 };
 
 template <int FMT>
-__device__ __forceinline__ void dn_load(DnPay<FMT>& p, const uint8_t* tile, int lane) {
+__device__ __forceinline__ void dn_load(DnPay<FMT>& p, __amdgpu_buffer_rsrc_t tile, int lane) {
   const int n = lane & 15, g4 = lane >> 4;
   if constexpr (FMT == MOE_FMT_K2) {
-    p.q = load16(tile + 16 * lane);
-    p.scm = *reinterpret_cast<const uint32_t*>(tile + 1024 + 16 * n + 4 * g4);
-    p.dd = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
+    p.q = bload16(tile, 16 * lane);
+    p.scm = bload4(tile, 1024 + 16 * n + 4 * g4);
+    p.dd = bload4(tile, 1280 + 4 * n);
   } else {
-    p.q0 = load16(tile + 16 * lane);
-    p.q1 = load16(tile + 1024 + 16 * lane);
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(tile + 2048 + 12 * n);
-    p.s0 = sp[0];
-    p.s1 = sp[1];
-    p.s2 = sp[2];
-    p.dd = *reinterpret_cast<const uint32_t*>(tile + 2240 + 4 * n);
+    p.q0 = bload16(tile, 16 * lane);
+    p.q1 = bload16(tile, 1024 + 16 * lane);
+    p.s0 = bload4(tile, 2048 + 12 * n);
+    p.s1 = bload4(tile, 2048 + 12 * n + 4);
+    p.s2 = bload4(tile, 2048 + 12 * n + 8);
+    p.dd = bload4(tile, 2240 + 4 * n);
   }
 }
 
@@ -790,7 +821,7 @@ __device__ __forceinline__ void dn_load(DnPay<FMT>& p, const uint8_t* tile, int 
 // (routed) or half a chunk (shared).  Every wave issues the loads of all its
 // units before the activations are staged, so HBM latency overlaps staging.
 constexpr int kDnUnits = 4;    // routed units held in registers per wave
-constexpr int kStageVec = 4;   // staged 16-byte vectors per thread per pass
+constexpr int kStageVec = 6;   // staged 16-byte vectors per thread per pass
 
 template <int FMT>
 __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float* topk_w, float* y) {
@@ -815,74 +846,89 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
   const int n_units = k * n_ck, n_sunits = 2 * n_cks;
   const size_t tb = FMT == MOE_FMT_K2 ? kK2Tile : kK4Tile;
 
-  // ---- first round of loads: routed units wave + NW*i, one shared unit
+  // ---- loads, oldest first: the first pass of the staged activations, the
+  // shared unit, then the routed units wave + NW*i.  A wave's loads complete
+  // in issue order, so the staging waits only for the activations, not
+  // behind weight tiles.
   DnPay<FMT> P[kDnUnits];
   int uj[kDnUnits], ukc[kDnUnits], ue[kDnUnits];
+  // (units past the end or naming an invalid expert load zeros, no memory)
   auto issue_round = [&](int base) {
     for (int i = 0; i < kDnUnits; ++i) {
       const int u = base + wave + NW * i;
-      ue[i] = -1;
-      if (u < n_units) {
-        const int j = u / n_ck;
-        uj[i] = j;
-        ukc[i] = u - j * n_ck;
-        const int e = a.topk_idx[j];
-        if (e >= 0 && e < a.E) {
-          ue[i] = e;
-          dn_load<FMT>(P[i], a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + ukc[i]) * tb, lane);
-        }
-      }
+      const int j = u / n_ck;
+      uj[i] = j;
+      ukc[i] = u - j * n_ck;
+      const int e = u < n_units ? expert_id(a.topk_idx, j) : -1;
+      ue[i] = (e >= 0 && e < a.E) ? e : -1;
+      const uint8_t* tile = ue[i] >= 0 ? a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + ukc[i]) * tb
+                                       : a.down;
+      dn_load<FMT>(P[i], tile_rsrc(tile, ue[i] >= 0 ? (int)tb : 0), lane);
     }
   };
   u32x4 sraw[4];
   int s_kc = -1, s_kb0 = 0;
   auto issue_shared = [&](int su) {
-    s_kc = -1;
-    if (su < n_sunits) {
-      s_kc = su >> 1;
-      s_kb0 = 4 * (su & 1);
-      const uint8_t* tile = a.sdown + ((size_t)rt * n_cks + s_kc) * kBf16Tile;
-      for (int q = 0; q < 4; ++q) sraw[q] = load16(tile + 1024 * (s_kb0 + q) + 16 * lane);
-    }
+    const bool valid = su < n_sunits;
+    s_kc = valid ? su >> 1 : -1;
+    s_kb0 = 4 * (su & 1);
+    const uint8_t* tile = valid ? a.sdown + ((size_t)rt * n_cks + s_kc) * kBf16Tile : a.down;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kBf16Tile : 0);
+    for (int q = 0; q < 4; ++q) sraw[q] = bload16(rs, 1024 * (s_kb0 + q) + 16 * lane);
   };
-  issue_round(0);
-  issue_shared(wave);
 
-  // ---- stage the activations.  Every thread issues all of its loads
-  // (h vectors, per-16-row sums, shared h) before it uses any of them, so
-  // the staging costs one memory round trip.
+  // ---- staging of the activations: h vectors, per-16-row sums, shared h
   const int cvp = I_pad / 8, cv = I / 8;              // 8-column vectors per slot row
   const int nrp = I_pad / 16, nr = I / 16;            // 16-row sums per slot row
   const int n_hv = k * cvp, n_xv = k * (nrp / 2), n_sv = Is_pad / 8;
-  for (int base = 0; base < n_hv + n_xv + n_sv; base += kStageVec * (int)blockDim.x) {
-    u32x4 v[kStageVec];
-    int dst[kStageVec];      // LDS byte offset, -1 = nothing
+  const int n_stage = n_hv + n_xv + n_sv, pass = kStageVec * (int)blockDim.x;
+  // One buffer descriptor spans h, hs and hsum (consecutive in the
+  // workspace, h first): a lane with nothing to stage loads past its end and
+  // gets zeros, so the staging loads need no branch (a load inside a branch
+  // makes the compiler wait for every earlier load where the paths join).
+  const uint8_t* hb = reinterpret_cast<const uint8_t*>(a.h);
+  const int off_hs = (int)(reinterpret_cast<const uint8_t*>(a.hs) - hb);
+  const int off_xs = (int)(reinterpret_cast<const uint8_t*>(a.hsum) - hb);
+  const __amdgpu_buffer_rsrc_t hrs = tile_rsrc(hb, off_xs + k * nrp * 2 * 4);
+  // Offsets and destinations first, then the loads as one straight run.
+  // dst: LDS byte offset | scaling flags (0x20000000, 0x40000000) | 0x10000000
+  // for a sum pair whose second half lies past the end; -1 = nothing.
+  auto stage_load = [&](int base, u32x4 (&v)[kStageVec], int (&dst)[kStageVec]) {
+    const int nrh = nrp / 2;
+    int off[kStageVec];
 #pragma unroll
     for (int i = 0; i < kStageVec; ++i) {
       const int id = base + tid + i * (int)blockDim.x;
-      v[i] = u32x4{0u, 0u, 0u, 0u};
-      dst[i] = -1;
-      if (id < n_hv) {
-        const int j = id / cvp, c = id - j * cvp;
-        if (c < cv) v[i] = load16(a.h + (size_t)j * I + 8 * c);
-        dst[i] = (j * I_pad + 8 * c) * 2;
-        if (FMT == MOE_FMT_K2) dst[i] |= (c >> 2) & 1 ? 0x40000000 : 0x20000000;
-      } else if (id < n_hv + n_xv) {
-        const int q = id - n_hv, j = q / (nrp / 2), c = q - j * (nrp / 2);
-        const float* src = a.hsum + ((size_t)j * nrp + 2 * c) * 2;
-        if (2 * c + 1 < nr) v[i] = load16(src);
-        else if (2 * c < nr) v[i] = u32x4{__builtin_bit_cast(uint32_t, src[0]), __builtin_bit_cast(uint32_t, src[1]), 0u, 0u};
-        dst[i] = (int)((uint8_t*)(xo + ((size_t)j * nrp + 2 * c) * 2) - smem);
-      } else if (id < n_hv + n_xv + n_sv) {
-        const int c = id - n_hv - n_xv;
-        if (c < Is / 8) v[i] = load16(a.hs + 8 * c);
-        dst[i] = (int)((uint8_t*)(hss + 8 * c) - smem);
+      const bool k0 = id < n_hv, k1 = !k0 && id < n_hv + n_xv, k2 = !k0 && !k1 && id < n_stage;
+      const int q = k0 ? id : (k1 ? id - n_hv : id - n_hv - n_xv);
+      const int per = k0 ? cvp : nrh;
+      const int j = q / per, c = q - j * per;           // kinds 0, 1
+      int o = 0x7FFFFFF0;                               // past the end: zeros
+      if (k0 && c < cv) o = (j * I + 8 * c) * 2;
+      if (k1 && 2 * c < nr) o = off_xs + (j * nrp + 2 * c) * 8;
+      if (k2 && q < Is / 8) o = off_hs + 16 * q;
+      off[i] = o;
+      int d = -1;
+      if (k0) {
+        d = (j * I_pad + 8 * c) * 2;
+        if (FMT == MOE_FMT_K2) d |= (c >> 2) & 1 ? 0x40000000 : 0x20000000;
+      } else if (k1) {
+        d = (int)((uint8_t*)(xo + ((size_t)j * nrp + 2 * c) * 2) - smem);
+        if (2 * c + 1 >= nr) d |= 0x10000000;
+      } else if (k2) {
+        d = (int)((uint8_t*)(hss + 8 * q) - smem);
       }
+      dst[i] = d;
     }
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) v[i] = bload16(hrs, off[i]);
+  };
+  auto stage_store = [&](const u32x4 (&v)[kStageVec], const int (&dst)[kStageVec]) {
 #pragma unroll
     for (int i = 0; i < kStageVec; ++i) {
       if (dst[i] < 0) continue;
       u32x4 w = v[i];
+      if (dst[i] & 0x10000000) w = u32x4{w.x, w.y, 0u, 0u};      // odd tail: one sum pair
       if (FMT == MOE_FMT_K2 && (dst[i] & 0x60000000)) {
         // column pair s of an 8-column group sits at slot t(kb, s); scale by 4^-t
         const half8 f = (dst[i] & 0x40000000)
@@ -890,29 +936,51 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
                             : half8{1.0f16, 1.0f16, 0.25f16, 0.25f16, 0.0625f16, 0.0625f16, 0.015625f16, 0.015625f16};
         w = as_u32x4(as_half8(w) * f);
       }
-      *reinterpret_cast<u32x4*>(smem + (dst[i] & 0x1FFFFFFF)) = w;
+      *reinterpret_cast<u32x4*>(smem + (dst[i] & 0x0FFFFFFF)) = w;
     }
+  };
+  // all passes but the last before any weight load (a loop around loads
+  // makes the compiler's later waits conservative); the last pass's stores
+  // wait only for its own loads
+  const int n_pass = (n_stage + pass - 1) / pass;
+  for (int ps = 0; ps + 1 < n_pass; ++ps) {
+    u32x4 v[kStageVec];
+    int dst[kStageVec];
+    stage_load(ps * pass, v, dst);
+    stage_store(v, dst);
+  }
+  {
+    u32x4 v[kStageVec];
+    int dst[kStageVec];
+    stage_load((n_pass - 1) * pass, v, dst);
+    issue_shared(wave);
+    issue_round(0);
+    stage_store(v, dst);
   }
   if (tid < 4) reinterpret_cast<uint32_t*>(zero16)[tid] = 0u;
   __syncthreads();
 
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
   float acc = 0.f;
-  for (int base = 0; base < n_units; base += kDnUnits * NW) {
-    if (base > 0) issue_round(base);
+  // the first round is straight-line code, so each unit waits for its own
+  // tile only (a loop around loads makes the compiler's waits conservative)
+  auto compute_round = [&]() {
     for (int i = 0; i < kDnUnits; ++i) {
       if (ue[i] < 0) continue;
       const int j = uj[i], kc = ukc[i];
-      const float wgt = topk_w[j];
+      const float wgt = choice_weight(topk_w, j);
       const DnPay<FMT>& p = P[i];
       const _Float16* hbase = hst + (size_t)j * I_pad + kc * 256 + g4 * 8;
       if constexpr (FMT == MOE_FMT_K2) {
+        // row 2 kb + g4/2 of A_kb holds sub-block 2 kb + g4/2 of h: a lane
+        // (m, g4) feeds only k-block m/2, and only when m's parity is g4/2,
+        // so it reads its one vector once and A_kb is that vector or zero
+        const bool feeds = (m & 1) == (g4 >> 1);
+        const int kb_act = m >> 1;
+        const u32x4 hv = load16(feeds ? reinterpret_cast<const uint8_t*>(hbase + kb_act * 32) : zero16);
+        const u32x4 z = {0u, 0u, 0u, 0u};
         float4v c = zero;
-        for (int kb = 0; kb < 8; ++kb) {
-          const bool act = m == 2 * kb + (g4 >> 1);
-          const uint8_t* src = act ? reinterpret_cast<const uint8_t*>(hbase + kb * 32) : zero16;
-          c = mfma_f16(as_half8(load16(src)), as_half8(k2_magic(p.q, kb)), c);
-        }
+        for (int kb = 0; kb < 8; ++kb) c = mfma_f16(as_half8(kb == kb_act ? hv : z), as_half8(k2_magic(p.q, kb)), c);
         // C[4 g4 + i][n] = sub-block 4 g4 + i of this super-block; xo holds
         // (X, O) of sub-block s at 2s, 2s+1
         const float4v X = *reinterpret_cast<const float4v*>(xo + ((size_t)j * (I_pad / 16) + kc * 16 + 4 * g4) * 2);
@@ -941,6 +1009,11 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
         if (g4 == 0) acc += wgt * part;
       }
     }
+  };
+  compute_round();
+  for (int base = kDnUnits * NW; base < n_units; base += kDnUnits * NW) {
+    issue_round(base);
+    compute_round();
   }
   // shared expert: units of half a K-chunk (4 k-blocks)
   for (int su = wave; su < n_sunits; su += NW) {
