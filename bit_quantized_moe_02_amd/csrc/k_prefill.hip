@@ -17,6 +17,8 @@
 // tolerance, which bf16 operands do not; the shared expert's up/gate uses
 // bf16 operands directly because both x and its weights are exact in bf16.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "../../include/qmoe.h"
@@ -221,6 +223,54 @@ __device__ __forceinline__ half8 b_decode(const K2B& b, int kk, const uint8_t*) 
   return w;
 }
 
+// K2 in the grouped GEMM, cheaper per weight: the row's per-sub-block
+// factors d*sc and -dmin*m are formed once per chunk as fp16 (packed
+// products of exact operands, one rounding each; the lane's sub-block at
+// step kk is kk), and a weight is fma(q, d*sc, -dmin*m) in fp16 (q exact,
+// one more rounding).
+struct K2Fac {
+  half2v ds[8];   // d*sc of sub-blocks 2i, 2i+1
+  half2v nm[8];   // -dmin*m of sub-blocks 2i, 2i+1
+};
+__device__ __forceinline__ void k2_factors(const K2B& b, K2Fac& f) {
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)(b.dd & 0xFFFFu));
+  const _Float16 ndmin = -__builtin_bit_cast(_Float16, (uint16_t)(b.dd >> 16));
+  const half2v d2 = {d, d}, nd2 = {ndmin, ndmin}, m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = b.scm[w] & 0x0F0F0F0Fu, hi = (b.scm[w] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // bytes 2h and 2h+1 (sub-blocks 4w + 2h, 4w + 2h + 1) into the two
+      // halves of a word, as fp16 1024 + nibble, minus 1024
+      const uint32_t sel = h ? 0x0C030C02u : 0x0C010C00u;
+      const half2v sc = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0u, lo, sel) | 0x64006400u) + m1024;
+      const half2v mn = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0u, hi, sel) | 0x64006400u) + m1024;
+      f.ds[2 * w + h] = sc * d2;
+      f.nm[2 * w + h] = mn * nd2;
+    }
+  }
+}
+__device__ __forceinline__ half8 b_decode(const K2B& b, const K2Fac& f, int kk) {
+  const int kb = kk >> 1;
+  const half8 mg = as_half8(k2_magic((kk & 1) ? b.q1 : b.q0, kb));
+  const _Float16 ds = f.ds[kk >> 1][kk & 1], nm = f.nm[kk >> 1][kk & 1];
+  const half2v ds2 = {ds, ds}, nm2 = {nm, nm};
+  half8 w;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int t = k2_slot_t(kb, s);
+    const _Float16 sc = (_Float16)__builtin_ldexpf(1.0f, -2 * t);
+    const _Float16 off = (_Float16)(-1024.0f * __builtin_ldexpf(1.0f, -2 * t));
+    const half2v mp = {mg[2 * s], mg[2 * s + 1]};
+    const half2v q = __builtin_elementwise_fma(mp, half2v{sc, sc}, half2v{off, off});   // exact
+    const half2v r = __builtin_elementwise_fma(q, ds2, nm2);
+    w[2 * s] = r[0];
+    w[2 * s + 1] = r[1];
+  }
+  return w;
+}
+
 // BF16 tiles: the lane's 16 bytes for step kk (raw bf16).
 __device__ __forceinline__ u32x4 bf16_piece(const uint8_t* tile, int kk, int lane) {
   const int n = lane & 15, hl = lane >> 5, kb = kk >> 1, qq = 2 * (kk & 1) + hl;
@@ -252,7 +302,7 @@ __device__ __forceinline__ half8 a_at(const uint8_t* p, int mt) {
 }
 
 template <int MTA, typename B>
-__device__ __forceinline__ void ug_steps(float16v (&acc)[2][kUgTiles][kMT], const B (&cu)[kUgTiles],
+__device__ __forceinline__ void ug_steps(float16v (&acc)[2][kUgTiles][MTA], const B (&cu)[kUgTiles],
                                          const B (&cg)[kUgTiles], const uint8_t* tab, const uint8_t* buf, int lane) {
   half8 av[MTA];
   {
@@ -308,12 +358,15 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
   }
   using B = typename BRegs<FMT>::T;
 
-  for (int64_t m0 = p_begin; m0 < p_end; m0 += kMRows) {
+  // one pass of up to kMRows tokens over MTA M-tiles (the last pass of an
+  // expert runs only the M-tiles its tokens fill)
+  auto run_pass = [&](auto mta_c, int64_t m0) {
+    constexpr int MTA = decltype(mta_c)::value;
     int rows[dma_per_wave<kUgWaves>()];
     stage_rows<kUgWaves>(rows, m0, p_end, [&](int64_t p) { return (int64_t)(a.sorted_slots[p] / k); });
-    float16v acc[2][kUgTiles][kMT];
+    float16v acc[2][kUgTiles][MTA];
     for (int b = 0; b < kUgTiles; ++b)
-      for (int mt = 0; mt < kMT; ++mt) acc[0][b][mt] = acc[1][b][mt] = zero16v();
+      for (int mt = 0; mt < MTA; ++mt) acc[0][b][mt] = acc[1][b][mt] = zero16v();
     B cu[kUgTiles], cg[kUgTiles], nu[kUgTiles], ng[kUgTiles];
     __syncthreads();                                                   // the last pass is done with the buffers
     a_dma<kUgWaves>(stage, a.x16, a.H, rows, 0, a.H);
@@ -331,7 +384,7 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
           b_load(ng[b], tg[b] + (size_t)(chunk + 1) * tb, lane);
         }
       }
-      if (active) ug_steps<kMT>(acc, cu, cg, tab, buf, lane);
+      if (active) ug_steps<MTA>(acc, cu, cg, tab, buf, lane);
       for (int b = 0; b < kUgTiles; ++b) {
         cu[b] = nu[b];
         cg[b] = ng[b];
@@ -341,12 +394,18 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
     for (int b = 0; b < kUgTiles; ++b) {
       const int row = row0 + 32 * b + (lane & 31);
       if (row >= a.I) continue;
-      for (int mt = 0; mt < kMT; ++mt)
+      for (int mt = 0; mt < MTA; ++mt)
         for (int i = 0; i < 16; ++i) {
           const int64_t p = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
           if (p < p_end) a.h[p * a.I + row] = (_Float16)(silu(acc[1][b][mt][i]) * acc[0][b][mt][i]);
         }
     }
+  };
+  for (int64_t m0 = p_begin; m0 < p_end; m0 += kMRows) {
+    const int64_t left = p_end - m0;
+    if (left > 64) run_pass(std::integral_constant<int, 3>{}, m0);
+    else if (left > 32) run_pass(std::integral_constant<int, 2>{}, m0);
+    else run_pass(std::integral_constant<int, 1>{}, m0);
   }
 }
 
@@ -486,6 +545,9 @@ __device__ __forceinline__ void dn_steps(float16v (&acc)[kDnTiles][kMT], const B
   half8 av[MTA];
 #pragma unroll
   for (int mt = 0; mt < MTA; ++mt) av[mt] = a_read(buf, mt, 0, lane);
+  K2Fac fac[kDnTiles];
+  if constexpr (FMT == MOE_FMT_K2)
+    for (int b = 0; b < kDnTiles; ++b) k2_factors(cur[b], fac[b]);
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
     half8 an[MTA];
@@ -493,7 +555,10 @@ __device__ __forceinline__ void dn_steps(float16v (&acc)[kDnTiles][kMT], const B
 #pragma unroll
       for (int mt = 0; mt < MTA; ++mt) an[mt] = a_read(buf, mt, kk + 1, lane);
     half8 bw[kDnTiles];
-    for (int b = 0; b < kDnTiles; ++b) bw[b] = b_decode(cur[b], kk, nullptr);
+    for (int b = 0; b < kDnTiles; ++b) {
+      if constexpr (FMT == MOE_FMT_K2) bw[b] = b_decode(cur[b], fac[b], kk);
+      else bw[b] = b_decode(cur[b], kk, nullptr);
+    }
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt)
       for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av[mt], bw[b], acc[b][mt]);

@@ -35,6 +35,28 @@ def _oracle_expert_cached(name: str, e: int):
     return tuple(out)
 
 
+def down_k2_as_prefill(wl: synth.Workload, e: int):
+    """Expert e's K2 down matrix as the grouped GEMM holds it: per sub-block
+    fp16(d*sc) and fp16(-dmin*m), then fp16(q*fp16(d*sc) + fp16(-dmin*m))
+    with one rounding (a fused multiply-add)."""
+    return _down_k2_cached(wl.name, e)
+
+
+@functools.lru_cache(maxsize=64)
+def _down_k2_cached(name: str, e: int):
+    wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else _CUSTOM[name]
+    assert wl.fmts[2] == "k2"
+    w = synth.expert_weight(wl, "down", e)
+    f = O.quantize_matrix("k2", w, codebook())
+    q = f["q"].astype(np.float64)
+    sc = np.repeat(f["sc"].astype(np.float64), 16, axis=1)
+    m = np.repeat(f["m"].astype(np.float64), 16, axis=1)
+    d = np.repeat(f["d"], 256, axis=1)
+    dmin = np.repeat(f["dmin"], 256, axis=1)
+    ds, nm = O.f16(d * sc), O.f16(-(dmin * m))
+    return O.f16(q * ds + nm)[:, : w.shape[1]]      # q*ds + nm is exact in fp64
+
+
 _CUSTOM: dict = {}
 
 

@@ -12,9 +12,8 @@ import pytest
 import oracle as O
 import synth
 
-from layer_fixture import (codebook, device_layer, near_tie_tokens, oracle_expert, oracle_layer, oracle_shared,
-                           register, rel_err,
-                           x_bits)
+from layer_fixture import (codebook, device_layer, down_k2_as_prefill, near_tie_tokens, oracle_expert, oracle_layer,
+                           oracle_shared, register, rel_err, x_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -115,7 +114,8 @@ def test_dequant_bit_exact(q, fmt, rows, k):
 # Routing and grouping
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode_b16_hot", 16), ("decode_b1", 16),
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 3), ("decode_b16_hot", 16), ("decode_b1", 16),
+                                    ("decode_b1", 2), ("draft_verify_t3", 3), ("k4_h7168_decode", 3),
                                     ("prefill_2048", 512)])
 def test_route_matches_oracle(q, name, T):
     print(f"route {name} T={T}", flush=True)
@@ -249,7 +249,20 @@ def _multi_token_rounds_weights(wl, T):
     return (0, 1) if batched else ()
 
 
-def _check_layer(y, wl, x64, expect_idx=None, mirror_tol=None, round_w=()):
+def _mirror_expert(wl, e, round_w, prefill):
+    """Expert e's (up, gate, down) as the kernels hold them: matrices in
+    round_w rounded to fp16 once, except that the grouped GEMM's K2 down
+    forms its fp16 weights from fp16 per-sub-block factors."""
+    out = []
+    for i, m in enumerate(oracle_expert(wl, e)):
+        if i == 2 and prefill and wl.fmts[2] == "k2":
+            out.append(down_k2_as_prefill(wl, e))
+        else:
+            out.append(O.f16(m) if i in round_w else m)
+    return tuple(out)
+
+
+def _check_layer(y, wl, x64, expect_idx=None, mirror_tol=None, round_w=(), prefill=False):
     y_ref, o_idx, _ = oracle_layer(wl, x64)
     err = rel_err(y, y_ref)
     print(f"max rel err vs fp64 oracle: {err.max():.3e} (tokens {len(err)})")
@@ -260,8 +273,7 @@ def _check_layer(y, wl, x64, expect_idx=None, mirror_tol=None, round_w=()):
             # to fp16 as the kernels hold them; the shared expert's bf16
             # weights are exact in either form
             y_m, _, _ = O.moe_layer(x64, synth.router_weight(wl), synth.logit_bias(wl), wl.top_k,
-                                    lambda e: tuple(O.f16(m) if i in round_w else m
-                                                    for i, m in enumerate(oracle_expert(wl, e))),
+                                    lambda e: _mirror_expert(wl, e, round_w, prefill),
                                     shared=oracle_shared(wl), round_h=_mirror_h)
         else:
             y_m, _, _ = oracle_layer(wl, x64, round_h=_mirror_h)
@@ -429,7 +441,7 @@ def test_prefill_full_layer(q, name):
     xb, x64 = x_bits(wl, wl.tokens)
     idx, w = _route(q, layer, xb, wl.top_k)
     y, _, _ = _prefill(q, layer, xb, idx, w, wl.top_k)
-    _check_layer(y.cpu().numpy(), wl, x64, mirror_tol=2e-4, round_w=(0, 1, 2))
+    _check_layer(y.cpu().numpy(), wl, x64, mirror_tol=2e-4, round_w=(0, 1, 2), prefill=True)
     # the same tokens through the decode path, 16 at a time
     if wl.tokens <= 16:
         yd, _ = _decode(q, layer, xb, idx, w, wl.top_k)
@@ -450,7 +462,7 @@ def test_prefill_full_size_sampled(q, name, n_sample):
     y, _, _ = _prefill(q, layer, xb, idx, w, wl.top_k)
     ys = y.cpu().numpy()
     assert np.all(np.isfinite(ys))
-    _check_layer(ys[sample], wl, x64[sample], mirror_tol=2e-4, round_w=(0, 1, 2))
+    _check_layer(ys[sample], wl, x64[sample], mirror_tol=2e-4, round_w=(0, 1, 2), prefill=True)
 
 
 def test_prefill_is_deterministic(q):
