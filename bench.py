@@ -225,7 +225,10 @@ def main():
     w_all = torch.empty((n_total, T, k), dtype=torch.float32, device="cuda")
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     rws = torch.empty(qmoe.moe_route_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
-    ws = torch.empty(qmoe.moe_ffn_workspace_bytes(layers[0].w, T, k, not decode), dtype=torch.uint8, device="cuda")
+    if decode:     # the whole decode step in one call (router, top-k, experts, combine)
+        ws = torch.empty(qmoe.moe_layer_decode_workspace_bytes(layers[0].w, T, k), dtype=torch.uint8, device="cuda")
+    else:
+        ws = torch.empty(qmoe.moe_ffn_workspace_bytes(layers[0].w, T, k, True), dtype=torch.uint8, device="cuda")
     if not decode:
         off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
         ss = torch.empty(T * k, dtype=torch.int32, device="cuda")
@@ -242,12 +245,13 @@ def main():
     def step(s, timed_kernel):
         layer = layers[s % instances]
         x = xs[s % n_x]
-        qmoe.moe_route(x, layer.router, layer.bias, T, H, E, k, idx_all[s], w_all[s], rws)
+        if not decode:
+            qmoe.moe_route(x, layer.router, layer.bias, T, H, E, k, idx_all[s], w_all[s], rws)
         if timed_kernel is not None:
             for kn in kernels:
                 qmoe.moe_profile_next_launch(kn, *ev[kn][timed_kernel])
         if decode:
-            qmoe.moe_expert_ffn_decode(layer.w, x, T, k, idx_all[s], w_all[s], y, ws)
+            qmoe.moe_layer_decode(layer.w, layer.router, layer.bias, x, T, k, idx_all[s], w_all[s], y, ws)
         else:
             qmoe.moe_group_tokens(idx_all[s], T, k, E, off, ss, sp, gws)
             qmoe.moe_expert_ffn_prefill(layer.w, x, T, k, idx_all[s], w_all[s], off, ss, sp, y, ws)
@@ -347,7 +351,8 @@ def main():
         "config": {"workload": wl.name, "hidden": H, "inter": I, "experts": E, "top_k": k, "shared_inter": Is,
                    "tokens_per_step": T, "formats": "/".join(f.upper() for f in wl.fmts),
                    "layer_instances": instances, "launch": "hip_graph" if use_graph else "eager",
-                   **({"decode_kernels": "single-token, once per token" if T <= DEC_PER_TOKEN_MAX else "batched"}
+                   **({"entry": "moe_layer_decode",
+                       "decode_kernels": "single-token, once per token" if T <= DEC_PER_TOKEN_MAX else "batched"}
                       if decode else {})},
         "roofline": roof,
         "kernels": per_kernel,

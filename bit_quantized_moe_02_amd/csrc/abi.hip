@@ -188,23 +188,37 @@ extern "C" size_t moe_ffn_workspace_bytes(const moe_weights* w, int32_t T, int32
   return pf_layout(g, T, k).total;
 }
 
-extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
-                                     const int32_t* topk_idx, const float* topk_w, float* y, void* ws,
-                                     size_t ws_bytes, void* stream) {
-  clear_error();
-  Geometry g;
-  int rc = check_weights(w, &g, "moe_expert_ffn_decode");
+namespace {
+
+// Router output that the decode kernels take instead of given top-k: the
+// partial logits of all T tokens; the single-token CB2 up/gate ranks each
+// token itself and writes topk_idx / topk_w.
+struct DecRoute {
+  const float* logits;
+  int n_parts;
+};
+
+// Checks of the decode entry points that do not depend on routing.
+int check_decode(const char* who, const moe_weights* w, Geometry* g, const void* x_bf16, int32_t T, int32_t k,
+                 const void* topk_idx, const void* topk_w, const float* y, const void* ws) {
+  int rc = check_weights(w, g, who);
   if (rc != MOE_OK) return rc;
-  if (!x_bf16 || !topk_idx || !topk_w || !y || !ws)
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: NULL pointer");
-  if (T < 1 || T > 16) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: T must be in [1, 16]");
-  if (k < 1 || k > 16 || k > g.E) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: need 1 <= k <= min(E, 16)");
+  if (!x_bf16 || !topk_idx || !topk_w || !y || !ws) return fail(MOE_ERR_INVALID_ARG, std::string(who) + ": NULL pointer");
+  if (T < 1 || T > 16) return fail(MOE_ERR_INVALID_ARG, std::string(who) + ": T must be in [1, 16]");
+  if (k < 1 || k > 16 || k > g->E)
+    return fail(MOE_ERR_INVALID_ARG, std::string(who) + ": need 1 <= k <= min(E, 16)");
   if (!aligned16(x_bf16) || !aligned16(ws) || !aligned16(y))
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_decode: x, y and ws must be 16-byte aligned");
+    return fail(MOE_ERR_INVALID_ARG, std::string(who) + ": x, y and ws must be 16-byte aligned");
+  return MOE_OK;
+}
+
+// The expert FFN for 1..16 tokens.  With route != null, topk_idx / topk_w
+// are outputs: the single-token CB2 path ranks each token's experts inside
+// its up/gate kernel; every other path runs the top-k kernel first.
+int run_decode(const char* who, const moe_weights* w, const Geometry& g, const void* x_bf16, int32_t T,
+               int32_t k, int32_t* topk_idx, float* topk_w, float* y, uint8_t* wsb, hipStream_t s,
+               const DecRoute* route) {
   const DecLayout L = dec_layout(g, T, k);
-  if (ws_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn_decode: workspace too small (need " + std::to_string(L.total) + ")");
-  uint8_t* wsb = (uint8_t*)ws;
   DecArgs a{};
   a.x = (const uint16_t*)x_bf16;
   a.T = T;
@@ -240,9 +254,18 @@ extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, i
   a.ysh = (float*)(wsb + L.ysh);
   a.err_count = (int*)(wsb + L.err);
   const int cus = n_cus();
-  hipStream_t s = (hipStream_t)stream;
   if (T <= kDecPerTokenMax && dec1_down_lds(a, 16) <= 160 * 1024) {
     // few tokens: the single-token kernels once per token (exact weights)
+    const int nw_cb2 = n_chunks < 4 ? 4 : n_chunks;
+    // (one token only: for more, one top-k launch for all of them is cheaper
+    // than ranking inside each token's up/gate)
+    const bool route_here = route && T == 1 && g.fmt_ug == MOE_FMT_CB2 && n_chunks <= 16 &&
+                            g.E <= 64 * nw_cb2 && route->n_parts == 1 &&
+                            dec1_cb2_upgate_lds(nw_cb2, true) <= 160 * 1024;
+    if (route && !route_here) {
+      hipError_t e = launch_route_topk(route->logits, route->n_parts, T, g.E, k, topk_idx, topk_w, s);
+      if (e != hipSuccess) return hip_fail(who, e);
+    }
     for (int t = 0; t < T; ++t) {
       DecArgs at = a;
       at.T = 1;
@@ -251,17 +274,29 @@ extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, i
       at.h = a.h + (size_t)t * k * g.I;
       at.hs = a.hs + (size_t)t * g.Is;
       at.hsum = a.hsum + (size_t)t * k * (g.I_pad / 16) * 2;
+      if (route_here) {
+        at.logits = route->logits;
+        at.n_parts = route->n_parts;
+        at.T_route = T;
+        at.t_route = t;
+        at.topk_idx_out = topk_idx + (size_t)t * k;
+        at.topk_w_out = topk_w + (size_t)t * k;
+      }
       hipError_t e = launch_dec1(at, g.fmt_ug, g.fmt_dn, cpw, topk_w + (size_t)t * k, y + (size_t)t * g.H, cus, s);
-      if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode", e);
+      if (e != hipSuccess) return hip_fail(who, e);
     }
     return MOE_OK;
+  }
+  if (route) {
+    hipError_t e = launch_route_topk(route->logits, route->n_parts, T, g.E, k, topk_idx, topk_w, s);
+    if (e != hipSuccess) return hip_fail(who, e);
   }
   const int nck = g.I_pad / 256, ncks = g.Is > 0 ? g.Is_pad / 256 : 0;
   const int nw_m = (nck > ncks ? nck : ncks) < 4 ? 4 : (nck > ncks ? nck : ncks);
   if (g.fmt_ug == MOE_FMT_CB2 && n_chunks <= 16 && nck <= 8 && ncks <= 8 &&
       decm_down_lds(a, nw_m) <= 160 * 1024) {
     hipError_t e = launch_decm(a, topk_w, y, cus, s);
-    if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode", e);
+    if (e != hipSuccess) return hip_fail(who, e);
     return MOE_OK;
   }
   const int64_t nd_max = (int64_t)(T * k < g.E ? T * k : g.E);
@@ -270,12 +305,61 @@ extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, i
   const int grid_ug = (int)(items_ug < cus ? items_ug : cus);
   const int grid_dn = (int)(items_dn < 2 * cus ? items_dn : 2 * cus);
   hipError_t e = launch_dec_upgate(a, g.fmt_ug, cpw, grid_ug, s);
-  if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode (up/gate)", e);
+  if (e != hipSuccess) return hip_fail(who, e);
   e = launch_dec_down(a, g.fmt_dn, grid_dn, s);
-  if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode (down)", e);
+  if (e != hipSuccess) return hip_fail(who, e);
   e = launch_combine(a, topk_idx, topk_w, y, s);
-  if (e != hipSuccess) return hip_fail("moe_expert_ffn_decode (combine)", e);
+  if (e != hipSuccess) return hip_fail(who, e);
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
+                                     const int32_t* topk_idx, const float* topk_w, float* y, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  clear_error();
+  Geometry g;
+  int rc = check_decode("moe_expert_ffn_decode", w, &g, x_bf16, T, k, topk_idx, topk_w, y, ws);
+  if (rc != MOE_OK) return rc;
+  const DecLayout L = dec_layout(g, T, k);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn_decode: workspace too small (need " + std::to_string(L.total) + ")");
+  // (topk_idx and topk_w are only read on this path)
+  return run_decode("moe_expert_ffn_decode", w, g, x_bf16, T, k, const_cast<int32_t*>(topk_idx),
+                    const_cast<float*>(topk_w), y, (uint8_t*)ws, (hipStream_t)stream, nullptr);
+}
+
+extern "C" size_t moe_layer_decode_workspace_bytes(const moe_weights* w, int32_t T, int32_t k) {
+  Geometry g;
+  if (T < 1 || T > 16 || k < 1 || !w || check_weights(w, &g, "moe_layer_decode_workspace_bytes") != MOE_OK) {
+    clear_error();
+    return 0;
+  }
+  return align_up(dec_layout(g, T, k).total) + align_up(route_logit_floats(T, g.E) * 4);
+}
+
+extern "C" int moe_layer_decode(const moe_weights* w, const float* w_router, const float* logit_bias,
+                                const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx, float* topk_w,
+                                float* y, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  Geometry g;
+  int rc = check_decode("moe_layer_decode", w, &g, x_bf16, T, k, topk_idx, topk_w, y, ws);
+  if (rc != MOE_OK) return rc;
+  if (!w_router) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: NULL router");
+  if (!aligned16(w_router)) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: w_router must be 16-byte aligned");
+  if (g.E > 1024) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: E <= 1024");
+  const size_t off_logits = align_up(dec_layout(g, T, k).total);
+  if (ws_bytes < moe_layer_decode_workspace_bytes(w, T, k))
+    return fail(MOE_ERR_WORKSPACE, "moe_layer_decode: workspace too small (need " +
+                                       std::to_string(moe_layer_decode_workspace_bytes(w, T, k)) + ")");
+  uint8_t* wsb = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  float* logits = (float*)(wsb + off_logits);
+  hipError_t e = launch_route_logits((const uint16_t*)x_bf16, w_router, logit_bias, T, g.H, g.E, logits, s);
+  if (e != hipSuccess) return hip_fail("moe_layer_decode (router)", e);
+  const DecRoute route{logits, route_logit_parts(T, g.H)};
+  return run_decode("moe_layer_decode", w, g, x_bf16, T, k, topk_idx, topk_w, y, wsb, s, &route);
 }
 
 extern "C" int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,

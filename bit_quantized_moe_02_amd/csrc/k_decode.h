@@ -29,6 +29,14 @@ struct DecArgs {
   float* ybuf;                // [T*k][H]   fp32 per-slot down outputs
   float* ysh;                 // [T][H]     fp32 shared-expert output
   int* err_count;             // invalid expert ids seen
+  // Routing inside the single-token CB2 up/gate (null logits: topk_idx is
+  // given).  The kernel ranks token t_route's top k from the router's logits
+  // [T_route][E] and workgroup 0 writes them to topk_idx_out / topk_w_out
+  // (which the down kernel then reads as topk_idx / topk_w).
+  const float* logits;
+  int n_parts, T_route, t_route;     // n_parts: 1 (final logits)
+  int32_t* topk_idx_out;
+  float* topk_w_out;
 };
 
 size_t dec_upgate_lds(const DecArgs& a, int fmt);
@@ -38,6 +46,9 @@ hipError_t launch_dec_down(const DecArgs& a, int fmt, int grid, hipStream_t s);
 // Single-token path (k_decode1.hip): up/gate then down with the shared
 // expert and the weighted combine fused; writes y directly.
 size_t dec1_down_lds(const DecArgs& a, int nw);
+// LDS of the single-token CB2 up/gate with nw waves (route: it ranks the
+// token's experts itself).
+size_t dec1_cb2_upgate_lds(int nw, bool route);
 // cus = compute units of the device (the grids are sized from it).
 hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const float* topk_w, float* y,
                        int cus, hipStream_t s);

@@ -22,6 +22,7 @@
 #include "../../include/qmoe.h"
 #include "device_common.hpp"
 #include "k_decode.h"
+#include "route_common.hpp"
 #include "launch_util.h"
 
 using namespace qmoe_dev;
@@ -347,6 +348,10 @@ __device__ __forceinline__ float cb2_scaled(const float4v& c, const uint32_t sc[
   return ok ? v : 0.f;
 }
 
+// Route: the token's top k are ranked here from the router's partial
+// logits (every workgroup ranks them; workgroup 0 writes them out) while the
+// shared expert's tiles are already in flight.  E <= the workgroup's threads.
+template <bool Route>
 __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tab = smem;                                                     // [0, kTabRep x 64 KB)
@@ -354,6 +359,8 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* red_r = reinterpret_cast<float*>(smem + kTabRep * kCb2CombBytes);  // [kRedBatch][2][NW][32]
   float* red_s = red_r + kRedBatch * 2 * NW * 32;                         // [NW][2][8]
+  int* ids = reinterpret_cast<int*>(red_s + NW * 2 * 8);                  // [16] (Route)
+  qmoe_route::TopkLds* tk = reinterpret_cast<qmoe_route::TopkLds*>(ids + 16);   // (Route)
 
   const int k = a.k, n_chunks = a.H / 256, n_rt = a.I / 16, n_rts = a.Is / 16;
   const int G = gridDim.x, gi = blockIdx.x;
@@ -371,6 +378,11 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   // still in flight, so these loads are unconditional (lanes that need none
   // load a copy and ignore it): a load inside a divergent branch makes the
   // compiler wait for every earlier load at the join.
+  // Route: the logit of expert e = tid, through the scalar cache (a vector
+  // load issued beside the weight tiles would wait as long as they do):
+  // wave w reads experts 64w .. 64w+63 and lane l keeps expert 64w + l's.
+  // (read after the vector loads below are issued: a scalar wait counts
+  // every scalar load, and the vector loads' addresses need some)
   int8_t cbv[4];
   {
     const int8_t* cbp = a.codebook + ((tid & 511) >> 1) * 8 + 4 * (tid & 1);
@@ -393,12 +405,45 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   };
   issue_shared(s_lo, s_lo < s_hi);
 
+  if constexpr (Route) {
+    float mylogit = 0.f;
+    typedef const __attribute__((address_space(4))) float* cfp;
+    const int e0 = 64 * wave;
+    if (e0 + 64 <= a.E) {
+      const cfp lp = (cfp)(a.logits + (size_t)a.t_route * a.E + e0);
+      float lv[64];
+#pragma unroll
+      for (int i = 0; i < 64; ++i) lv[i] = lp[i];
+#pragma unroll
+      for (int i = 0; i < 64; ++i) mylogit = lane == i ? lv[i] : mylogit;
+    } else if (e0 < a.E) {
+      const cfp lp = (cfp)(a.logits + (size_t)a.t_route * a.E + e0);
+      for (int i = 0; i < a.E - e0; ++i) {
+        const float v = lp[i];
+        mylogit = lane == i ? v : mylogit;
+      }
+    }
+    auto logit_of = [&](int) { return mylogit; };        // called for e = tid only
+    auto out = [&](int j, int e, float w) {
+      ids[j] = e;
+      if (blockIdx.x == 0) {
+        a.topk_idx_out[j] = e;
+        a.topk_w_out[j] = w;
+      }
+    };
+    if (blockDim.x >= 1024) qmoe_route::rank_topk<1024>(*tk, a.E, k, logit_of, out);
+    else if (blockDim.x >= 512) qmoe_route::rank_topk<512>(*tk, a.E, k, logit_of, out);
+    else qmoe_route::rank_topk<256>(*tk, a.E, k, logit_of, out);
+    __syncthreads();
+  }
+
   int j_ld = r_lo / n_rt, rt_ld = r_lo - j_ld * n_rt;      // next routed item to load
   Cb2Pay P0, P1, P2;
   auto issue = [&](Cb2Pay& P, int r) {
     int e = -1;
     if (r < r_hi) {
-      e = expert_id(a.topk_idx, j_ld);
+      if constexpr (Route) e = __builtin_amdgcn_readfirstlane(ids[j_ld]);
+      else e = expert_id(a.topk_idx, j_ld);
       if (e >= a.E) e = -1;
     }
     const bool ok = e >= 0 && active;
@@ -1056,8 +1101,9 @@ size_t dec1_down_lds(const DecArgs& a, int nw) {
   return off + (size_t)nw * 16 * 4;
 }
 
-size_t dec1_cb2_upgate_lds(int nw) {
-  return (size_t)kTabRep * kCb2CombBytes + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4;
+size_t dec1_cb2_upgate_lds(int nw, bool route) {
+  return (size_t)kTabRep * kCb2CombBytes + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4 +
+         (route ? 16 * 4 + sizeof(qmoe_route::TopkLds) : 0);
 }
 
 hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const float* topk_w, float* y,
@@ -1080,11 +1126,13 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const 
     const int U_s = 2 * (a.Is / 16), U_r = a.k * (a.I / 16);
     const int most = U_s > U_r ? U_s : U_r;
     const int grid = most < cus ? most : cus;
-    err = ensure_dyn_lds((const void*)dec1_cb2_upgate_kernel);
+    const bool route = a.logits != nullptr;
+    void (*fk)(DecArgs) = route ? dec1_cb2_upgate_kernel<true> : dec1_cb2_upgate_kernel<false>;
+    err = ensure_dyn_lds((const void*)fk);
     if (err != hipSuccess) return err;
-    const size_t lds = dec1_cb2_upgate_lds(nw);
+    const size_t lds = dec1_cb2_upgate_lds(nw, route);
     err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
-      hipLaunchKernelGGL(dec1_cb2_upgate_kernel, dim3(grid), dim3(64 * nw), lds, s, a);
+      hipLaunchKernelGGL(fk, dim3(grid), dim3(64 * nw), lds, s, a);
     });
   } else {
     const int nw_ug = (n_chunks + cpw - 1) / cpw;

@@ -8,28 +8,30 @@
 #include <algorithm>
 
 #include "device_common.hpp"
+#include "route_common.hpp"
 #include "k_route.h"
 #include "../../include/qmoe.h"
 #include "launch_util.h"
 
 using namespace qmoe_dev;
+using namespace qmoe_route;
 
 namespace {
 
-// Few tokens (T <= 16): one wave per (expert, 1/n_parts of H); each lane
-// takes 8 consecutive columns of each 512-column slice (one slice per wave
-// when H <= 8192, so every load of a wave is in flight at once), the wave sums
-// with a butterfly and writes its part's partial logit (the top-k kernel adds
-// the parts in part order).
+// Few tokens (T <= 16): one workgroup per expert, one wave per part of H
+// (n_parts parts of whole 512-column slices, one slice per wave when H <=
+// 8192, so every load of a wave is in flight at once); each lane takes 8
+// consecutive columns of each slice, the wave sums with a butterfly, and the
+// parts are added in part order (bias with part 0) into the final logit.
 constexpr int kMaxLogitParts = 16;
 
-__global__ __launch_bounds__(256) void logits_small_kernel(const uint16_t* x, const float* wr,
-                                                           const float* bias, int T, int H, int E,
-                                                           float* logits) {
+__global__ __launch_bounds__(64 * kMaxLogitParts) void logits_small_kernel(const uint16_t* x, const float* wr,
+                                                                           const float* bias, int T, int H,
+                                                                           int E, float* logits) {
+  __shared__ float part_sum[kMaxLogitParts][16];
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int part = blockIdx.y, n_parts = gridDim.y;
-  if (e >= E) return;
+  const int e = blockIdx.x;
+  const int part = threadIdx.x >> 6, n_parts = blockDim.x >> 6;
   float acc[16];
   for (int t = 0; t < 16; ++t) acc[t] = 0.f;
   const float* w = wr + (size_t)e * H;
@@ -55,7 +57,13 @@ __global__ __launch_bounds__(256) void logits_small_kernel(const uint16_t* x, co
   for (int t = 0; t < T; ++t) {
     float v = acc[t];
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0) logits[((size_t)part * T + t) * E + e] = v + ((bias && part == 0) ? bias[e] : 0.f);
+    if (lane == 0) part_sum[part][t] = v + ((bias && part == 0) ? bias[e] : 0.f);
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    float v = part_sum[0][threadIdx.x];
+    for (int p = 1; p < n_parts; ++p) v += part_sum[p][threadIdx.x];
+    logits[(size_t)threadIdx.x * E + e] = v;
   }
 }
 
@@ -128,93 +136,15 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(const uint16_t* x, co
   }
 }
 
-// Top-k by rank counting, one 1024-thread workgroup per token.  The logit of
-// expert e is the sum of n_parts partial logits (in part order).  Each
-// (logit, e) becomes a 64-bit key whose integer order is "larger logit first,
-// equal logits (+0 and -0 identified) lower index first"; all keys are
-// distinct, so the rank of a key -- the number of keys above it -- is its
-// position in that order.  Four threads count each key's rank over a quarter
-// of the keys each.  The experts of rank < k are kept, and
-// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) with the sum taken in rank
-// order.
-__device__ __forceinline__ uint64_t route_key(float l, int e) {
-  if (l == 0.0f) l = 0.0f;
-  uint32_t b = __builtin_bit_cast(uint32_t, l);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-// Rank top-k of one token with NT threads (NT a multiple of 256): logit_of(e)
-// gives expert e's logit; NT/256 threads count each key's rank over a share
-// of the keys.  Shared scratch comes from the caller.
-struct TopkLds {
-  uint64_t key[1024];
-  float lg[1024];
-  int part_rank[4][256];
-  float kv[16];
-  int ki[16];
-};
-
-template <int NT, typename LogitOf>
-__device__ __forceinline__ void rank_topk(TopkLds& sm, int E, int k, int32_t* topk_idx, float* topk_w,
-                                          LogitOf logit_of) {
-  constexpr int Q = NT / 256;
-  const int tid = threadIdx.x;
-  const int Ep = (E + 7) & ~7;                 // keys padded with 0 (below every real key)
-  for (int e = tid; e < Ep; e += NT) {
-    float s = 0.f;
-    uint64_t kk = 0;
-    if (e < E) {
-      s = logit_of(e);
-      kk = route_key(s, e);
-    }
-    sm.key[e] = kk;
-    sm.lg[e] = s;
-  }
-  __syncthreads();
-  const int q = tid >> 8, el = tid & 255;
-  const int span = Ep / Q;                      // multiple of 2
-  for (int e0 = 0; e0 < E; e0 += 256) {
-    const int e = e0 + el;
-    int cnt = 0;
-    if (e < E) {
-      const uint64_t mine = sm.key[e];
-      const int i_end = (q + 1) * span;
-      for (int i = q * span; i < i_end; i += 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.key[i]);
-        const uint64_t k0 = (uint64_t)v.x | ((uint64_t)v.y << 32);
-        const uint64_t k1 = (uint64_t)v.z | ((uint64_t)v.w << 32);
-        cnt += (k0 > mine) + (k1 > mine);
-      }
-    }
-    sm.part_rank[q][el] = cnt;
-    __syncthreads();
-    if (q == 0 && e < E) {
-      int rank = 0;
-      for (int i = 0; i < Q; ++i) rank += sm.part_rank[i][el];
-      if (rank < k) {
-        sm.kv[rank] = sm.lg[e];
-        sm.ki[rank] = e;
-      }
-    }
-    __syncthreads();
-  }
-  if (tid < k) {
-    const float top = sm.kv[0];
-    float z = 0.f;
-    for (int j = 0; j < k; ++j) z += expf(sm.kv[j] - top);
-    topk_idx[tid] = sm.ki[tid];
-    topk_w[tid] = expf(sm.kv[tid] - top) / z;
-  }
-}
-
 constexpr int kTopkThreads = 1024;
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits, int n_parts, int T, int E, int k,
                                                             int32_t* topk_idx, float* topk_w) {
   __shared__ __align__(16) TopkLds sm;
   const int t = blockIdx.x;
-  rank_topk<kTopkThreads>(sm, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, [&](int e) {
+  int32_t* oi = topk_idx + (size_t)t * k;
+  float* ow = topk_w + (size_t)t * k;
+  rank_topk<kTopkThreads>(sm, E, k, [&](int e) {
     float pv[kMaxLogitParts];                  // all partial loads in flight together
 #pragma unroll
     for (int p = 0; p < kMaxLogitParts; ++p) pv[p] = p < n_parts ? logits[((size_t)p * T + t) * E + e] : 0.f;
@@ -223,6 +153,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits,
     for (int p = 1; p < kMaxLogitParts; ++p)
       if (p < n_parts) s += pv[p];
     return s;
+  }, [&](int j, int e, float w) {
+    oi[j] = e;
+    ow[j] = w;
   });
 }
 
@@ -230,22 +163,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits,
 
 namespace qmoe {
 
-hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
-                        int k, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
-  const int n_parts = T <= 16 ? std::min(kMaxLogitParts, (H + 511) / 512) : 1;
-  hipError_t err = launch_timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+int route_logit_parts(int, int) { return 1; }
+
+hipError_t launch_route_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
+                               float* logits, hipStream_t s) {
+  const int n_parts = std::min(kMaxLogitParts, (H + 511) / 512);
+  return launch_timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
     if (T <= 16)
-      hipLaunchKernelGGL(logits_small_kernel, dim3((E + 3) / 4, n_parts), dim3(256), 0, s, x, wr, bias, T,
-                         H, E, logits);
+      hipLaunchKernelGGL(logits_small_kernel, dim3(E), dim3(64 * n_parts), 0, s, x, wr, bias, T, H, E, logits);
     else
       hipLaunchKernelGGL(logits_tiled_kernel, dim3((E + kLgE - 1) / kLgE, (T + kLgT - 1) / kLgT), dim3(256), 0,
                          s, x, wr, bias, T, H, E, logits);
   });
-  if (err != hipSuccess) return err;
+}
+
+hipError_t launch_route_topk(const float* logits, int n_parts, int T, int E, int k, int32_t* topk_idx,
+                             float* topk_w, hipStream_t s) {
   return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
     hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(kTopkThreads), 0, s, logits, n_parts, T, E, k, topk_idx,
                        topk_w);
   });
+}
+
+hipError_t launch_route(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
+                        int k, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  hipError_t err = launch_route_logits(x, wr, bias, T, H, E, logits, s);
+  if (err != hipSuccess) return err;
+  return launch_route_topk(logits, route_logit_parts(T, H), T, E, k, topk_idx, topk_w, s);
 }
 
 }  // namespace qmoe

@@ -1,0 +1,97 @@
+// Top-k ranking shared by the router kernels and the single-token up/gate
+// kernel that routes its token itself ([digest] "Model weights": routing
+// stays unquantized; the function is softmax, top-k, renormalize).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace qmoe_route {
+
+using qmoe_dev::u32x4;
+
+// Top-k by rank counting, one 1024-thread workgroup per token.  The logit of
+// expert e is the sum of n_parts partial logits (in part order).  Each
+// (logit, e) becomes a 64-bit key whose integer order is "larger logit first,
+// equal logits (+0 and -0 identified) lower index first"; all keys are
+// distinct, so the rank of a key -- the number of keys above it -- is its
+// position in that order.  Four threads count each key's rank over a quarter
+// of the keys each.  The experts of rank < k are kept, and
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) with the sum taken in rank
+// order.
+__device__ __forceinline__ uint64_t route_key(float l, int e) {
+  if (l == 0.0f) l = 0.0f;
+  uint32_t b = __builtin_bit_cast(uint32_t, l);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+// Rank top-k of one token with the first NT threads of the workgroup (NT a
+// multiple of 256; every thread reaches the barriers): logit_of(e) gives
+// expert e's logit; NT/256 threads count each key's rank over a share of the
+// keys; out(j, e, w) receives choice j (thread j, j < k).  Shared scratch
+// comes from the caller.
+struct TopkLds {
+  uint64_t key[1024];
+  float lg[1024];
+  int part_rank[4][256];
+  float kv[16];
+  int ki[16];
+};
+
+template <int NT, typename LogitOf, typename Out>
+__device__ __forceinline__ void rank_topk(TopkLds& sm, int E, int k, LogitOf logit_of, Out out) {
+  constexpr int Q = NT / 256;
+  const int tid = threadIdx.x;
+  const int Ep = (E + 7) & ~7;                 // keys padded with 0 (below every real key)
+  for (int e = tid; tid < NT && e < Ep; e += NT) {
+    float s = 0.f;
+    uint64_t kk = 0;
+    if (e < E) {
+      s = logit_of(e);
+      kk = route_key(s, e);
+    }
+    sm.key[e] = kk;
+    sm.lg[e] = s;
+  }
+  __syncthreads();
+  const int q = tid >> 8, el = tid & 255;
+  const int span = Ep / Q;                      // multiple of 2
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int e = e0 + el;
+    int cnt = 0;
+    if (e < E && q < Q) {
+      const uint64_t mine = sm.key[e];
+      const int i_end = (q + 1) * span;
+      for (int i = q * span; i < i_end; i += 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.key[i]);
+        const uint64_t k0 = (uint64_t)v.x | ((uint64_t)v.y << 32);
+        const uint64_t k1 = (uint64_t)v.z | ((uint64_t)v.w << 32);
+        cnt += (k0 > mine) + (k1 > mine);
+      }
+    }
+    if (q < Q) sm.part_rank[q][el] = cnt;
+    __syncthreads();
+    if (q == 0 && e < E) {
+      int rank = 0;
+      for (int i = 0; i < Q; ++i) rank += sm.part_rank[i][el];
+      if (rank < k) {
+        sm.kv[rank] = sm.lg[e];
+        sm.ki[rank] = e;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid < k) {
+    const float top = sm.kv[0];
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += expf(sm.kv[j] - top);
+    out(tid, sm.ki[tid], expf(sm.kv[tid] - top) / z);
+  }
+}
+
+
+}  // namespace qmoe_route

@@ -35,7 +35,8 @@ EXPORTED = [
     "moe_codebook_generate", "moe_packed_bytes", "moe_quantize_pack",
     "moe_route_workspace_bytes", "moe_route", "moe_group_workspace_bytes",
     "moe_group_tokens", "moe_ffn_workspace_bytes", "moe_expert_ffn_decode",
-    "moe_expert_ffn_prefill", "moe_debug_dequant", "moe_profile_next_launch", "moe_last_error",
+    "moe_expert_ffn_prefill", "moe_layer_decode_workspace_bytes", "moe_layer_decode",
+    "moe_debug_dequant", "moe_profile_next_launch", "moe_last_error",
 ]
 
 MOE_KERNEL = {"route_logits": 0, "route_topk": 1, "decode_upgate": 2, "decode_down": 3,
@@ -81,6 +82,9 @@ def _load():
                                                  vp, sz, vp]),
         "moe_expert_ffn_prefill": (ctypes.c_int, [ctypes.POINTER(MoeWeights), vp, i32, i32, vp, vp, vp,
                                                   vp, vp, vp, vp, sz, vp]),
+        "moe_layer_decode_workspace_bytes": (sz, [ctypes.POINTER(MoeWeights), i32, i32]),
+        "moe_layer_decode": (ctypes.c_int, [ctypes.POINTER(MoeWeights), vp, vp, vp, i32, i32, vp, vp, vp,
+                                            vp, sz, vp]),
         "moe_debug_dequant": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp, vp]),
         "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, vp, vp]),
         "moe_last_error": (ctypes.c_char_p, []),
@@ -173,6 +177,16 @@ def moe_ffn_workspace_bytes(w: MoeWeights, T: int, k: int, prefill: bool) -> int
 def moe_expert_ffn_decode(w: MoeWeights, x_bf16, T, k, topk_idx, topk_w, y, ws, stream=None):
     _check(lib.moe_expert_ffn_decode(ctypes.byref(w), _ptr(x_bf16), T, k, _ptr(topk_idx), _ptr(topk_w),
                                      _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_decode_workspace_bytes(w: MoeWeights, T: int, k: int) -> int:
+    return int(lib.moe_layer_decode_workspace_bytes(ctypes.byref(w), T, k))
+
+
+def moe_layer_decode(w: MoeWeights, w_router, logit_bias, x_bf16, T, k, topk_idx, topk_w, y, ws, stream=None):
+    _check(lib.moe_layer_decode(ctypes.byref(w), _ptr(w_router), _ptr(logit_bias), _ptr(x_bf16), T, k,
+                                _ptr(topk_idx), _ptr(topk_w), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)))
 
 
 def moe_expert_ffn_prefill(w: MoeWeights, x_bf16, T, k, topk_idx, topk_w, expert_offsets, sorted_slots,

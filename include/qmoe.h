@@ -224,6 +224,23 @@ int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, int32_t T, i
                           const int32_t* topk_idx, const float* topk_w, float* y,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of moe_layer_decode (0 for invalid arguments). */
+size_t moe_layer_decode_workspace_bytes(const moe_weights* w, int32_t T, int32_t k);
+
+/* One decode step of the whole layer: moe_route then moe_expert_ffn_decode
+ * in one call, with the same results (topk_idx, topk_w and y as those two
+ * calls give; topk_* are outputs here).  One token on a CB2 layer with
+ * hidden <= 4096 and E <= 64*max(4, hidden/256) has its experts ranked
+ * inside the up/gate kernel, from the router's logits, while the shared
+ * expert's weights already stream; other shapes run the router's top-k
+ * kernel first.  Arguments as for those two calls; ws: device scratch
+ * of at least moe_layer_decode_workspace_bytes(w, T, k), 16-byte aligned,
+ * no initialization needed; its first bytes hold h as moe_expert_ffn_decode
+ * leaves it.  Limits: 1 <= T <= 16, 1 <= k <= min(E, 16), E <= 1024. */
+int moe_layer_decode(const moe_weights* w, const float* w_router, const float* logit_bias,
+                     const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx, float* topk_w,
+                     float* y, void* ws, size_t ws_bytes, void* stream);
+
 /* Expert FFN for a prefill chunk (any T >= 1), same result as the decode
  * call, computed as grouped GEMMs over moe_group_tokens' output (device
  * int32 arrays as that call writes them).  Dequantized weights and h are

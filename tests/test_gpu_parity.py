@@ -398,6 +398,74 @@ def test_decode_invalid_and_repeated_ids(q, wl, T):
     assert errp.max() <= TOL_LAYER, errp
 
 
+@pytest.mark.parametrize("wl,T", [(synth.WORKLOADS["decode_b1"], 1), (synth.WORKLOADS["draft_verify_t3"], 3),
+                                  (synth.WORKLOADS["decode_b1_noshared"], 2),
+                                  (synth.WORKLOADS["decode_b16_hot"], 16), (synth.WORKLOADS["k4_h7168_decode"], 1),
+                                  (synth.WORKLOADS["tiny"], 1), (synth.WORKLOADS["tiny"], 4), (ODD_CB2, 3),
+                                  (ODD_K4, 2)],
+                         ids=["decode_b1", "draft_t3", "noshared_T2", "b16_hot", "k4_T1", "tiny_T1", "tiny_T4",
+                              "odd_cb2_T3", "odd_k4_T2"])
+def test_layer_decode_matches_route_then_ffn(q, wl, T):
+    """The one-call decode step gives bit for bit the top-k and outputs of
+    moe_route followed by moe_expert_ffn_decode (up to 3 tokens of a CB2
+    layer rank their experts inside the up/gate kernel; the other shapes run
+    the router's top-k kernel), and its layer output meets the fp64 oracle."""
+    import torch
+    print(f"layer decode {wl.name} T={T}", flush=True)
+    xb, x64 = x_bits(wl, T, step=3)
+    need = set(O.route(x64, synth.router_weight(wl), synth.logit_bias(wl), wl.top_k)[0].reshape(-1).tolist())
+    layer = device_layer(wl, experts=need)
+    k, H, E = wl.top_k, wl.hidden, wl.n_experts
+    idx, w = _route(q, layer, xb, k)
+    y_ref, _ = _decode(q, layer, xb, idx, w, k)
+    li = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    lw = torch.full((T, k), -7.0, dtype=torch.float32, device="cuda")
+    y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.randint(0, 256, (q.moe_layer_decode_workspace_bytes(layer.w, T, k),), dtype=torch.uint8,
+                       device="cuda")
+    q.moe_layer_decode(layer.w, layer.router, layer.bias, _bf16(xb), T, k, li, lw, y, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(li, idx), "top-k indices differ from moe_route's"
+    assert torch.equal(lw, w), "top-k weights differ from moe_route's"
+    assert torch.equal(y, y_ref), "outputs differ from moe_expert_ffn_decode's"
+    _check_layer(y.cpu().numpy(), wl, x64)
+
+
+def test_layer_decode_graph_replay(q):
+    """moe_layer_decode captured once in a HIP graph and replayed on new
+    inputs: each replay equals an eager call."""
+    import torch
+    wl = synth.WORKLOADS["decode_b1"]
+    n = 4
+    xb, x64 = x_bits(wl, n, step=11)
+    need = set(O.route(x64, synth.router_weight(wl), synth.logit_bias(wl), wl.top_k)[0].reshape(-1).tolist())
+    layer = device_layer(wl, experts=need)
+    k, H = wl.top_k, wl.hidden
+    x_dev = _bf16(xb)
+    x_static = x_dev[0:1].clone()
+    li = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    lw = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(q.moe_layer_decode_workspace_bytes(layer.w, 1, k), dtype=torch.uint8, device="cuda")
+    q.moe_layer_decode(layer.w, layer.router, layer.bias, x_static, 1, k, li, lw, y, ws)   # warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.moe_layer_decode(layer.w, layer.router, layer.bias, x_static, 1, k, li, lw, y, ws)
+    ei = torch.empty_like(li)
+    ew = torch.empty_like(lw)
+    ey = torch.empty_like(y)
+    ews = torch.empty_like(ws)
+    for t in range(n):
+        x_static.copy_(x_dev[t:t + 1])
+        g.replay()
+        torch.cuda.synchronize()
+        q.moe_layer_decode(layer.w, layer.router, layer.bias, x_dev[t:t + 1], 1, k, ei, ew, ey, ews)
+        torch.cuda.synchronize()
+        assert torch.equal(li, ei) and torch.equal(lw, ew) and torch.equal(y, ey), f"replay {t} differs"
+        _check_layer(y.cpu().numpy(), wl, x64[t:t + 1])
+
+
 @pytest.mark.parametrize("name", ["decode_b16_hot", "draft_verify_t3"])
 def test_decode_multi_token_full_size(q, name):
     print(name, flush=True)

@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(q):
     names = _declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(q.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -173,6 +173,16 @@ def test_device_call_argument_errors(q):
     assert dec(ctypes.byref(w), None, 1, 8, P, P, P, P, ws, None) == 1
     w2 = _fake_weights(q, fmt_down=3)
     assert dec(ctypes.byref(w2), P, 1, 8, P, P, P, P, ws, None) == 2               # mixed formats
+    # whole decode step
+    lws = q.moe_layer_decode_workspace_bytes(w, 1, 8)
+    assert lws > ws
+    assert q.moe_layer_decode_workspace_bytes(w, 17, 8) == 0
+    lay = lib.moe_layer_decode
+    assert lay(ctypes.byref(w), P, None, P, 1, 8, P, P, P, P, lws - 1, None) == 3   # workspace
+    assert lay(ctypes.byref(w), None, None, P, 1, 8, P, P, P, P, lws, None) == 1    # no router
+    assert lay(ctypes.byref(w), P + 4, None, P, 1, 8, P, P, P, P, lws, None) == 1   # router alignment
+    assert lay(ctypes.byref(w), P, None, P, 17, 8, P, P, P, P, 1 << 30, None) == 1  # T > 16
+    assert lay(ctypes.byref(w2), P, None, P, 1, 8, P, P, P, P, lws, None) == 2      # mixed formats
     w3 = _fake_weights(q, hidden=4000)
     assert dec(ctypes.byref(w3), P, 1, 8, P, P, P, P, ws, None) == 1
     w4 = _fake_weights(q, up=P + 8)
