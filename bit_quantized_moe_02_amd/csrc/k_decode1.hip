@@ -1083,6 +1083,136 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
   }
 }
 
+// K2 down + shared down + combine, with no staging: each unit's slice of h
+// and its per-16-row sums are loaded beside its weight tile (the loads
+// complete together), so a unit is computed as soon as its own bytes are
+// in and compute overlaps the weight stream; only the final cross-wave sum
+// waits for every wave.  Workgroup and units as in dec1_down_kernel.
+struct DnDirect {
+  u32x4 q;            // the lane's 16 bytes of codes
+  uint32_t scm, dd;   // sub-block scales/mins of row n, fp16 d | dmin << 16
+  u32x4 hv;           // the lane's 8 h values (lanes that feed k-block m/2), else 0
+  float xo;           // lane l < 32: value l of the chunk's 16 (X, O) pairs, else 0
+};
+
+__global__ __launch_bounds__(1024) void dec1_down_k2d_kernel(DecArgs a, const float* topk_w, float* y) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  float* red = reinterpret_cast<float*>(smem);                              // [NW][16]
+  const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k = a.k, I = a.I, I_pad = a.I_pad, Is = a.Is;
+  const int n_ck = I_pad / 256, n_cks = Is > 0 ? a.Is_pad / 256 : 0;
+  const int nrp = I_pad / 16, nr = I / 16;
+  const int rt = blockIdx.x;
+  const int n = lane & 15, g4 = lane >> 4, m = lane & 15;
+  const int n_units = k * n_ck, n_sunits = 2 * n_cks;
+  const bool feeds = (m & 1) == (g4 >> 1);             // row 2 kb + g4/2 of A_kb is sub-block m
+  const int kb_act = m >> 1;
+
+  // one descriptor over h, hs and hsum (consecutive in the workspace, h
+  // first); loads past its end give zeros and touch no memory
+  const uint8_t* hb = reinterpret_cast<const uint8_t*>(a.h);
+  const int off_hs = (int)(reinterpret_cast<const uint8_t*>(a.hs) - hb);
+  const int off_xs = (int)(reinterpret_cast<const uint8_t*>(a.hsum) - hb);
+  const __amdgpu_buffer_rsrc_t hrs = tile_rsrc(hb, off_xs + k * nrp * 2 * 4);
+  constexpr int kPast = 0x7FFFFFF0;
+
+  DnDirect P[kDnUnits];
+  int uj[kDnUnits], ukc[kDnUnits], ue[kDnUnits];
+  auto issue_round = [&](int base) {
+    for (int i = 0; i < kDnUnits; ++i) {
+      const int u = base + wave + NW * i;
+      const int j = u / n_ck, kc = u - j * n_ck;
+      uj[i] = j;
+      ukc[i] = kc;
+      const int e = u < n_units ? expert_id(a.topk_idx, j) : -1;
+      ue[i] = (e >= 0 && e < a.E) ? e : -1;
+      const bool ok = ue[i] >= 0;
+      const uint8_t* tile = ok ? a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + kc) * kK2Tile
+                               : a.down;
+      const __amdgpu_buffer_rsrc_t tr = tile_rsrc(tile, ok ? kK2Tile : 0);
+      P[i].q = bload16(tr, 16 * lane);
+      P[i].scm = bload4(tr, 1024 + 16 * n + 4 * g4);
+      P[i].dd = bload4(tr, 1280 + 4 * n);
+      const int col = kc * 256 + kb_act * 32 + g4 * 8;
+      P[i].hv = bload16(hrs, (ok && feeds && col < I) ? (j * I + col) * 2 : kPast);
+      // sums past the matrix's last row are read as zero
+      const int sbl = kc * 16 + (lane >> 1);
+      P[i].xo = __builtin_bit_cast(float, bload4(hrs, (ok && lane < 32 && sbl < nr)
+                                                          ? off_xs + (j * nrp + kc * 16) * 8 + 4 * lane
+                                                          : kPast));
+    }
+  };
+  // shared unit: half a K-chunk (4 k-blocks); lanes m == 0 take their four
+  // 8-column pieces of hs
+  u32x4 sraw[4], shv[4];
+  int s_kc = -1, s_kb0 = 0;
+  auto issue_shared = [&](int su) {
+    const bool valid = su < n_sunits;
+    s_kc = valid ? su >> 1 : -1;
+    s_kb0 = 4 * (su & 1);
+    const uint8_t* tile = valid ? a.sdown + ((size_t)rt * n_cks + s_kc) * kBf16Tile : a.down;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kBf16Tile : 0);
+    for (int q = 0; q < 4; ++q) sraw[q] = bload16(rs, 1024 * (s_kb0 + q) + 16 * lane);
+    for (int q = 0; q < 4; ++q) {
+      const int col = s_kc * 256 + (s_kb0 + q) * 32 + g4 * 8;
+      shv[q] = bload16(hrs, (valid && m == 0 && col < Is) ? off_hs + col * 2 : kPast);
+    }
+  };
+  issue_shared(wave);
+  issue_round(0);
+
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  float acc = 0.f;
+  auto compute_round = [&]() {
+    for (int i = 0; i < kDnUnits; ++i) {
+      if (ue[i] < 0) continue;
+      const int j = uj[i], kc = ukc[i];
+      const DnDirect& p = P[i];
+      // column pair s of an 8-column group sits at slot t(kb, s): h scaled by 4^-t
+      const half8 f = (kb_act & 1)
+                          ? half8{0.00390625f16, 0.00390625f16, 1.0f16, 1.0f16, 0.25f16, 0.25f16, 0.0625f16, 0.0625f16}
+                          : half8{1.0f16, 1.0f16, 0.25f16, 0.25f16, 0.0625f16, 0.0625f16, 0.015625f16, 0.015625f16};
+      const u32x4 hs8 = as_u32x4(as_half8(p.hv) * f);
+      float4v c = zero;
+      for (int kb = 0; kb < 8; ++kb) c = mfma_f16(as_half8(kb == kb_act ? hs8 : z4), as_half8(k2_magic(p.q, kb)), c);
+      // C[4 g4 + q][n] = sub-block 4 g4 + q, whose (X, O) sit in lanes
+      // 8 g4 + 2q and 8 g4 + 2q + 1
+      float dsum = 0.f, msum = 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const float xq = __shfl(p.xo, 8 * g4 + 2 * q), oq = __shfl(p.xo, 8 * g4 + 2 * q + 1);
+        const uint32_t byte = (p.scm >> (8 * q)) & 0xFFu;
+        dsum += (float)(byte & 15u) * (c[q] - oq);
+        msum += (float)(byte >> 4) * xq;
+      }
+      const float wgt = choice_weight(topk_w, j);
+      acc += (wgt * h2f(p.dd & 0xFFFFu)) * dsum - (wgt * h2f(p.dd >> 16)) * msum;
+    }
+  };
+  compute_round();
+  for (int base = kDnUnits * NW; base < n_units; base += kDnUnits * NW) {
+    issue_round(base);
+    compute_round();
+  }
+  for (int su = wave; su < n_sunits; su += NW) {
+    if (su != wave) issue_shared(su);
+    float4v c = zero;
+    for (int q = 0; q < 4; ++q) c = mfma_f16(as_half8(m == 0 ? shv[q] : z4), bf16x8_to_half8(sraw[q]), c);
+    acc += c[0];
+  }
+  // sum the 4 lanes of each output row, then the waves in order
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (lane < 16) red[wave * 16 + lane] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float sum = 0.f;
+    for (int w = 0; w < NW; ++w) sum += red[w * 16 + tid];
+    y[rt * 16 + tid] = sum;
+  }
+}
+
 }  // namespace
 
 namespace qmoe {
@@ -1153,10 +1283,10 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const 
   // the tiles run in a single round (H = 7168: 26.6 us instead of 33.3 us)
   const int nw_dn = a.H / 16 > cus ? 8 : 16;
   void (*fd)(DecArgs, const float*, float*) =
-      fmt_dn == MOE_FMT_K2 ? dec1_down_kernel<MOE_FMT_K2> : dec1_down_kernel<MOE_FMT_K4>;
+      fmt_dn == MOE_FMT_K2 ? dec1_down_k2d_kernel : dec1_down_kernel<MOE_FMT_K4>;
   err = ensure_dyn_lds((const void*)fd);
   if (err != hipSuccess) return err;
-  const size_t lds_dn = dec1_down_lds(a, nw_dn);
+  const size_t lds_dn = fmt_dn == MOE_FMT_K2 ? (size_t)nw_dn * 16 * 4 : dec1_down_lds(a, nw_dn);
   return launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&] {
     hipLaunchKernelGGL(fd, dim3(a.H / 16), dim3(64 * nw_dn), lds_dn, s, a, topk_w, y);
   });

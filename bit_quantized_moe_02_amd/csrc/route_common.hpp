@@ -46,7 +46,7 @@ template <int NT, typename LogitOf, typename Out>
 __device__ __forceinline__ void rank_topk(TopkLds& sm, int E, int k, LogitOf logit_of, Out out) {
   constexpr int Q = NT / 256;
   const int tid = threadIdx.x;
-  const int Ep = (E + 7) & ~7;                 // keys padded with 0 (below every real key)
+  const int Ep = (E + 31) & ~31;               // keys padded with 0 (below every real key)
   for (int e = tid; tid < NT && e < Ep; e += NT) {
     float s = 0.f;
     uint64_t kk = 0;
@@ -59,18 +59,25 @@ __device__ __forceinline__ void rank_topk(TopkLds& sm, int E, int k, LogitOf log
   }
   __syncthreads();
   const int q = tid >> 8, el = tid & 255;
-  const int span = Ep / Q;                      // multiple of 2
+  const int span = Ep / Q;                      // multiple of 8
   for (int e0 = 0; e0 < E; e0 += 256) {
     const int e = e0 + el;
     int cnt = 0;
     if (e < E && q < Q) {
       const uint64_t mine = sm.key[e];
       const int i_end = (q + 1) * span;
-      for (int i = q * span; i < i_end; i += 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.key[i]);
-        const uint64_t k0 = (uint64_t)v.x | ((uint64_t)v.y << 32);
-        const uint64_t k1 = (uint64_t)v.z | ((uint64_t)v.w << 32);
-        cnt += (k0 > mine) + (k1 > mine);
+      // span is a multiple of 8: four 16-byte reads in flight per step
+#pragma unroll 2
+      for (int i = q * span; i < i_end; i += 8) {
+        u32x4 v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const u32x4*>(&sm.key[i + 2 * r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint64_t k0 = (uint64_t)v[r].x | ((uint64_t)v[r].y << 32);
+          const uint64_t k1 = (uint64_t)v[r].z | ((uint64_t)v[r].w << 32);
+          cnt += (k0 > mine) + (k1 > mine);
+        }
       }
     }
     if (q < Q) sm.part_rank[q][el] = cnt;
