@@ -337,6 +337,55 @@ __device__ __forceinline__ void ug_steps(float16v (&acc)[2][kUgTiles][MTA], cons
   }
 }
 
+template <int MTA, typename B>
+__device__ __forceinline__ void ug_steps_bpf(float16v (&acc)[2][kUgTiles][MTA], const B (&cu)[kUgTiles],
+                                         const B (&cg)[kUgTiles], const uint8_t* tab, const uint8_t* buf, int lane) {
+  // A and B of step kk + 1 are read and decoded while step kk multiplies
+  // (CB2: the table reads' latency hides behind the MFMAs; the K4 decode
+  // needs the registers)
+  half8 av[MTA], bu[kUgTiles], bg[kUgTiles];
+  {
+    const uint8_t* p0 = a_step_addr(buf, 0, lane);
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt) av[mt] = a_at(p0, mt);
+#pragma unroll
+    for (int b = 0; b < kUgTiles; ++b) {
+      bu[b] = b_decode(cu[b], 0, tab);
+      bg[b] = b_decode(cg[b], 0, tab);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    half8 an[MTA], bun[kUgTiles], bgn[kUgTiles];
+    if (kk + 1 < 16) {
+      const uint8_t* pn = a_step_addr(buf, kk + 1, lane);
+#pragma unroll
+      for (int mt = 0; mt < MTA; ++mt) an[mt] = a_at(pn, mt);
+#pragma unroll
+      for (int b = 0; b < kUgTiles; ++b) {
+        bun[b] = b_decode(cu[b], kk + 1, tab);
+        bgn[b] = b_decode(cg[b], kk + 1, tab);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MTA; ++mt)
+#pragma unroll
+      for (int b = 0; b < kUgTiles; ++b) {
+        acc[0][b][mt] = mfma32(av[mt], bu[b], acc[0][b][mt]);
+        acc[1][b][mt] = mfma32(av[mt], bg[b], acc[1][b][mt]);
+      }
+    if (kk + 1 < 16) {
+#pragma unroll
+      for (int mt = 0; mt < MTA; ++mt) av[mt] = an[mt];
+#pragma unroll
+      for (int b = 0; b < kUgTiles; ++b) {
+        bu[b] = bun[b];
+        bg[b] = bgn[b];
+      }
+    }
+  }
+}
+
 template <int FMT>
 __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e, int nt) {
   const int64_t p_begin = a.offsets[e], p_end = a.offsets[e + 1];
@@ -384,7 +433,10 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
           b_load(ng[b], tg[b] + (size_t)(chunk + 1) * tb, lane);
         }
       }
-      if (active) ug_steps<MTA>(acc, cu, cg, tab, buf, lane);
+      if (active) {
+        if constexpr (FMT == MOE_FMT_CB2) ug_steps_bpf<MTA>(acc, cu, cg, tab, buf, lane);
+        else ug_steps<MTA>(acc, cu, cg, tab, buf, lane);
+      }
       for (int b = 0; b < kUgTiles; ++b) {
         cu[b] = nu[b];
         cg[b] = ng[b];
