@@ -593,37 +593,33 @@ __global__ __launch_bounds__(256) void pf_x16_kernel(const uint16_t* x, uint16_t
 template <int FMT, int MTA, typename B>
 __device__ __forceinline__ void dn_steps(float16v (&acc)[kDnTiles][kMT], const B (&cur)[kDnTiles], const uint8_t* buf,
                                          int lane) {
-  // A of step kk + 1 is read while step kk decodes and multiplies
-  half8 av[MTA];
-#pragma unroll
-  for (int mt = 0; mt < MTA; ++mt) av[mt] = a_read(buf, mt, 0, lane);
+  // A and B of step kk + 1 are read and decoded while step kk multiplies
   K2Fac fac[kDnTiles];
   if constexpr (FMT == MOE_FMT_K2)
     for (int b = 0; b < kDnTiles; ++b) k2_factors(cur[b], fac[b]);
+  auto decode = [&](int b, int kk) {
+    if constexpr (FMT == MOE_FMT_K2) return b_decode(cur[b], fac[b], kk);
+    else return b_decode(cur[b], kk, nullptr);
+  };
+  half8 av[MTA], bw[kDnTiles];
+#pragma unroll
+  for (int mt = 0; mt < MTA; ++mt) av[mt] = a_read(buf, mt, 0, lane);
+  for (int b = 0; b < kDnTiles; ++b) bw[b] = decode(b, 0);
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
-    half8 an[MTA];
-    if (kk + 1 < 16)
+    half8 an[MTA], bn[kDnTiles];
+    if (kk + 1 < 16) {
 #pragma unroll
       for (int mt = 0; mt < MTA; ++mt) an[mt] = a_read(buf, mt, kk + 1, lane);
-    half8 bw[kDnTiles];
-    for (int b = 0; b < kDnTiles; ++b) {
-      if constexpr (FMT == MOE_FMT_K2) bw[b] = b_decode(cur[b], fac[b], kk);
-      else bw[b] = b_decode(cur[b], kk, nullptr);
+      for (int b = 0; b < kDnTiles; ++b) bn[b] = decode(b, kk + 1);
     }
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt)
       for (int b = 0; b < kDnTiles; ++b) acc[b][mt] = mfma32(av[mt], bw[b], acc[b][mt]);
-    if (kk + 1 < 16)
+    if (kk + 1 < 16) {
 #pragma unroll
       for (int mt = 0; mt < MTA; ++mt) av[mt] = an[mt];
-    // issue order per step: the next step's A reads, then the MFMAs
-    // interleaved with the decode arithmetic
-    __builtin_amdgcn_sched_group_barrier(0x100, MTA, 0);
-#pragma unroll
-    for (int mt = 0; mt < MTA; ++mt) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 24 / MTA, 0);
+      for (int b = 0; b < kDnTiles; ++b) bw[b] = bn[b];
     }
   }
 }
