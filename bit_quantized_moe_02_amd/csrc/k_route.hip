@@ -136,27 +136,49 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(const uint16_t* x, co
   }
 }
 
-constexpr int kTopkThreads = 1024;
+// Top-k of the final logits [T][E], one wave per token (E <= 1024): lane l
+// holds the keys of experts 64q + l; each of the k rounds takes the wave's
+// largest key (the same 64-bit (logit, index) keys as rank_topk, so the same
+// order and ties), the lane that held it drops it, and the kept logits give
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) summed in rank order -- the
+// same operations as rank_topk, so the same bits.  No LDS, no barriers.
+constexpr int kTopkWaves = 4;
+constexpr int kTopkMaxKeys = 16;        // keys per lane: E <= 1024
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits, int n_parts, int T, int E, int k,
-                                                            int32_t* topk_idx, float* topk_w) {
-  __shared__ __align__(16) TopkLds sm;
-  const int t = blockIdx.x;
-  int32_t* oi = topk_idx + (size_t)t * k;
-  float* ow = topk_w + (size_t)t * k;
-  rank_topk<kTopkThreads>(sm, E, k, [&](int e) {
-    float pv[kMaxLogitParts];                  // all partial loads in flight together
+__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* logits, int T, int E, int k,
+                                                               int32_t* topk_idx, float* topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nq = (E + 63) / 64;
+  uint64_t key[kTopkMaxKeys];
 #pragma unroll
-    for (int p = 0; p < kMaxLogitParts; ++p) pv[p] = p < n_parts ? logits[((size_t)p * T + t) * E + e] : 0.f;
-    float s = pv[0];
+  for (int q = 0; q < kTopkMaxKeys; ++q) {
+    const int e = 64 * q + lane;
+    key[q] = (q < nq && e < E) ? route_key(logits[(size_t)t * E + e], e) : 0;
+  }
+  float kv[16];
+  int ki[16];
+  for (int j = 0; j < k; ++j) {
+    uint64_t m = 0;
 #pragma unroll
-    for (int p = 1; p < kMaxLogitParts; ++p)
-      if (p < n_parts) s += pv[p];
-    return s;
-  }, [&](int j, int e, float w) {
-    oi[j] = e;
-    ow[j] = w;
-  });
+    for (int q = 0; q < kTopkMaxKeys; ++q) m = key[q] > m ? key[q] : m;
+    m = wave_max_u64(m);
+#pragma unroll
+    for (int q = 0; q < kTopkMaxKeys; ++q)
+      if (key[q] == m) key[q] = 0;
+    kv[j] = key_logit(m);
+    ki[j] = (int)(0xFFFFFFFFu - (uint32_t)m);
+  }
+  if (lane == 0) {
+    const float top = kv[0];
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += expf(kv[j] - top);
+    for (int j = 0; j < k; ++j) {
+      topk_idx[(size_t)t * k + j] = ki[j];
+      topk_w[(size_t)t * k + j] = expf(kv[j] - top) / z;
+    }
+  }
 }
 
 }  // namespace
@@ -179,9 +201,10 @@ hipError_t launch_route_logits(const uint16_t* x, const float* wr, const float* 
 
 hipError_t launch_route_topk(const float* logits, int n_parts, int T, int E, int k, int32_t* topk_idx,
                              float* topk_w, hipStream_t s) {
+  if (n_parts != 1) return hipErrorInvalidValue;           // the logits kernels write final logits
   return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
-    hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(kTopkThreads), 0, s, logits, n_parts, T, E, k, topk_idx,
-                       topk_w);
+    hipLaunchKernelGGL(topk_kernel, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), 0, s, logits,
+                       T, E, k, topk_idx, topk_w);
   });
 }
 

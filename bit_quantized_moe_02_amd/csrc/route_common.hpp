@@ -101,4 +101,21 @@ __device__ __forceinline__ void rank_topk(TopkLds& sm, int E, int k, LogitOf log
 }
 
 
+// Wave-wide maximum of a 64-bit key (every lane gets it).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  uint32_t b = (uint32_t)(key >> 32);
+  b = (b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b;      // inverse of route_key's map
+  return __builtin_bit_cast(float, b);
+}
+
 }  // namespace qmoe_route
