@@ -67,76 +67,128 @@ __global__ __launch_bounds__(64 * kMaxLogitParts) void logits_small_kernel(const
   }
 }
 
-// Many tokens: fp32 matrix cores (v_mfma_f32_16x16x4_f32).  A workgroup of
-// 4 waves computes 64 tokens x 32 experts; wave w takes tokens 16w..16w+15
-// against two 16-expert tiles.  K is staged through LDS 64 columns at a time
-// (x converted bf16 -> fp32 exactly), the next chunk's loads in flight while
-// the current one is multiplied.
-constexpr int kLgT = 64, kLgE = 32, kLgK = 64;
+// Many tokens on bf16 matrix cores.  The fp32 router weights split exactly
+// into three bf16 parts (w = w1 + w2 + w3: w1 = bf16(w), w2 = bf16(w - w1),
+// w3 = w - w1 - w2, each remainder exact in fp32 and the last one a bf16
+// number), so x·w = x·w1 + x·w2 + x·w3 with every product exact in fp32
+// (8-bit x 8-bit significands) and fp32 accumulation.  A workgroup of 4 waves
+// computes 64 tokens x 32 experts; the experts' weights are split into three
+// bf16 planes in LDS 64 columns at a time (double-buffered, the next chunk's
+// fp32 loads in flight), each wave reads its 16 token rows of x straight from
+// memory (the next chunk's in flight) and runs v_mfma_f32_16x16x32_bf16
+// against two 16-expert tiles.  The columns are split into kLogitSplit parts
+// (grid z), whose partial logits the top-k kernel adds in part order, so
+// that enough workgroups keep loads in flight (the loop is latency-bound).
+constexpr int kLbT = 64, kLbE = 32, kLbK = 64;
+constexpr int kLbRow = kLbK * 2 + 16;                   // bytes per plane row (padded: no bank conflicts)
 
-__device__ __forceinline__ float4v mfma_f32x4(float a, float b, const float4v& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;          // finite inputs
 }
 
-__global__ __launch_bounds__(256) void logits_tiled_kernel(const uint16_t* x, const float* wr,
-                                                           const float* bias, int T, int H, int E,
-                                                           float* logits) {
-  __shared__ float xs[kLgT][kLgK + 1];
-  __shared__ float ws[kLgE][kLgK + 1];
+__global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* x, const float* wr, const float* bias,
+                                                            int T, int H, int E, float* logits) {
+  __shared__ __align__(16) uint8_t wp[2][3][kLbE * kLbRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.y * kLgT, e0 = blockIdx.x * kLgE;
-  // loads of one chunk: x 64 rows x 8 pieces of 8 bf16, w 32 rows x 16 pieces of 4 fp32
-  u32x4 xr[2], wv[2];
-  auto load_chunk = [&](int k0) {
-    for (int i = 0; i < 2; ++i) {
-      const int p = tid + 256 * i;
-      const int r = p >> 3, c = k0 + (p & 7) * 8;
-      xr[i] = (t0 + r < T && c < H) ? load16(x + (size_t)(t0 + r) * H + c) : u32x4{0u, 0u, 0u, 0u};
-      const int re = p >> 4, ce = k0 + (p & 15) * 4;
-      wv[i] = (e0 + re < E && ce < H) ? load16(wr + (size_t)(e0 + re) * H + ce) : u32x4{0u, 0u, 0u, 0u};
-    }
+  const int t0 = blockIdx.y * kLbT, e0 = blockIdx.x * kLbE;
+  const int part = blockIdx.z, n_parts = gridDim.z;
+  const int cpp = (H + kLbK * n_parts - 1) / (kLbK * n_parts) * kLbK;     // columns per part
+  const int k_beg = part * cpp, k_end = min(H, k_beg + cpp);
+  // staging: thread -> expert row sr, columns sc .. sc + 7 of the chunk
+  const int sr = tid >> 3, sc = (tid & 7) * 8;
+  const bool srow = e0 + sr < E;
+  const float* wrow = wr + (size_t)(srow ? e0 + sr : 0) * H;
+  auto load_w = [&](int k0, float4v (&w)[2]) {
+    const bool ok = srow && k0 + sc < k_end;              // H is a multiple of 8
+    const float4v z = {0.f, 0.f, 0.f, 0.f};
+    w[0] = ok ? *reinterpret_cast<const float4v*>(wrow + k0 + sc) : z;
+    w[1] = ok ? *reinterpret_cast<const float4v*>(wrow + k0 + sc + 4) : z;
   };
-  auto store_chunk = [&]() {
-    for (int i = 0; i < 2; ++i) {
-      const int p = tid + 256 * i;
-      const int r = p >> 3, c = (p & 7) * 8;
-      for (int q = 0; q < 4; ++q) {
-        xs[r][c + 2 * q] = bf2f(xr[i][q] & 0xFFFFu);
-        xs[r][c + 2 * q + 1] = bf2f(xr[i][q] >> 16);
+  auto store_w = [&](int buf, const float4v (&w)[2]) {
+    uint32_t p1[4], p2[4], p3[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t b1[2], b2[2], b3[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float v = w[i >> 1][2 * (i & 1) + h];
+        b1[h] = bf16_rne_bits(v);
+        const float r1 = v - __builtin_bit_cast(float, b1[h] << 16);
+        b2[h] = bf16_rne_bits(r1);
+        const float r2 = r1 - __builtin_bit_cast(float, b2[h] << 16);
+        b3[h] = __builtin_bit_cast(uint32_t, r2) >> 16;    // r2 fits in bf16 exactly
       }
-      const int re = p >> 4, ce = (p & 15) * 4;
-      // (bit-cast the whole vector: a bit-cast of a vector element here read
-      // element 0 for every element)
-      const float4v f = __builtin_bit_cast(float4v, wv[i]);
-      for (int q = 0; q < 4; ++q) ws[re][ce + q] = f[q];
+      p1[i] = b1[0] | (b1[1] << 16);
+      p2[i] = b2[0] | (b2[1] << 16);
+      p3[i] = b3[0] | (b3[1] << 16);
+    }
+    const int off = sr * kLbRow + sc * 2;
+    *reinterpret_cast<u32x4*>(&wp[buf][0][off]) = u32x4{p1[0], p1[1], p1[2], p1[3]};
+    *reinterpret_cast<u32x4*>(&wp[buf][1][off]) = u32x4{p2[0], p2[1], p2[2], p2[3]};
+    *reinterpret_cast<u32x4*>(&wp[buf][2][off]) = u32x4{p3[0], p3[1], p3[2], p3[3]};
+  };
+  // A: token row at of this wave's 16, 8 columns at 8 (lane / 16) of each 32-column step
+  const int at = t0 + 16 * wave + (lane & 15);
+  const bool arow = at < T;
+  const uint16_t* xrow = x + (size_t)(arow ? at : 0) * H;
+  auto load_a = [&](int k0, u32x4 (&a)[2]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kk = k0 + 32 * s + 8 * (lane >> 4);
+      a[s] = (arow && kk < k_end) ? load16(xrow + kk) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  float4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  load_chunk(0);
-  for (int k0 = 0; k0 < H; k0 += kLgK) {
-    __syncthreads();
-    store_chunk();
-    __syncthreads();
-    if (k0 + kLgK < H) load_chunk(k0 + kLgK);
-    const int kq = lane >> 4, ri = lane & 15;
-#pragma unroll 4
-    for (int ks = 0; ks < kLgK / 4; ++ks) {
-      const float av = xs[16 * wave + ri][4 * ks + kq];
-      acc0 = mfma_f32x4(av, ws[ri][4 * ks + kq], acc0);
-      acc1 = mfma_f32x4(av, ws[16 + ri][4 * ks + kq], acc1);
+  float4v acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float4v wn[2];
+  u32x4 an[2], ac[2];
+  load_w(k_beg, wn);
+  load_a(k_beg, ac);
+  store_w(0, wn);
+  __syncthreads();
+  for (int k0 = k_beg; k0 < k_end; k0 += kLbK) {
+    const int buf = ((k0 - k_beg) / kLbK) & 1;
+    const bool more = k0 + kLbK < k_end;
+    if (more) {
+      load_w(k0 + kLbK, wn);
+      load_a(k0 + kLbK, an);
     }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const u32x4 bv = *reinterpret_cast<const u32x4*>(
+              &wp[buf][p][(16 * n + (lane & 15)) * kLbRow + (32 * s + 8 * (lane >> 4)) * 2]);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ac[s]),
+                                                          __builtin_bit_cast(bf16x8_t, bv), acc[n], 0, 0, 0);
+        }
+    if (more) {
+      store_w(buf ^ 1, wn);
+      ac[0] = an[0];
+      ac[1] = an[1];
+    }
+    __syncthreads();
   }
-  // C[4(lane/16) + i][lane%16]: token row, expert column
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 16 * wave + 4 * (lane >> 4) + i;
-    if (t >= T) continue;
-    const int ea = e0 + (lane & 15), eb = e0 + 16 + (lane & 15);
-    if (ea < E) logits[(size_t)t * E + ea] = acc0[i] + (bias ? bias[ea] : 0.f);
-    if (eb < E) logits[(size_t)t * E + eb] = acc1[i] + (bias ? bias[eb] : 0.f);
+  // C[4 (l / 16) + i][l % 16]: token row, expert column
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int e = e0 + 16 * n + (lane & 15);
+    if (e >= E) continue;
+    const float b = (bias && part == 0) ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * wave + 4 * (lane >> 4) + i;
+      if (t < T) logits[((size_t)part * T + t) * E + e] = acc[n][i] + b;
+    }
   }
 }
 
-// Top-k of the final logits [T][E], one wave per token (E <= 1024): lane l
+// Top-k of the logits [n_parts][T][E] (parts added in part order), one wave
+// per token (E <= 1024): lane l
 // holds the keys of experts 64q + l; each of the k rounds takes the wave's
 // largest key (the same 64-bit (logit, index) keys as rank_topk, so the same
 // order and ties), the lane that held it drops it, and the kept logits give
@@ -145,8 +197,8 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(const uint16_t* x, co
 constexpr int kTopkWaves = 4;
 constexpr int kTopkMaxKeys = 16;        // keys per lane: E <= 1024
 
-__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* logits, int T, int E, int k,
-                                                               int32_t* topk_idx, float* topk_w) {
+__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* logits, int n_parts, int T, int E,
+                                                               int k, int32_t* topk_idx, float* topk_w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -155,7 +207,12 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* logi
 #pragma unroll
   for (int q = 0; q < kTopkMaxKeys; ++q) {
     const int e = 64 * q + lane;
-    key[q] = (q < nq && e < E) ? route_key(logits[(size_t)t * E + e], e) : 0;
+    float l = 0.f;
+    if (q < nq && e < E) {
+      l = logits[(size_t)t * E + e];
+      for (int p = 1; p < n_parts; ++p) l += logits[((size_t)p * T + t) * E + e];
+    }
+    key[q] = (q < nq && e < E) ? route_key(l, e) : 0;
   }
   float kv[16];
   int ki[16];
@@ -185,7 +242,7 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* logi
 
 namespace qmoe {
 
-int route_logit_parts(int, int) { return 1; }
+int route_logit_parts(int T, int) { return T > 16 ? kLogitSplit : 1; }
 
 hipError_t launch_route_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
                                float* logits, hipStream_t s) {
@@ -194,17 +251,16 @@ hipError_t launch_route_logits(const uint16_t* x, const float* wr, const float* 
     if (T <= 16)
       hipLaunchKernelGGL(logits_small_kernel, dim3(E), dim3(64 * n_parts), 0, s, x, wr, bias, T, H, E, logits);
     else
-      hipLaunchKernelGGL(logits_tiled_kernel, dim3((E + kLgE - 1) / kLgE, (T + kLgT - 1) / kLgT), dim3(256), 0,
-                         s, x, wr, bias, T, H, E, logits);
+      hipLaunchKernelGGL(logits_bf16x3_kernel, dim3((E + kLbE - 1) / kLbE, (T + kLbT - 1) / kLbT, kLogitSplit),
+                         dim3(256), 0, s, x, wr, bias, T, H, E, logits);
   });
 }
 
 hipError_t launch_route_topk(const float* logits, int n_parts, int T, int E, int k, int32_t* topk_idx,
                              float* topk_w, hipStream_t s) {
-  if (n_parts != 1) return hipErrorInvalidValue;           // the logits kernels write final logits
   return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
     hipLaunchKernelGGL(topk_kernel, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), 0, s, logits,
-                       T, E, k, topk_idx, topk_w);
+                       n_parts, T, E, k, topk_idx, topk_w);
   });
 }
 
