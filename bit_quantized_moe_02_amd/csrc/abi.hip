@@ -254,7 +254,7 @@ int run_decode(const char* who, const moe_weights* w, const Geometry& g, const v
   a.ysh = (float*)(wsb + L.ysh);
   a.err_count = (int*)(wsb + L.err);
   const int cus = n_cus();
-  if (T <= kDecPerTokenMax && dec1_down_lds(a, 16) <= 160 * 1024) {
+  if (T <= kDecPerTokenMax && dec1_down_lds(a, g.fmt_dn, 16) <= 160 * 1024) {
     // few tokens: the single-token kernels once per token (exact weights)
     const int nw_cb2 = n_chunks < 4 ? 4 : n_chunks;
     // (one token only: for more, one top-k launch for all of them is cheaper

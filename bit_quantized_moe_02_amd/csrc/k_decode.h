@@ -45,7 +45,8 @@ hipError_t launch_dec_upgate(const DecArgs& a, int fmt, int cpw, int grid, hipSt
 hipError_t launch_dec_down(const DecArgs& a, int fmt, int grid, hipStream_t s);
 // Single-token path (k_decode1.hip): up/gate then down with the shared
 // expert and the weighted combine fused; writes y directly.
-size_t dec1_down_lds(const DecArgs& a, int nw);
+// LDS of the single-token down kernel of format fmt_dn with nw waves.
+size_t dec1_down_lds(const DecArgs& a, int fmt_dn, int nw);
 // LDS of the single-token CB2 up/gate with nw waves (route: it ranks the
 // token's experts itself).
 size_t dec1_cb2_upgate_lds(int nw, bool route);

@@ -828,39 +828,23 @@ size_t dec1_k4_upgate_lds(int H, int nw) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-wave payload of one routed down unit (one K-chunk of one 16-row tile).
-
-template <int FMT>
-struct DnPay;
-template <>
-struct DnPay<MOE_FMT_K2> {
-  u32x4 q;
-  uint32_t scm, dd;
-};
-template <>
-struct DnPay<MOE_FMT_K4> {
+// Per-wave payload of one routed K4 down unit (one K-chunk of one 16-row tile).
+struct DnPay4 {
   u32x4 q0, q1;
   uint32_t s0, s1, s2, dd;
 };
 
-template <int FMT>
-__device__ __forceinline__ void dn_load(DnPay<FMT>& p, __amdgpu_buffer_rsrc_t tile, int lane) {
-  const int n = lane & 15, g4 = lane >> 4;
-  if constexpr (FMT == MOE_FMT_K2) {
-    p.q = bload16(tile, 16 * lane);
-    p.scm = bload4(tile, 1024 + 16 * n + 4 * g4);
-    p.dd = bload4(tile, 1280 + 4 * n);
-  } else {
-    p.q0 = bload16(tile, 16 * lane);
-    p.q1 = bload16(tile, 1024 + 16 * lane);
-    p.s0 = bload4(tile, 2048 + 12 * n);
-    p.s1 = bload4(tile, 2048 + 12 * n + 4);
-    p.s2 = bload4(tile, 2048 + 12 * n + 8);
-    p.dd = bload4(tile, 2240 + 4 * n);
-  }
+__device__ __forceinline__ void dn_load4(DnPay4& p, __amdgpu_buffer_rsrc_t tile, int lane) {
+  const int n = lane & 15;
+  p.q0 = bload16(tile, 16 * lane);
+  p.q1 = bload16(tile, 1024 + 16 * lane);
+  p.s0 = bload4(tile, 2048 + 12 * n);
+  p.s1 = bload4(tile, 2048 + 12 * n + 4);
+  p.s2 = bload4(tile, 2048 + 12 * n + 8);
+  p.dd = bload4(tile, 2240 + 4 * n);
 }
 
-// Down + shared down + combine.  Workgroup = one 16-row tile of y; the k
+// K4 down + shared down + combine, activations staged in LDS.  Workgroup = one 16-row tile of y; the k
 // routed down matrices and the shared one form one stacked GEMV over
 // K = k*I + I_s, split over the waves in units of one 256-column K-chunk
 // (routed) or half a chunk (shared).  Every wave issues the loads of all its
@@ -868,15 +852,14 @@ __device__ __forceinline__ void dn_load(DnPay<FMT>& p, __amdgpu_buffer_rsrc_t ti
 constexpr int kDnUnits = 4;    // routed units held in registers per wave
 constexpr int kStageVec = 6;   // staged 16-byte vectors per thread per pass
 
-template <int FMT>
-__global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float* topk_w, float* y) {
+__global__ __launch_bounds__(1024) void dec1_k4_down_kernel(DecArgs a, const float* topk_w, float* y) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = a.k, I = a.I, I_pad = a.I_pad, Is = a.Is, Is_pad = a.Is_pad;
   const int n_ck = I_pad / 256, n_cks = Is > 0 ? Is_pad / 256 : 0;
   // LDS: staged activations (fp16), per-16-row sums, reduction
-  _Float16* hst = reinterpret_cast<_Float16*>(smem);                        // [k][I_pad] (K2: prescaled)
+  _Float16* hst = reinterpret_cast<_Float16*>(smem);                        // [k][I_pad]
   _Float16* hss = hst + (size_t)k * I_pad;                                    // [Is_pad]
   size_t off = ((size_t)k * I_pad + Is_pad) * 2;
   off = (off + 15) & ~size_t(15);
@@ -889,13 +872,13 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
   const int rt = blockIdx.x;
   const int n = lane & 15, g4 = lane >> 4, m = lane & 15;
   const int n_units = k * n_ck, n_sunits = 2 * n_cks;
-  const size_t tb = FMT == MOE_FMT_K2 ? kK2Tile : kK4Tile;
+  const size_t tb = kK4Tile;
 
   // ---- loads, oldest first: the first pass of the staged activations, the
   // shared unit, then the routed units wave + NW*i.  A wave's loads complete
   // in issue order, so the staging waits only for the activations, not
   // behind weight tiles.
-  DnPay<FMT> P[kDnUnits];
+  DnPay4 P[kDnUnits];
   int uj[kDnUnits], ukc[kDnUnits], ue[kDnUnits];
   // (units past the end or naming an invalid expert load zeros, no memory)
   auto issue_round = [&](int base) {
@@ -908,7 +891,7 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
       ue[i] = (e >= 0 && e < a.E) ? e : -1;
       const uint8_t* tile = ue[i] >= 0 ? a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_ck + ukc[i]) * tb
                                        : a.down;
-      dn_load<FMT>(P[i], tile_rsrc(tile, ue[i] >= 0 ? (int)tb : 0), lane);
+      dn_load4(P[i], tile_rsrc(tile, ue[i] >= 0 ? (int)tb : 0), lane);
     }
   };
   u32x4 sraw[4];
@@ -936,8 +919,8 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
   const int off_xs = (int)(reinterpret_cast<const uint8_t*>(a.hsum) - hb);
   const __amdgpu_buffer_rsrc_t hrs = tile_rsrc(hb, off_xs + k * nrp * 2 * 4);
   // Offsets and destinations first, then the loads as one straight run.
-  // dst: LDS byte offset | scaling flags (0x20000000, 0x40000000) | 0x10000000
-  // for a sum pair whose second half lies past the end; -1 = nothing.
+  // dst: LDS byte offset | 0x10000000 for a sum pair whose second half lies
+  // past the end; -1 = nothing.
   auto stage_load = [&](int base, u32x4 (&v)[kStageVec], int (&dst)[kStageVec]) {
     const int nrh = nrp / 2;
     int off[kStageVec];
@@ -956,7 +939,6 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
       int d = -1;
       if (k0) {
         d = (j * I_pad + 8 * c) * 2;
-        if (FMT == MOE_FMT_K2) d |= (c >> 2) & 1 ? 0x40000000 : 0x20000000;
       } else if (k1) {
         d = (int)((uint8_t*)(xo + ((size_t)j * nrp + 2 * c) * 2) - smem);
         if (2 * c + 1 >= nr) d |= 0x10000000;
@@ -974,13 +956,6 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
       if (dst[i] < 0) continue;
       u32x4 w = v[i];
       if (dst[i] & 0x10000000) w = u32x4{w.x, w.y, 0u, 0u};      // odd tail: one sum pair
-      if (FMT == MOE_FMT_K2 && (dst[i] & 0x60000000)) {
-        // column pair s of an 8-column group sits at slot t(kb, s); scale by 4^-t
-        const half8 f = (dst[i] & 0x40000000)
-                            ? half8{0.00390625f16, 0.00390625f16, 1.0f16, 1.0f16, 0.25f16, 0.25f16, 0.0625f16, 0.0625f16}
-                            : half8{1.0f16, 1.0f16, 0.25f16, 0.25f16, 0.0625f16, 0.0625f16, 0.015625f16, 0.015625f16};
-        w = as_u32x4(as_half8(w) * f);
-      }
       *reinterpret_cast<u32x4*>(smem + (dst[i] & 0x0FFFFFFF)) = w;
     }
   };
@@ -1014,45 +989,20 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
       if (ue[i] < 0) continue;
       const int j = uj[i], kc = ukc[i];
       const float wgt = choice_weight(topk_w, j);
-      const DnPay<FMT>& p = P[i];
+      const DnPay4& p = P[i];
       const _Float16* hbase = hst + (size_t)j * I_pad + kc * 256 + g4 * 8;
-      if constexpr (FMT == MOE_FMT_K2) {
-        // row 2 kb + g4/2 of A_kb holds sub-block 2 kb + g4/2 of h: a lane
-        // (m, g4) feeds only k-block m/2, and only when m's parity is g4/2,
-        // so it reads its one vector once and A_kb is that vector or zero
-        const bool feeds = (m & 1) == (g4 >> 1);
-        const int kb_act = m >> 1;
-        const u32x4 hv = load16(feeds ? reinterpret_cast<const uint8_t*>(hbase + kb_act * 32) : zero16);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        float4v c = zero;
-        for (int kb = 0; kb < 8; ++kb) c = mfma_f16(as_half8(kb == kb_act ? hv : z), as_half8(k2_magic(p.q, kb)), c);
-        // C[4 g4 + i][n] = sub-block 4 g4 + i of this super-block; xo holds
-        // (X, O) of sub-block s at 2s, 2s+1
-        const float4v X = *reinterpret_cast<const float4v*>(xo + ((size_t)j * (I_pad / 16) + kc * 16 + 4 * g4) * 2);
-        const float4v O = *reinterpret_cast<const float4v*>(xo + ((size_t)j * (I_pad / 16) + kc * 16 + 4 * g4) * 2 + 4);
-        const float xs[4] = {X[0], X[2], O[0], O[2]};
-        const float os[4] = {X[1], X[3], O[1], O[3]};
-        float dsum = 0.f, msum = 0.f;
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t byte = (p.scm >> (8 * q)) & 0xFFu;
-          dsum += (float)(byte & 15u) * (c[q] - os[q]);
-          msum += (float)(byte >> 4) * xs[q];
-        }
-        acc += (wgt * h2f(p.dd & 0xFFFFu)) * dsum - (wgt * h2f(p.dd >> 16)) * msum;
-      } else {  // K4
-        const float d = h2f(p.dd & 0xFFFFu), dmin = h2f(p.dd >> 16);
-        float part = 0.f;
-        for (int kb = 0; kb < 8; ++kb) {
-          const uint8_t* src = (m == 0) ? reinterpret_cast<const uint8_t*>(hbase + kb * 32) : zero16;
-          const uint32_t w = kb < 4 ? p.q0[kb & 3] : p.q1[kb & 3];
-          const float4v c = mfma_f16(as_half8(load16(src)), as_half8(k4_magic(w)), zero);
-          const float dsc = d * (float)k4_scale_value(p.s0, p.s1, p.s2, kb);
-          const float corr = 1024.0f * dsc + dmin * (float)k4_scale_value(p.s0, p.s1, p.s2, 8 + kb);
-          const float* xk = xo + ((size_t)j * (I_pad / 16) + kc * 16 + 2 * kb) * 2;
-          part += dsc * c[0] - corr * (xk[0] + xk[2]);
-        }
-        if (g4 == 0) acc += wgt * part;
+      const float d = h2f(p.dd & 0xFFFFu), dmin = h2f(p.dd >> 16);
+      float part = 0.f;
+      for (int kb = 0; kb < 8; ++kb) {
+        const uint8_t* src = (m == 0) ? reinterpret_cast<const uint8_t*>(hbase + kb * 32) : zero16;
+        const uint32_t w = kb < 4 ? p.q0[kb & 3] : p.q1[kb & 3];
+        const float4v c = mfma_f16(as_half8(load16(src)), as_half8(k4_magic(w)), zero);
+        const float dsc = d * (float)k4_scale_value(p.s0, p.s1, p.s2, kb);
+        const float corr = 1024.0f * dsc + dmin * (float)k4_scale_value(p.s0, p.s1, p.s2, 8 + kb);
+        const float* xk = xo + ((size_t)j * (I_pad / 16) + kc * 16 + 2 * kb) * 2;
+        part += dsc * c[0] - corr * (xk[0] + xk[2]);
       }
+      if (g4 == 0) acc += wgt * part;
     }
   };
   compute_round();
@@ -1087,7 +1037,7 @@ __global__ __launch_bounds__(1024) void dec1_down_kernel(DecArgs a, const float*
 // and its per-16-row sums are loaded beside its weight tile (the loads
 // complete together), so a unit is computed as soon as its own bytes are
 // in and compute overlaps the weight stream; only the final cross-wave sum
-// waits for every wave.  Workgroup and units as in dec1_down_kernel.
+// waits for every wave.  Workgroup and units as in dec1_k4_down_kernel.
 struct DnDirect {
   u32x4 q;            // the lane's 16 bytes of codes
   uint32_t scm, dd;   // sub-block scales/mins of row n, fp16 d | dmin << 16
@@ -1224,7 +1174,8 @@ size_t dec1_upgate_lds(const DecArgs& a, int fmt, int nw) {
   return off + (size_t)kBatch * nw * 2 * 16 * 4;
 }
 
-size_t dec1_down_lds(const DecArgs& a, int nw) {
+size_t dec1_down_lds(const DecArgs& a, int fmt_dn, int nw) {
+  if (fmt_dn == MOE_FMT_K2) return (size_t)nw * 16 * 4;  // direct loads: the reduction only
   size_t off = ((size_t)a.k * a.I_pad + a.Is_pad) * 2;
   off = (off + 15) & ~size_t(15);
   off += 16 + (size_t)a.k * (a.I_pad / 16) * 2 * 4;
@@ -1282,11 +1233,10 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const 
   // compute units in one round, else 8 so that two workgroups share a CU and
   // the tiles run in a single round (H = 7168: 26.6 us instead of 33.3 us)
   const int nw_dn = a.H / 16 > cus ? 8 : 16;
-  void (*fd)(DecArgs, const float*, float*) =
-      fmt_dn == MOE_FMT_K2 ? dec1_down_k2d_kernel : dec1_down_kernel<MOE_FMT_K4>;
+  void (*fd)(DecArgs, const float*, float*) = fmt_dn == MOE_FMT_K2 ? dec1_down_k2d_kernel : dec1_k4_down_kernel;
   err = ensure_dyn_lds((const void*)fd);
   if (err != hipSuccess) return err;
-  const size_t lds_dn = fmt_dn == MOE_FMT_K2 ? (size_t)nw_dn * 16 * 4 : dec1_down_lds(a, nw_dn);
+  const size_t lds_dn = dec1_down_lds(a, fmt_dn, nw_dn);
   return launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&] {
     hipLaunchKernelGGL(fd, dim3(a.H / 16), dim3(64 * nw_dn), lds_dn, s, a, topk_w, y);
   });

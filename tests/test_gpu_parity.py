@@ -326,11 +326,15 @@ def test_decode_single_token_full_size(q, name, steps):
 
 ODD_CB2 = register(synth.Workload("odd_cb2_test", 512, 160, 32, 5, 96, "cb2", "cb2", "k2", seed=13, tokens=1))
 ODD_K4 = register(synth.Workload("odd_k4_test", 768, 96, 24, 3, 48, "k4", "k4", "k4", seed=14, tokens=1))
+# k = 16 choices of I = 6144: the K2 down's activations (192 KiB as fp16)
+# would not fit one workgroup's LDS, and the single-token down loads them
+# beside each weight tile instead
+WIDE_K2 = register(synth.Workload("wide_k2_test", 512, 6144, 16, 16, 0, "cb2", "cb2", "k2", seed=15, tokens=1))
 
 
-@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], ODD_CB2, ODD_K4], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], ODD_CB2, ODD_K4, WIDE_K2], ids=lambda w: w.name)
 def test_decode_single_token_odd_shapes(q, wl):
-    """The single-token kernels on padded I / I_s, k = 2, 3, 5, with and
+    """The single-token kernels on padded I / I_s, k = 2, 3, 5, 16, with and
     without a shared expert, against the oracle and against the multi-token
     kernels on the same token."""
     print(f"decode T=1 {wl.name}", flush=True)
