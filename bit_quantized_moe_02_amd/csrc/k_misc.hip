@@ -89,8 +89,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* packed, int
 // Wave w owns the contiguous slot range [w*S, (w+1)*S): it counts its
 // experts, the counts are scanned (expert-major, then wave order), and each
 // wave writes its slots in slot order, ranking equal experts inside every
-// 64-slot chunk with a lane-order count.
+// 64-slot chunk with a lane-order count.  A wave loads the expert ids of
+// kGroupBatch chunks together (one memory latency per batch, not per chunk).
 constexpr int kGroupWaves = 16;
+constexpr int kGroupBatch = 16;
 
 __global__ __launch_bounds__(1024) void group_kernel(const int32_t* topk_idx, int n_slots, int E,
                                                      int32_t* offsets, int32_t* sorted_slots,
@@ -103,11 +105,28 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* topk_idx, in
   __syncthreads();
   const int S = (n_slots + kGroupWaves - 1) / kGroupWaves;
   const int s0 = wave * S, s1 = min(n_slots, s0 + S);
+  // ids of slots cb + 64 i + lane, i < kGroupBatch (only called with
+  // s0 <= cb < s1; a lane past s1 reads slot s1 - 1 and ignores it)
+  auto load_ids = [&](int cb, int (&ev)[kGroupBatch]) {
+#pragma unroll
+    for (int i = 0; i < kGroupBatch; ++i) {
+      const int s = cb + 64 * i + lane;
+      ev[i] = topk_idx[s < s1 ? s : s1 - 1];
+    }
+  };
   int bad = 0;
-  for (int s = s0 + lane; s < s1; s += 64) {
-    const int e = topk_idx[s];
-    if (e >= 0 && e < E) atomicAdd(&cnt[wave * E + e], 1);
-    else ++bad;
+  for (int cb = s0; cb < s1; cb += 64 * kGroupBatch) {
+    int ev[kGroupBatch];
+    load_ids(cb, ev);
+#pragma unroll
+    for (int i = 0; i < kGroupBatch; ++i) {
+      // (no branch before the id is used: a load whose value is read only
+      // inside a branch is moved into it, and then waited for alone)
+      const int e = ev[i];
+      const bool in = cb + 64 * i + lane < s1, valid = in & (e >= 0) & (e < E);
+      if (valid) atomicAdd(&cnt[wave * E + e], 1);
+      bad += in & !valid;
+    }
   }
   __syncthreads();
   // per expert: cursors = exclusive prefix over waves, totals
@@ -146,31 +165,38 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* topk_idx, in
   }
   __syncthreads();
   const int id_bits = 32 - __builtin_clz((unsigned)(E > 1 ? E - 1 : 1));   // bits of an id in [0, E)
-  for (int c0 = s0; c0 < s1; c0 += 64) {
-    const int s = c0 + lane;
-    const int e = (s < s1) ? topk_idx[s] : -1;
-    const bool valid = e >= 0 && e < E;
-    // lanes holding the same id: intersect, bit by bit, the ballots of the
-    // lanes that agree with this lane's id bit
-    uint64_t match = ~0ull;
-    for (int b = 0; b < id_bits; ++b) {
-      const uint64_t ones = __ballot((e >> b) & 1);
-      match &= ((e >> b) & 1) ? ones : ~ones;
+  for (int cb = s0; cb < s1; cb += 64 * kGroupBatch) {
+    int ev[kGroupBatch];
+    load_ids(cb, ev);
+#pragma unroll
+    for (int i = 0; i < kGroupBatch; ++i) {
+      const int c0 = cb + 64 * i;
+      if (c0 >= s1) break;                       // the same for the whole wave
+      const int s = c0 + lane;
+      const int e = (s < s1) ? ev[i] : -1;
+      const bool valid = e >= 0 && e < E;
+      // lanes holding the same id: intersect, bit by bit, the ballots of the
+      // lanes that agree with this lane's id bit
+      uint64_t match = ~0ull;
+      for (int b = 0; b < id_bits; ++b) {
+        const uint64_t ones = __ballot((e >> b) & 1);
+        match &= ((e >> b) & 1) ? ones : ~ones;
+      }
+      match &= __ballot(valid);
+      const int rank = __popcll(match & ((1ull << lane) - 1ull));
+      const int same = __popcll(match);
+      int cursor = 0;
+      if (valid) cursor = cnt[wave * E + e];
+      if (valid) {
+        const int pos = tot[e] + cursor + rank;
+        sorted_slots[pos] = s;
+        slot_pos[s] = pos;
+      } else if (s < s1) {
+        slot_pos[s] = -1;
+      }
+      // the last lane of each expert in this chunk advances the cursor
+      if (valid && rank == same - 1) cnt[wave * E + e] = cursor + same;
     }
-    match &= __ballot(valid);
-    const int rank = __popcll(match & ((1ull << lane) - 1ull));
-    const int same = __popcll(match);
-    int cursor = 0;
-    if (valid) cursor = cnt[wave * E + e];
-    if (valid) {
-      const int pos = tot[e] + cursor + rank;
-      sorted_slots[pos] = s;
-      slot_pos[s] = pos;
-    } else if (s < s1) {
-      slot_pos[s] = -1;
-    }
-    // the last lane of each expert in this chunk advances the cursor
-    if (valid && rank == same - 1) cnt[wave * E + e] = cursor + same;
   }
   for (int o = 1; o < 64; o <<= 1) bad += __shfl_xor(bad, o);
   if (lane == 0 && bad) atomicAdd(err_count, bad);

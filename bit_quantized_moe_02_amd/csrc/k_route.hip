@@ -79,6 +79,11 @@ __global__ __launch_bounds__(64 * kMaxLogitParts) void logits_small_kernel(const
 // against two 16-expert tiles.  The columns are split into kLogitSplit parts
 // (grid z), whose partial logits the top-k kernel adds in part order, so
 // that enough workgroups keep loads in flight (the loop is latency-bound).
+// Consecutive workgroups go to the 8 XCDs in turn (workgroup L on XCD L % 8,
+// each XCD with its own L2): workgroup L runs block b = (L % 8) (N / 8) + L / 8
+// of the N blocks (expert block fastest, then token tile, then part), so each
+// XCD takes a contiguous run of blocks, a token tile's expert blocks share one
+// XCD and its L2 fetches that tile of x once (b = L when 8 does not divide N).
 constexpr int kLbT = 64, kLbE = 32, kLbK = 64;
 constexpr int kLbRow = kLbK * 2 + 16;                   // bytes per plane row (padded: no bank conflicts)
 
@@ -90,11 +95,14 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 }
 
 __global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* x, const float* wr, const float* bias,
-                                                            int T, int H, int E, float* logits) {
+                                                            int T, int H, int E, int n_parts, float* logits) {
   __shared__ __align__(16) uint8_t wp[2][3][kLbE * kLbRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.y * kLbT, e0 = blockIdx.x * kLbE;
-  const int part = blockIdx.z, n_parts = gridDim.z;
+  const int N = gridDim.x, L = blockIdx.x;
+  const int b = (N & 7) ? L : (L & 7) * (N >> 3) + (L >> 3);
+  const int nbe = (E + kLbE - 1) / kLbE, nbt = (T + kLbT - 1) / kLbT;
+  const int t0 = (b / nbe) % nbt * kLbT, e0 = b % nbe * kLbE;
+  const int part = b / (nbe * nbt);
   const int cpp = (H + kLbK * n_parts - 1) / (kLbK * n_parts) * kLbK;     // columns per part
   const int k_beg = part * cpp, k_end = min(H, k_beg + cpp);
   // staging: thread -> expert row sr, columns sc .. sc + 7 of the chunk
@@ -248,11 +256,13 @@ hipError_t launch_route_logits(const uint16_t* x, const float* wr, const float* 
                                float* logits, hipStream_t s) {
   const int n_parts = std::min(kMaxLogitParts, (H + 511) / 512);
   return launch_timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
-    if (T <= 16)
+    if (T <= 16) {
       hipLaunchKernelGGL(logits_small_kernel, dim3(E), dim3(64 * n_parts), 0, s, x, wr, bias, T, H, E, logits);
-    else
-      hipLaunchKernelGGL(logits_bf16x3_kernel, dim3((E + kLbE - 1) / kLbE, (T + kLbT - 1) / kLbT, kLogitSplit),
-                         dim3(256), 0, s, x, wr, bias, T, H, E, logits);
+    } else {
+      const int blocks = (E + kLbE - 1) / kLbE * ((T + kLbT - 1) / kLbT) * kLogitSplit;
+      hipLaunchKernelGGL(logits_bf16x3_kernel, dim3(blocks), dim3(256), 0, s, x, wr, bias, T, H, E, kLogitSplit,
+                         logits);
+    }
   });
 }
 
