@@ -203,34 +203,41 @@ __global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* x, c
 // w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) summed in rank order -- the
 // same operations as rank_topk, so the same bits.  No LDS, no barriers.
 constexpr int kTopkWaves = 4;
-constexpr int kTopkMaxKeys = 16;        // keys per lane: E <= 1024
 
-__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* logits, int n_parts, int T, int E,
-                                                               int k, int32_t* topk_idx, float* topk_w) {
+template <int NQ, int P>
+__global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* logits, int T, int E, int k,
+                                                               int32_t* topk_idx, float* topk_w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int nq = (E + 63) / 64;
-  uint64_t key[kTopkMaxKeys];
+  // all NQ x P loads are issued before the first is used (a load whose value
+  // is read only inside a branch is waited for alone).  A lane past the last
+  // expert reads expert E - 1 and keys logit -inf with its own index e >= E:
+  // below every real expert's key (also a real -inf, whose index is
+  // smaller), so never taken as k <= E.
+  float pv[P][NQ];
 #pragma unroll
-  for (int q = 0; q < kTopkMaxKeys; ++q) {
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) pv[p][q] = logits[((size_t)p * T + t) * E + min(64 * q + lane, E - 1)];
+  uint64_t key[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    float l = pv[0][q];
+#pragma unroll
+    for (int p = 1; p < P; ++p) l += pv[p][q];
     const int e = 64 * q + lane;
-    float l = 0.f;
-    if (q < nq && e < E) {
-      l = logits[(size_t)t * E + e];
-      for (int p = 1; p < n_parts; ++p) l += logits[((size_t)p * T + t) * E + e];
-    }
-    key[q] = (q < nq && e < E) ? route_key(l, e) : 0;
+    key[q] = route_key(e < E ? l : -__builtin_inff(), e);
   }
   float kv[16];
   int ki[16];
   for (int j = 0; j < k; ++j) {
     uint64_t m = 0;
 #pragma unroll
-    for (int q = 0; q < kTopkMaxKeys; ++q) m = key[q] > m ? key[q] : m;
+    for (int q = 0; q < NQ; ++q) m = key[q] > m ? key[q] : m;
     m = wave_max_u64(m);
 #pragma unroll
-    for (int q = 0; q < kTopkMaxKeys; ++q)
+    for (int q = 0; q < NQ; ++q)
       if (key[q] == m) key[q] = 0;
     kv[j] = key_logit(m);
     ki[j] = (int)(0xFFFFFFFFu - (uint32_t)m);
@@ -244,6 +251,26 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk_kernel(const float* logi
       topk_w[(size_t)t * k + j] = expf(kv[j] - top) / z;
     }
   }
+}
+
+// Top-k of a few tokens' single-part logits, one 1024-thread workgroup per
+// token ranking every key at once (rank_topk: the same keys and the same
+// weight arithmetic as topk_kernel, so the same bits).  Below ~16 tokens the
+// wave kernel's k serial rounds of wave maxima cost more than this one's
+// barriers.
+constexpr int kTopkRankThreads = 1024;
+
+__global__ __launch_bounds__(kTopkRankThreads) void topk_rank_kernel(const float* logits, int E, int k,
+                                                                     int32_t* topk_idx, float* topk_w) {
+  __shared__ __align__(16) TopkLds sm;
+  const int t = blockIdx.x;
+  const float* lt = logits + (size_t)t * E;
+  int32_t* oi = topk_idx + (size_t)t * k;
+  float* ow = topk_w + (size_t)t * k;
+  rank_topk<kTopkRankThreads>(sm, E, k, [&](int e) { return lt[e]; }, [&](int j, int e, float w) {
+    oi[j] = e;
+    ow[j] = w;
+  });
 }
 
 }  // namespace
@@ -268,9 +295,23 @@ hipError_t launch_route_logits(const uint16_t* x, const float* wr, const float* 
 
 hipError_t launch_route_topk(const float* logits, int n_parts, int T, int E, int k, int32_t* topk_idx,
                              float* topk_w, hipStream_t s) {
+  // keys per lane NQ = ceil(E / 64) rounded up to a power of two (E <= 1024);
+  // parts: 1 or kLogitSplit, as the logits kernels write them
+  if (E < 1 || E > 1024 || (n_parts != 1 && n_parts != kLogitSplit)) return hipErrorInvalidValue;
+  const int nq = (E + 63) / 64;
+  const bool split = n_parts != 1;
+  void (*fk)(const float*, int, int, int, int32_t*, float*) =
+      nq <= 1   ? (split ? topk_kernel<1, kLogitSplit> : topk_kernel<1, 1>)
+      : nq <= 2 ? (split ? topk_kernel<2, kLogitSplit> : topk_kernel<2, 1>)
+      : nq <= 4 ? (split ? topk_kernel<4, kLogitSplit> : topk_kernel<4, 1>)
+      : nq <= 8 ? (split ? topk_kernel<8, kLogitSplit> : topk_kernel<8, 1>)
+                : (split ? topk_kernel<16, kLogitSplit> : topk_kernel<16, 1>);
   return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
-    hipLaunchKernelGGL(topk_kernel, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), 0, s, logits,
-                       n_parts, T, E, k, topk_idx, topk_w);
+    if (T <= 16 && n_parts == 1)
+      hipLaunchKernelGGL(topk_rank_kernel, dim3(T), dim3(kTopkRankThreads), 0, s, logits, E, k, topk_idx, topk_w);
+    else
+      hipLaunchKernelGGL(fk, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), 0, s, logits, T, E, k,
+                         topk_idx, topk_w);
   });
 }
 
