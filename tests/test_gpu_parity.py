@@ -116,10 +116,13 @@ def test_dequant_bit_exact(q, fmt, rows, k):
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 3), ("decode_b16_hot", 16), ("decode_b1", 16),
                                     ("decode_b1", 2), ("draft_verify_t3", 3), ("k4_h7168_decode", 3),
-                                    ("prefill_2048", 512)])
+                                    ("prefill_2048", 512), ("odd_cb2_test", 40), ("odd_k4_test", 100)])
 def test_route_matches_oracle(q, name, T):
+    """Up to 16 tokens: the per-expert GEMV and one ranking workgroup per
+    token; more: the matrix-core logits in column parts and one wave per
+    token (E = 32 and 24 leave lanes without an expert)."""
     print(f"route {name} T={T}", flush=True)
-    wl = synth.WORKLOADS[name]
+    wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else {w.name: w for w in (ODD_CB2, ODD_K4)}[name]
     layer = device_layer(wl, experts=[])
     xb, x64 = x_bits(wl, T)
     idx, w = _route(q, layer, xb, wl.top_k)
