@@ -144,7 +144,7 @@ def test_worked_kquant_blocks():
     g = _golden("worked_examples.json")
     for ex in g["kquant"]:
         fmt = ex["fmt"]
-        B, Q, S = O.kq_params(fmt)
+        B, Q, S = KQ_FIELDS[fmt]
         q = np.zeros((1, 256), dtype=np.uint8)
         q[0, :len(ex["q"])] = ex["q"]
         f = {"q": q,
@@ -242,10 +242,16 @@ def test_cb2_zero_and_edge_groups():
 # ---------------------------------------------------------------------------
 # K-quant quantizers
 
+# (sub-block length, largest code, largest scale or min) that the packed
+# fields hold, taken from the formats and not from the oracle: K2 has 2-bit
+# codes and 4-bit scales and mins per 16 weights, K4 4-bit codes and 6-bit
+# scales and mins per 32 weights.
+KQ_FIELDS = {"k2": (16, 3, 15), "k4": (32, 15, 63)}
+
 
 @pytest.mark.parametrize("fmt", ["k2", "k4"])
 def test_kquant_codes_are_nearest_grid_points(fmt):
-    B, Q, S = O.kq_params(fmt)
+    B, Q, S = KQ_FIELDS[fmt]
     rng = np.random.default_rng(6)
     w = (rng.standard_normal((3, 512)) * 0.02).astype(np.float32)
     f = O.kq_quantize(w, fmt)
@@ -269,8 +275,34 @@ def test_kquant_codes_are_nearest_grid_points(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["k2", "k4"])
+def test_kquant_scales_and_mins_are_nearest_codes(fmt):
+    """Per sub-block, sc is the code in 0..S nearest to range/(Q d) and m the
+    one nearest to -min(0, min w)/dmin (ties to the larger code), found by
+    brute force; the sub-block with the largest range (offset) reaches S."""
+    B, Q, S = KQ_FIELDS[fmt]
+    rng = np.random.default_rng(16)
+    w = (rng.standard_normal((4, 512)) * 0.02).astype(np.float32)
+    f = O.kq_quantize(w, fmt)
+    for r in range(4):
+        for blk in range(2):
+            d, dmin = f["d"][r, blk], f["dmin"][r, blk]
+            assert d > 0 and dmin > 0
+            for sb in range(256 // B):
+                x = w[r, 256 * blk + sb * B: 256 * blk + (sb + 1) * B].astype(np.float64)
+                lo, hi = min(0.0, x.min()), x.max()
+                for code, target, unit in ((int(f["sc"][r, blk * (256 // B) + sb]), (hi - lo) / Q, d),
+                                           (int(f["m"][r, blk * (256 // B) + sb]), -lo, dmin)):
+                    dist = [abs(target - unit * c) for c in range(S + 1)]
+                    best = min(range(S + 1), key=lambda c: (dist[c], -c))
+                    assert code == best or dist[code] - dist[best] <= 1e-15, (r, blk, sb, code, best)
+            n = 256 // B
+            assert f["sc"][r, blk * n:(blk + 1) * n].max() == S
+            assert f["m"][r, blk * n:(blk + 1) * n].max() == S
+
+
+@pytest.mark.parametrize("fmt", ["k2", "k4"])
 def test_kquant_error_bound(fmt):
-    B, Q, S = O.kq_params(fmt)
+    B, Q, S = KQ_FIELDS[fmt]
     rng = np.random.default_rng(7)
     w = (rng.standard_normal((8, 512)) * 0.02).astype(np.float32)
     f = O.kq_quantize(w, fmt)
@@ -285,7 +317,7 @@ def test_kquant_error_bound(fmt):
 
 @pytest.mark.parametrize("fmt", ["k2", "k4"])
 def test_kquant_exact_superblock_roundtrip(fmt):
-    B, Q, S = O.kq_params(fmt)
+    B, Q, S = KQ_FIELDS[fmt]
     rng = np.random.default_rng(8)
     d = 2.0 ** -8
     dmin = 2.0 ** -9
@@ -308,7 +340,7 @@ def test_kquant_exact_superblock_roundtrip(fmt):
 
 @pytest.mark.parametrize("fmt", ["k2", "k4"])
 def test_kquant_edge_subblocks(fmt):
-    B, Q, S = O.kq_params(fmt)
+    B, Q, S = KQ_FIELDS[fmt]
     w = np.zeros((1, 256), dtype=np.float32)
     w[0, 0:B] = 0.05                  # constant positive: lo = 0, one grid point
     w[0, B:2 * B] = -0.05             # constant negative
@@ -329,7 +361,7 @@ def test_kquant_edge_subblocks(fmt):
 
 @pytest.mark.parametrize("fmt", ["k2", "k4"])
 def test_kquant_dequant_exact_against_rationals(fmt):
-    B, Q, S = O.kq_params(fmt)
+    B, Q, S = KQ_FIELDS[fmt]
     rng = np.random.default_rng(9)
     w = (rng.standard_normal((2, 256)) * rng.choice([1e-3, 0.02, 3.0])).astype(np.float32)
     f = O.kq_quantize(w, fmt)
