@@ -113,16 +113,22 @@ def test_dequant_bit_exact(q, fmt, rows, k):
 # ---------------------------------------------------------------------------
 # Routing and grouping
 
+# the largest expert count and choice count the library takes (E = 1024,
+# k = 16); H = 4096 gives the single-token up/gate 16 waves, enough lanes to
+# rank 1024 experts itself
+MAX_E = register(synth.Workload("max_e_test", 4096, 128, 1024, 16, 128, "cb2", "cb2", "k2", seed=17, tokens=1))
+
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 3), ("decode_b16_hot", 16), ("decode_b1", 16),
                                     ("decode_b1", 2), ("draft_verify_t3", 3), ("k4_h7168_decode", 3),
-                                    ("prefill_2048", 512), ("odd_cb2_test", 40), ("odd_k4_test", 100)])
+                                    ("prefill_2048", 512), ("odd_cb2_test", 40), ("odd_k4_test", 100),
+                                    ("max_e_test", 1), ("max_e_test", 40)])
 def test_route_matches_oracle(q, name, T):
     """Up to 16 tokens: the per-expert GEMV and one ranking workgroup per
     token; more: the matrix-core logits in column parts and one wave per
     token (E = 32 and 24 leave lanes without an expert)."""
     print(f"route {name} T={T}", flush=True)
-    wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else {w.name: w for w in (ODD_CB2, ODD_K4)}[name]
+    wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else {w.name: w for w in (ODD_CB2, ODD_K4, MAX_E)}[name]
     layer = device_layer(wl, experts=[])
     xb, x64 = x_bits(wl, T)
     idx, w = _route(q, layer, xb, wl.top_k)
@@ -409,9 +415,9 @@ def test_decode_invalid_and_repeated_ids(q, wl, T):
                                   (synth.WORKLOADS["decode_b1_noshared"], 2),
                                   (synth.WORKLOADS["decode_b16_hot"], 16), (synth.WORKLOADS["k4_h7168_decode"], 1),
                                   (synth.WORKLOADS["tiny"], 1), (synth.WORKLOADS["tiny"], 4), (ODD_CB2, 3),
-                                  (ODD_K4, 2)],
+                                  (ODD_K4, 2), (MAX_E, 1), (MAX_E, 3)],
                          ids=["decode_b1", "draft_t3", "noshared_T2", "b16_hot", "k4_T1", "tiny_T1", "tiny_T4",
-                              "odd_cb2_T3", "odd_k4_T2"])
+                              "odd_cb2_T3", "odd_k4_T2", "max_e_T1", "max_e_T3"])
 def test_layer_decode_matches_route_then_ffn(q, wl, T):
     """The one-call decode step gives bit for bit the top-k and outputs of
     moe_route followed by moe_expert_ffn_decode (up to 3 tokens of a CB2
