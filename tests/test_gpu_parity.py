@@ -339,9 +339,13 @@ ODD_K4 = register(synth.Workload("odd_k4_test", 768, 96, 24, 3, 48, "k4", "k4", 
 # would not fit one workgroup's LDS, and the single-token down loads them
 # beside each weight tile instead
 WIDE_K2 = register(synth.Workload("wide_k2_test", 512, 6144, 16, 16, 0, "cb2", "cb2", "k2", seed=15, tokens=1))
+# the largest hidden size (H = 8192, 32 K-chunks): the single-token CB2
+# up/gate for H > 4096 (two chunks per wave) and the generic multi-token
+# kernels; also a prefill case
+MAX_H = register(synth.Workload("max_h_test", 8192, 128, 16, 4, 128, "cb2", "cb2", "k2", seed=18, tokens=20))
 
 
-@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], ODD_CB2, ODD_K4, WIDE_K2], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], ODD_CB2, ODD_K4, WIDE_K2, MAX_H], ids=lambda w: w.name)
 def test_decode_single_token_odd_shapes(q, wl):
     """The single-token kernels on padded I / I_s, k = 2, 3, 5, 16, with and
     without a shared expert, against the oracle and against the multi-token
@@ -514,10 +518,10 @@ MEDIUM_K4 = register(synth.Workload("medium_k4_test", 768, 160, 12, 3, 96, "k4",
                                     tokens=257))
 
 
-@pytest.mark.parametrize("name", ["tiny", "medium_test", "medium_k4_test"])
+@pytest.mark.parametrize("name", ["tiny", "medium_test", "medium_k4_test", "max_h_test"])
 def test_prefill_full_layer(q, name):
     print(f"prefill {name}", flush=True)
-    wl = synth.WORKLOADS.get(name) or {"medium_test": MEDIUM, "medium_k4_test": MEDIUM_K4}[name]
+    wl = synth.WORKLOADS.get(name) or {"medium_test": MEDIUM, "medium_k4_test": MEDIUM_K4, "max_h_test": MAX_H}[name]
     layer = device_layer(wl)
     xb, x64 = x_bits(wl, wl.tokens)
     idx, w = _route(q, layer, xb, wl.top_k)
