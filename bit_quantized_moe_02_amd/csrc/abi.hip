@@ -282,7 +282,7 @@ int run_decode(const char* who, const moe_weights* w, const Geometry& g, const v
         at.topk_idx_out = topk_idx + (size_t)t * k;
         at.topk_w_out = topk_w + (size_t)t * k;
       }
-      hipError_t e = launch_dec1(at, g.fmt_ug, g.fmt_dn, cpw, topk_w + (size_t)t * k, y + (size_t)t * g.H, cus, s);
+      hipError_t e = launch_dec1(at, g.fmt_ug, g.fmt_dn, topk_w + (size_t)t * k, y + (size_t)t * g.H, cus, s);
       if (e != hipSuccess) return hip_fail(who, e);
     }
     return MOE_OK;

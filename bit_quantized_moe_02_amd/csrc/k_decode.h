@@ -51,7 +51,7 @@ size_t dec1_down_lds(const DecArgs& a, int fmt_dn, int nw);
 // token's experts itself).
 size_t dec1_cb2_upgate_lds(int nw, bool route);
 // cus = compute units of the device (the grids are sized from it).
-hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const float* topk_w, float* y,
+hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,
                        int cus, hipStream_t s);
 hipError_t launch_combine(const DecArgs& a, const int32_t* topk_idx, const float* topk_w, float* y,
                           hipStream_t s);

@@ -75,57 +75,36 @@ __device__ int64_t item_start1(int64_t g, int64_t G, int64_t n_s, int64_t w_s, i
 }
 
 // ---------------------------------------------------------------------------
-// Per-wave payload of one routed row tile (both matrices) for CPW K-chunks.
+// CB2 up/gate at one token for H > 4096 (17 to 32 K-chunks): kCpw = 2
+// K-chunks per wave.  Per-wave payload of one routed row tile (both
+// matrices): codes and scales of its chunks.
 
-template <int FMT, int CPW>
-struct UgPay;
+constexpr int kCpw = 2;
 
-template <int CPW>
-struct UgPay<MOE_FMT_CB2, CPW> {
-  u32x4 code[2][CPW], scale[2][CPW];
+struct UgPay {
+  u32x4 code[2][kCpw], scale[2][kCpw];
 };
 
-template <int CPW>
-struct UgPay<MOE_FMT_K4, CPW> {
-  u32x4 q0[2][CPW], q1[2][CPW];
-  uint32_t s0[2][CPW], s1[2][CPW], s2[2][CPW], dd[2][CPW];
-};
-
-template <int FMT, int CPW>
-__device__ __forceinline__ void ug_load(UgPay<FMT, CPW>& p, const DecArgs& a, int e, int64_t rt, int wave,
-                                        int lane, int n_chunks) {
+__device__ __forceinline__ void ug_load(UgPay& p, const DecArgs& a, int e, int64_t rt, int wave, int lane,
+                                        int n_chunks) {
   const int n = lane & 15;
   for (int mat = 0; mat < 2; ++mat)
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int chunk = min(wave * CPW + cc, n_chunks - 1);
-      const uint8_t* tile = (mat ? a.gate : a.up) + (size_t)e * a.expert_bytes +
-                            ((size_t)rt * n_chunks + chunk) * (FMT == MOE_FMT_CB2 ? kCb2Tile : kK4Tile);
-      if constexpr (FMT == MOE_FMT_CB2) {
-        p.code[mat][cc] = load16(tile + 16 * lane);
-        p.scale[mat][cc] = load16(tile + 1024 + 16 * n);
-      } else {
-        p.q0[mat][cc] = load16(tile + 16 * lane);
-        p.q1[mat][cc] = load16(tile + 1024 + 16 * lane);
-        const uint32_t* sp = reinterpret_cast<const uint32_t*>(tile + 2048 + 12 * n);
-        p.s0[mat][cc] = sp[0];
-        p.s1[mat][cc] = sp[1];
-        p.s2[mat][cc] = sp[2];
-        p.dd[mat][cc] = *reinterpret_cast<const uint32_t*>(tile + 2240 + 4 * n);
-      }
+    for (int cc = 0; cc < kCpw; ++cc) {
+      const int chunk = min(wave * kCpw + cc, n_chunks - 1);
+      const uint8_t* tile =
+          (mat ? a.gate : a.up) + (size_t)e * a.expert_bytes + ((size_t)rt * n_chunks + chunk) * kCb2Tile;
+      p.code[mat][cc] = load16(tile + 16 * lane);
+      p.scale[mat][cc] = load16(tile + 1024 + 16 * n);
     }
 }
 
-template <int FMT, int CPW>
-__global__ __launch_bounds__(1024) void dec1_upgate_kernel(DecArgs a) {
+__global__ __launch_bounds__(1024) void dec1_cb2_wide_upgate_kernel(DecArgs a) {
+  constexpr int CPW = kCpw;
   extern __shared__ __align__(16) uint8_t smem[];
   int64_t* range = reinterpret_cast<int64_t*>(smem);
-  size_t off = 256;
-  uint8_t* val_tab = smem + off;
+  uint8_t* val_tab = smem + 256;
   uint8_t* flip_tab = val_tab + kCb2TableBytes;
-  if (FMT == MOE_FMT_CB2) off += 2 * kCb2TableBytes;
-  float* xsum = reinterpret_cast<float*>(smem + off);               // K4: per 32-column block
-  if (FMT == MOE_FMT_K4) off += (size_t)(a.H / 32) * 4;
-  float* red = reinterpret_cast<float*>(smem + off);                // [kBatch][NW][2][16]
+  float* red = reinterpret_cast<float*>(smem + 256 + 2 * kCb2TableBytes);   // [kBatch][NW][2][16]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
   const int k = a.k, n_chunks = a.H / 256;
@@ -135,13 +114,7 @@ __global__ __launch_bounds__(1024) void dec1_upgate_kernel(DecArgs a) {
     range[0] = item_start1(blockIdx.x, gridDim.x, n_rts, w_s, (int64_t)k * n_rt, w_r);
     range[1] = item_start1(blockIdx.x + 1, gridDim.x, n_rts, w_s, (int64_t)k * n_rt, w_r);
   }
-  if (FMT == MOE_FMT_CB2) cb2_fill_tables(a.codebook, val_tab, flip_tab, tid, blockDim.x);
-  if (FMT == MOE_FMT_K4)
-    for (int b = tid; b < a.H / 32; b += blockDim.x) {
-      float s = 0.f;
-      for (int j = 0; j < 32; ++j) s += (float)(_Float16)bf2f(a.x[b * 32 + j]);
-      xsum[b] = s;
-    }
+  cb2_fill_tables(a.codebook, val_tab, flip_tab, tid, blockDim.x);
   __syncthreads();
   const int64_t lo = range[0], hi = range[1];
   if (lo >= hi) return;
@@ -238,45 +211,22 @@ __global__ __launch_bounds__(1024) void dec1_upgate_kernel(DecArgs a) {
     const int j = (int)((it - n_rts) / n_rt);
     return (int)a.topk_idx[j];
   };
-  // With one K-chunk per wave the next row tile's loads are issued before
-  // this one is computed; with two chunks per wave the registers are needed
-  // for the activations and the loads are issued per row tile.
-  constexpr bool kPrefetch = CPW == 1;
-  UgPay<FMT, CPW> cur, nxt;
-  if (kPrefetch) {
-    const int e = expert_of(item);
-    if (wave_has_chunks && e >= 0 && e < a.E) ug_load<FMT, CPW>(cur, a, e, (item - n_rts) % n_rt, wave, lane, n_chunks);
-  }
+  // (two chunks per wave: the registers hold the activations, so a row
+  // tile's loads are issued when it is computed, not one tile ahead)
+  UgPay cur;
   for (; item < hi; ++item) {
-    if (kPrefetch && item + 1 < hi) {
-      const int e1 = expert_of(item + 1);
-      if (wave_has_chunks && e1 >= 0 && e1 < a.E)
-        ug_load<FMT, CPW>(nxt, a, e1, (item + 1 - n_rts) % n_rt, wave, lane, n_chunks);
-    }
     const int e = expert_of(item);
-    if (!kPrefetch && wave_has_chunks && e >= 0 && e < a.E)
-      ug_load<FMT, CPW>(cur, a, e, (item - n_rts) % n_rt, wave, lane, n_chunks);
+    if (wave_has_chunks && e >= 0 && e < a.E) ug_load(cur, a, e, (item - n_rts) % n_rt, wave, lane, n_chunks);
     float v[2] = {0.f, 0.f};
     if (wave_has_chunks && e >= 0 && e < a.E) {
       for (int mat = 0; mat < 2; ++mat)
         for (int cc = 0; cc < CPW; ++cc) {
           const int chunk = wave * CPW + cc;
           if (chunk >= n_chunks) break;
-          if constexpr (FMT == MOE_FMT_CB2) {
-            for (int kb = 0; kb < 8; ++kb) {
-              const uint32_t code = (cur.code[mat][cc][kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu;
-              const float4v c = mfma_f16(A[cc][kb], cb2_group(code, val_lane, flip_lane), zero);
-              v[mat] += h2f((cur.scale[mat][cc][kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu) * c[0];
-            }
-          } else {
-            const float d = h2f(cur.dd[mat][cc] & 0xFFFFu), dmin = h2f(cur.dd[mat][cc] >> 16);
-            for (int kb = 0; kb < 8; ++kb) {
-              const uint32_t w = kb < 4 ? cur.q0[mat][cc][kb & 3] : cur.q1[mat][cc][kb & 3];
-              const float4v c = mfma_f16(A[cc][kb], as_half8(k4_magic(w)), zero);
-              const float dsc = d * (float)k4_scale_value(cur.s0[mat][cc], cur.s1[mat][cc], cur.s2[mat][cc], kb);
-              const float mn = (float)k4_scale_value(cur.s0[mat][cc], cur.s1[mat][cc], cur.s2[mat][cc], 8 + kb);
-              v[mat] += dsc * c[0] - (1024.0f * dsc + dmin * mn) * xsum[chunk * 8 + kb];
-            }
+          for (int kb = 0; kb < 8; ++kb) {
+            const uint32_t code = (cur.code[mat][cc][kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu;
+            const float4v c = mfma_f16(A[cc][kb], cb2_group(code, val_lane, flip_lane), zero);
+            v[mat] += h2f((cur.scale[mat][cc][kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu) * c[0];
           }
         }
     }
@@ -289,7 +239,6 @@ __global__ __launch_bounds__(1024) void dec1_upgate_kernel(DecArgs a) {
       first = item + 1;
       nb = 0;
     }
-    if (kPrefetch) cur = nxt;
   }
 }
 
@@ -1167,12 +1116,7 @@ __global__ __launch_bounds__(1024) void dec1_down_k2d_kernel(DecArgs a, const fl
 
 namespace qmoe {
 
-size_t dec1_upgate_lds(const DecArgs& a, int fmt, int nw) {
-  size_t off = 256;
-  if (fmt == MOE_FMT_CB2) off += 2 * kCb2TableBytes;
-  if (fmt == MOE_FMT_K4) off += (size_t)(a.H / 32) * 4;
-  return off + (size_t)kBatch * nw * 2 * 16 * 4;
-}
+size_t dec1_cb2_wide_upgate_lds(int nw) { return 256 + 2 * kCb2TableBytes + (size_t)kBatch * nw * 2 * 16 * 4; }
 
 size_t dec1_down_lds(const DecArgs& a, int fmt_dn, int nw) {
   if (fmt_dn == MOE_FMT_K2) return (size_t)nw * 16 * 4;  // direct loads: the reduction only
@@ -1187,7 +1131,7 @@ size_t dec1_cb2_upgate_lds(int nw, bool route) {
          (route ? 16 * 4 + sizeof(qmoe_route::TopkLds) : 0);
 }
 
-hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const float* topk_w, float* y,
+hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,
                        int cus, hipStream_t s) {
   hipError_t err;
   const int n_chunks = a.H / 256;
@@ -1216,17 +1160,17 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, int cpw, const 
       hipLaunchKernelGGL(fk, dim3(grid), dim3(64 * nw), lds, s, a);
     });
   } else {
-    const int nw_ug = (n_chunks + cpw - 1) / cpw;
+    // CB2 with 17 to 32 K-chunks (K4 layers take dec1_k4_upgate_kernel at every H)
+    if (fmt_ug != MOE_FMT_CB2 || n_chunks > 16 * kCpw) return hipErrorInvalidValue;
+    const int nw_ug = (n_chunks + kCpw - 1) / kCpw;
     const int64_t items = (int64_t)a.k * (a.I / 16) + a.Is / 16;
     const int grid_ug = (int)(items < cus ? items : cus);
-    void (*fu)(DecArgs) = nullptr;
-    if (fmt_ug == MOE_FMT_CB2) fu = cpw == 1 ? dec1_upgate_kernel<MOE_FMT_CB2, 1> : dec1_upgate_kernel<MOE_FMT_CB2, 2>;
-    else fu = cpw == 1 ? dec1_upgate_kernel<MOE_FMT_K4, 1> : dec1_upgate_kernel<MOE_FMT_K4, 2>;
-    err = ensure_dyn_lds((const void*)fu);
+    err = ensure_dyn_lds((const void*)dec1_cb2_wide_upgate_kernel);
     if (err != hipSuccess) return err;
-    const size_t lds_ug = dec1_upgate_lds(a, fmt_ug, nw_ug);
-    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s,
-                       [&] { hipLaunchKernelGGL(fu, dim3(grid_ug), dim3(64 * nw_ug), lds_ug, s, a); });
+    const size_t lds_ug = dec1_cb2_wide_upgate_lds(nw_ug);
+    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
+      hipLaunchKernelGGL(dec1_cb2_wide_upgate_kernel, dim3(grid_ug), dim3(64 * nw_ug), lds_ug, s, a);
+    });
   }
   if (err != hipSuccess) return err;
   // one workgroup per 16-row tile of y: 16 waves while the tiles fit the
