@@ -343,9 +343,13 @@ WIDE_K2 = register(synth.Workload("wide_k2_test", 512, 6144, 16, 16, 0, "cb2", "
 # up/gate for H > 4096 (two chunks per wave) and the generic multi-token
 # kernels; also a prefill case
 MAX_H = register(synth.Workload("max_h_test", 8192, 128, 16, 4, 128, "cb2", "cb2", "k2", seed=18, tokens=20))
+# K4 at H = 8192: the single-token K4 up/gate in K-parts and the generic
+# multi-token K4 kernels with two chunks per wave
+MAX_H_K4 = register(synth.Workload("max_h_k4_test", 8192, 96, 8, 2, 64, "k4", "k4", "k4", seed=19, tokens=1))
 
 
-@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], ODD_CB2, ODD_K4, WIDE_K2, MAX_H], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [synth.WORKLOADS["tiny"], ODD_CB2, ODD_K4, WIDE_K2, MAX_H, MAX_H_K4],
+                         ids=lambda w: w.name)
 def test_decode_single_token_odd_shapes(q, wl):
     """The single-token kernels on padded I / I_s, k = 2, 3, 5, 16, with and
     without a shared expert, against the oracle and against the multi-token
