@@ -104,12 +104,29 @@ def _check(rc):
         raise QmoeError(rc, lib.moe_last_error().decode())
 
 
-def _ptr(t):
+def _dev(t, name, dtype, n=0, optional=False):
+    """Device address of tensor `t` as a kernel argument, after the checks
+    that keep a kernel from touching the wrong memory: a CUDA tensor of
+    `dtype`, contiguous, with at least `n` elements.  None passes only where
+    the call takes NULL (`optional`)."""
     if t is None:
-        return None
-    if isinstance(t, np.ndarray):
-        return t.ctypes.data
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call needs {n}")
     return t.data_ptr()
+
+
+def _ws(ws):
+    """(address, bytes) of a uint8 device workspace; the library checks the size."""
+    return _dev(ws, "ws", torch.uint8), ws.numel()
 
 
 def _stream(stream):
@@ -156,8 +173,10 @@ def moe_route_workspace_bytes(T: int, E: int) -> int:
 
 
 def moe_route(x_bf16, w_router, logit_bias, T, H, E, k, topk_idx, topk_w, ws, stream=None):
-    _check(lib.moe_route(_ptr(x_bf16), _ptr(w_router), _ptr(logit_bias), T, H, E, k, _ptr(topk_idx),
-                         _ptr(topk_w), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    _check(lib.moe_route(_dev(x_bf16, "x_bf16", torch.bfloat16, T * H), _dev(w_router, "w_router", torch.float32, E * H),
+                         _dev(logit_bias, "logit_bias", torch.float32, E, optional=True), T, H, E, k,
+                         _dev(topk_idx, "topk_idx", torch.int32, T * k), _dev(topk_w, "topk_w", torch.float32, T * k),
+                         *_ws(ws), _stream(stream)))
 
 
 def moe_group_workspace_bytes(T: int, k: int, E: int) -> int:
@@ -165,9 +184,10 @@ def moe_group_workspace_bytes(T: int, k: int, E: int) -> int:
 
 
 def moe_group_tokens(topk_idx, T, k, E, expert_offsets, sorted_slots, slot_pos, ws, stream=None):
-    _check(lib.moe_group_tokens(_ptr(topk_idx), T, k, E, _ptr(expert_offsets), _ptr(sorted_slots),
-                                _ptr(slot_pos), _ptr(ws), ws.numel() * ws.element_size(),
-                                _stream(stream)))
+    _check(lib.moe_group_tokens(_dev(topk_idx, "topk_idx", torch.int32, T * k), T, k, E,
+                                _dev(expert_offsets, "expert_offsets", torch.int32, E + 1),
+                                _dev(sorted_slots, "sorted_slots", torch.int32, T * k),
+                                _dev(slot_pos, "slot_pos", torch.int32, T * k), *_ws(ws), _stream(stream)))
 
 
 def moe_ffn_workspace_bytes(w: MoeWeights, T: int, k: int, prefill: bool) -> int:
@@ -175,8 +195,11 @@ def moe_ffn_workspace_bytes(w: MoeWeights, T: int, k: int, prefill: bool) -> int
 
 
 def moe_expert_ffn_decode(w: MoeWeights, x_bf16, T, k, topk_idx, topk_w, y, ws, stream=None):
-    _check(lib.moe_expert_ffn_decode(ctypes.byref(w), _ptr(x_bf16), T, k, _ptr(topk_idx), _ptr(topk_w),
-                                     _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    H = w.hidden
+    _check(lib.moe_expert_ffn_decode(ctypes.byref(w), _dev(x_bf16, "x_bf16", torch.bfloat16, T * H), T, k,
+                                     _dev(topk_idx, "topk_idx", torch.int32, T * k),
+                                     _dev(topk_w, "topk_w", torch.float32, T * k),
+                                     _dev(y, "y", torch.float32, T * H), *_ws(ws), _stream(stream)))
 
 
 def moe_layer_decode_workspace_bytes(w: MoeWeights, T: int, k: int) -> int:
@@ -184,21 +207,33 @@ def moe_layer_decode_workspace_bytes(w: MoeWeights, T: int, k: int) -> int:
 
 
 def moe_layer_decode(w: MoeWeights, w_router, logit_bias, x_bf16, T, k, topk_idx, topk_w, y, ws, stream=None):
-    _check(lib.moe_layer_decode(ctypes.byref(w), _ptr(w_router), _ptr(logit_bias), _ptr(x_bf16), T, k,
-                                _ptr(topk_idx), _ptr(topk_w), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
-                                _stream(stream)))
+    E, H = w.n_experts, w.hidden
+    _check(lib.moe_layer_decode(ctypes.byref(w), _dev(w_router, "w_router", torch.float32, E * H),
+                                _dev(logit_bias, "logit_bias", torch.float32, E, optional=True),
+                                _dev(x_bf16, "x_bf16", torch.bfloat16, T * H), T, k,
+                                _dev(topk_idx, "topk_idx", torch.int32, T * k),
+                                _dev(topk_w, "topk_w", torch.float32, T * k),
+                                _dev(y, "y", torch.float32, T * H), *_ws(ws), _stream(stream)))
 
 
 def moe_expert_ffn_prefill(w: MoeWeights, x_bf16, T, k, topk_idx, topk_w, expert_offsets, sorted_slots,
                            slot_pos, y, ws, stream=None):
-    _check(lib.moe_expert_ffn_prefill(ctypes.byref(w), _ptr(x_bf16), T, k, _ptr(topk_idx), _ptr(topk_w),
-                                      _ptr(expert_offsets), _ptr(sorted_slots), _ptr(slot_pos), _ptr(y),
-                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    E, H = w.n_experts, w.hidden
+    _check(lib.moe_expert_ffn_prefill(ctypes.byref(w), _dev(x_bf16, "x_bf16", torch.bfloat16, T * H), T, k,
+                                      _dev(topk_idx, "topk_idx", torch.int32, T * k),
+                                      _dev(topk_w, "topk_w", torch.float32, T * k),
+                                      _dev(expert_offsets, "expert_offsets", torch.int32, E + 1),
+                                      _dev(sorted_slots, "sorted_slots", torch.int32, T * k),
+                                      _dev(slot_pos, "slot_pos", torch.int32, T * k),
+                                      _dev(y, "y", torch.float32, T * H), *_ws(ws), _stream(stream)))
 
 
 def moe_debug_dequant(fmt, packed, rows, k, codebook, out, stream=None):
-    _check(lib.moe_debug_dequant(FMT.get(fmt, fmt), _ptr(packed), rows, k, _ptr(codebook), _ptr(out),
-                                 _stream(stream)))
+    f = FMT.get(fmt, fmt)
+    kp = -(-k // 256) * 256
+    _check(lib.moe_debug_dequant(f, _dev(packed, "packed", torch.uint8, moe_packed_bytes(f, rows, k)), rows, k,
+                                 _dev(codebook, "codebook", torch.int8, 256 * 8, optional=True),
+                                 _dev(out, "out", torch.float32, rows * kp), _stream(stream)))
 
 
 def moe_profile_next_launch(kernel, start_event, stop_event):
@@ -231,6 +266,19 @@ class DeviceLayer:
         self.router = router
         self.bias = bias
         self.n_experts, self.hidden, self.inter, self.shared_inter = n_experts, hidden, inter, shared_inter
-        self.w = MoeWeights(n_experts, hidden, inter, shared_inter, FMT[fmts[0]], FMT[fmts[1]], FMT[fmts[2]],
-                            0, _ptr(up), _ptr(gate), _ptr(down), _ptr(codebook), _ptr(shared_up),
-                            _ptr(shared_gate), _ptr(shared_down))
+        E, H, I, Is = n_experts, hidden, inter, shared_inter
+        nb_up, nb_dn = moe_packed_bytes(fmts[0], I, H), moe_packed_bytes(fmts[2], H, I)
+        u8 = torch.uint8
+        shared = Is > 0
+        self.w = MoeWeights(E, H, I, Is, FMT[fmts[0]], FMT[fmts[1]], FMT[fmts[2]], 0,
+                            _dev(up, "up", u8, E * nb_up), _dev(gate, "gate", u8, E * nb_up),
+                            _dev(down, "down", u8, E * nb_dn),
+                            _dev(codebook, "codebook", torch.int8, 256 * 8, optional=True),
+                            _dev(shared_up, "shared_up", u8, moe_packed_bytes("bf16", Is, H) if shared else 0,
+                                 optional=not shared),
+                            _dev(shared_gate, "shared_gate", u8, moe_packed_bytes("bf16", Is, H) if shared else 0,
+                                 optional=not shared),
+                            _dev(shared_down, "shared_down", u8, moe_packed_bytes("bf16", H, Is) if shared else 0,
+                                 optional=not shared))
+        _dev(router, "router", torch.float32, E * H, optional=True)
+        _dev(bias, "bias", torch.float32, E, optional=True)

@@ -208,6 +208,23 @@ def test_profile_hook_arguments(q):
     assert q.lib.moe_profile_next_launch(-1, None, None) == 0
 
 
+def test_binding_refuses_host_tensors(q):
+    """The device-call wrappers check every tensor before the library sees
+    its address: a host tensor would hand a kernel a CPU address."""
+    import torch
+    T, H, E, k = 1, 256, 8, 2
+    x = torch.zeros((T, H), dtype=torch.bfloat16)
+    wr = torch.zeros((E, H), dtype=torch.float32)
+    idx = torch.zeros((T, k), dtype=torch.int32)
+    w = torch.zeros((T, k), dtype=torch.float32)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="x_bf16 must be a CUDA tensor"):
+        q.moe_route(x, wr, None, T, H, E, k, idx, w, ws)
+    with pytest.raises(ValueError, match="up must be a CUDA tensor"):
+        q.DeviceLayer(E, H, 128, 0, ("cb2", "cb2", "k2"), torch.zeros(8, dtype=torch.uint8),
+                      torch.zeros(8, dtype=torch.uint8), torch.zeros(8, dtype=torch.uint8))
+
+
 def test_binding_raises_with_message(q):
     w = np.zeros((15, 256), np.float32)
     with pytest.raises(q.QmoeError) as ei:
