@@ -24,7 +24,7 @@ Functions, in the order a layer uses them:
 
 Everything is fp64 except where a format fixes a precision (fp16 scales,
 fp32 dequantized weights).  Readings of points the pages leave open are
-listed where they are used; each reading is repeated in the design doc.
+listed where they are used.
 """
 from __future__ import annotations
 
