@@ -43,8 +43,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 MEASURED_TRAFFIC = {
     ("decode_b1", "decode_upgate"): ("abb06f880411c12b:66c6882cc36e9a40", 76.28e6 + 0.049e6),
     ("decode_b1", "decode_down"): ("abb06f880411c12b:66c6882cc36e9a40", 39.33e6 + 0.016e6),
-    ("prefill_2048", "prefill_upgate"): ("579c3de7fe5774c0:66c6882cc36e9a40", 1761.42e6 + 75.497e6),
-    ("prefill_2048", "prefill_down"): ("579c3de7fe5774c0:66c6882cc36e9a40", 1015.51e6 + 301.990e6),
+    ("prefill_2048", "prefill_upgate"): ("073ea6d28936fe05:66c6882cc36e9a40", 1761.42e6 + 75.497e6),
+    ("prefill_2048", "prefill_down"): ("073ea6d28936fe05:66c6882cc36e9a40", 1015.51e6 + 301.990e6),
 }
 TRAFFIC_SOURCES = {"decode": ["k_decode1.hip", "device_common.hpp"], "prefill": ["k_prefill.hip", "device_common.hpp"]}
 

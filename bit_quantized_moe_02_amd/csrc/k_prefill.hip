@@ -8,11 +8,14 @@
 // Each wave owns 32 weight rows (two 16-row tiles) per matrix and multiplies
 // them with v_mfma_f32_32x32x16 against up to three 32-token M-tiles: every
 // weight is dequantized once per workgroup pass into an fp16 B operand (the
-// quantization scales folded in, one fp16 rounding per weight) and used by
-// 32 tokens per instruction.  M-tiles past the expert's last token are
-// skipped.  Token rows are gathered into LDS one 256-column K-chunk at a
-// time (bf16 -> fp16 for the quantized experts); the next chunk's rows and
-// weights are loaded into registers while the current chunk is multiplied.
+// quantization scales folded in: one fp16 rounding per CB2 or K4 weight; a K2
+// down weight is one fp16 fma of its exact code with fp16 per-sub-block
+// factors) and used by 32 tokens per instruction.  M-tiles past the expert's
+// last token are skipped.  Token rows go into LDS one 256-column K-chunk at a
+// time by LDS DMA (the quantized experts read the fp16 copy of x that
+// pf_x16_kernel makes); the next chunk's rows stream into the other LDS
+// buffer and its weights into registers while the current chunk is
+// multiplied.
 // fp16 operands with fp32 accumulation keep the layer within the 2e-3
 // tolerance, which bf16 operands do not; the shared expert's up/gate uses
 // bf16 operands directly because both x and its weights are exact in bf16.
