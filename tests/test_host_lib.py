@@ -72,6 +72,18 @@ def test_pack_bytes_equal_oracle(q, fmt, rows, k, std):
     assert np.array_equal(lib, ora), f"{np.sum(lib != ora)} bytes differ"
 
 
+@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4", "bf16"])
+def test_pack_bytes_independent_of_threads(q, fmt):
+    """The host packer splits rows over threads: any thread count (0 = all
+    cores) gives the same bytes."""
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((80, 768)) * 0.02).astype(np.float32)
+    cb = q.moe_codebook_generate(0) if fmt == "cb2" else None
+    ref = q.moe_quantize_pack(fmt, w, cb, n_threads=1)
+    for n in (0, 2, 3, 5, 64):
+        assert np.array_equal(q.moe_quantize_pack(fmt, w, cb, n_threads=n), ref), n
+
+
 @pytest.mark.parametrize("fmt", ["cb2", "k2", "k4"])
 def test_pack_edge_blocks_equal_oracle(q, fmt):
     rng = np.random.default_rng(3)
