@@ -333,6 +333,38 @@ extern "C" int moe_codebook_generate(uint64_t seed, int8_t* table_out) {
   return MOE_OK;
 }
 
+// True when some fp16 scale of the packed matrix would not be finite: CB2's
+// s = fp16(max|w| / 0.75) over a 32-weight group, or a K-quant super-block's
+// d = fp16(max_s a_s / S) or dmin = fp16(max_s b_s / S).  fp16 rounding is
+// monotone, so the largest group or sub-block decides; columns past k are the
+// zeros the packers pad with.  Checked before any output byte is written.
+static bool scale_overflows(int fmt, const float* w, int64_t rows, int64_t k) {
+  if (fmt == MOE_FMT_CB2) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < rows * k; ++i) amax = std::max(amax, fabs((double)w[i]));
+    return (f16_nonneg_zero(amax / 0.75) & 0x7C00) == 0x7C00;
+  }
+  if (fmt != MOE_FMT_K2 && fmt != MOE_FMT_K4) return false;
+  const KqParams p = fmt == MOE_FMT_K2 ? KqParams{16, 3, 15} : KqParams{32, 15, 63};
+  double amax = 0.0, bmax = 0.0;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < k; c += p.sub_len) {
+      const float* x = w + r * k + c;
+      const int64_t n = std::min<int64_t>(p.sub_len, k - c);
+      double lo = (double)x[0], hi = (double)x[0];
+      for (int64_t i = 1; i < n; ++i) {
+        lo = std::min(lo, (double)x[i]);
+        hi = std::max(hi, (double)x[i]);
+      }
+      if (n < p.sub_len) hi = std::max(hi, 0.0);       // padded zeros
+      lo = std::min(0.0, lo);
+      amax = std::max(amax, (hi - lo) / (double)p.qmax);
+      bmax = std::max(bmax, 0.0 - lo);
+    }
+  return (f16_nonneg_zero(amax / (double)p.smax) & 0x7C00) == 0x7C00 ||
+         (f16_nonneg_zero(bmax / (double)p.smax) & 0x7C00) == 0x7C00;
+}
+
 extern "C" size_t moe_packed_bytes(int fmt, int64_t rows, int64_t k) {
   const int tb = tile_bytes(fmt);
   if (tb == 0 || rows <= 0 || rows % 16 != 0 || k < 1) return 0;
@@ -359,6 +391,8 @@ extern "C" int moe_quantize_pack(int fmt, const float* w, int64_t rows, int64_t 
         return fail(MOE_ERR_INVALID_ARG, "moe_quantize_pack: codebook values must be in {-3,-1,1,3}");
   for (int64_t i = 0; i < rows * k; ++i)
     if (!std::isfinite(w[i])) return fail(MOE_ERR_INVALID_ARG, "moe_quantize_pack: non-finite weight");
+  if (scale_overflows(fmt, w, rows, k))
+    return fail(MOE_ERR_INVALID_ARG, "moe_quantize_pack: |w| too large for an fp16 scale");
 
   const int64_t kp = pad256(k);
   const int64_t n_rt = rows / 16, n_kc = kp / 256;
@@ -395,7 +429,7 @@ extern "C" int moe_quantize_pack(int fmt, const float* w, int64_t rows, int64_t 
     for (int t = 0; t < nt; ++t) th.emplace_back(worker, t);
     for (auto& t : th) t.join();
   }
-  for (int t = 0; t < nt; ++t)
+  for (int t = 0; t < nt; ++t)      // (scale_overflows has ruled this out)
     if (!ok[t]) return fail(MOE_ERR_INVALID_ARG, "moe_quantize_pack: |w| too large for an fp16 scale");
   return MOE_OK;
 }

@@ -141,6 +141,23 @@ def test_quantize_pack_errors(q):
     big[0, 0] = 60000.0
     assert lib.moe_quantize_pack(1, big.ctypes.data, 16, 256, cb.ctypes.data, out.ctypes.data, out.nbytes, 1) == 1
     assert "fp16 scale" in q.moe_last_error()
+    for fmt, val in ((1, 60000.0), (2, 5e6), (3, 7e7), (2, -2e6), (3, -5e6)):
+        # an fp16 scale (CB2 s, K-quant d or dmin) out of range: refused
+        # before any output byte is written
+        big = w.copy()
+        big[5, 100] = val
+        out_big = np.full(q.moe_packed_bytes({1: "cb2", 2: "k2", 3: "k4"}[fmt], 16, 256), 0xA5, np.uint8)
+        assert lib.moe_quantize_pack(fmt, big.ctypes.data, 16, 256, cb.ctypes.data, out_big.ctypes.data,
+                                     out_big.nbytes, 2) == 1, (fmt, val)
+        assert "fp16 scale" in q.moe_last_error()
+        assert np.all(out_big == 0xA5), (fmt, val)
+    # the largest values whose scales still fit are accepted
+    for fmt, val in ((1, 49000.0), (2, 2.9e6), (3, 4e6)):
+        ok = w.copy()
+        ok[5, 100] = val
+        out_ok = np.zeros(q.moe_packed_bytes({1: "cb2", 2: "k2", 3: "k4"}[fmt], 16, 256), np.uint8)
+        assert lib.moe_quantize_pack(fmt, ok.ctypes.data, 16, 256, cb.ctypes.data, out_ok.ctypes.data,
+                                     out_ok.nbytes, 2) == 0, (fmt, val, q.moe_last_error())
     badcb = cb.copy()
     badcb[0, 0] = 2
     assert lib.moe_quantize_pack(1, w.ctypes.data, 16, 256, badcb.ctypes.data, out.ctypes.data, out.nbytes, 1) == 1
