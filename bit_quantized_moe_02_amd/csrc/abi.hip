@@ -87,7 +87,7 @@ int check_weights(const moe_weights* w, Geometry* g, const char* fn) {
 constexpr int kDecPerTokenMax = 3;
 
 struct DecLayout {
-  size_t h, hs, hsum, ybuf, ysh, err, total;
+  size_t h, hs, hsum, ybuf, ysh, xexp, total;
 };
 
 DecLayout dec_layout(const Geometry& g, int T, int k) {
@@ -103,14 +103,14 @@ DecLayout dec_layout(const Geometry& g, int T, int k) {
   off = align_up(off + (size_t)T * k * g.H * 4);
   L.ysh = off;
   off = align_up(off + (size_t)T * g.H * 4);
-  L.err = off;
-  off = align_up(off + 4);
+  L.xexp = off;
+  off = align_up(off + (size_t)T * 4);
   L.total = off;
   return L;
 }
 
 struct PfLayout {
-  size_t h, hs, yslot, ysh, total;
+  size_t h, hs, yslot, ysh, xexp, epos, total;
 };
 
 PfLayout pf_layout(const Geometry& g, int64_t T, int k) {
@@ -124,6 +124,10 @@ PfLayout pf_layout(const Geometry& g, int64_t T, int k) {
   off = align_up(off + (size_t)T * k * g.H * 4);
   L.ysh = off;
   off = align_up(off + (size_t)T * g.H * 4);
+  L.xexp = off;
+  off = align_up(off + (size_t)T * 4);
+  L.epos = off;
+  off = align_up(off + (size_t)T * k * 4);
   L.total = off;
   return L;
 }
@@ -252,7 +256,7 @@ int run_decode(const char* who, const moe_weights* w, const Geometry& g, const v
   a.hsum = (float*)(wsb + L.hsum);
   a.ybuf = (float*)(wsb + L.ybuf);
   a.ysh = (float*)(wsb + L.ysh);
-  a.err_count = (int*)(wsb + L.err);
+  a.xexp = (int*)(wsb + L.xexp);
   const int cus = n_cus();
   if (T <= kDecPerTokenMax && dec1_down_lds(a, g.fmt_dn, 16) <= 160 * 1024) {
     // few tokens: the single-token kernels once per token (exact weights)
@@ -274,6 +278,7 @@ int run_decode(const char* who, const moe_weights* w, const Geometry& g, const v
       at.h = a.h + (size_t)t * k * g.I;
       at.hs = a.hs + (size_t)t * g.Is;
       at.hsum = a.hsum + (size_t)t * k * (g.I_pad / 16) * 2;
+      at.xexp = a.xexp + t;
       if (route_here) {
         at.logits = route->logits;
         at.n_parts = route->n_parts;
@@ -408,6 +413,8 @@ extern "C" int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, 
   a.hs = (_Float16*)(wsb + L.hs);
   a.yslot = (float*)(wsb + L.yslot);
   a.ysh = (float*)(wsb + L.ysh);
+  a.xexp = (int*)(wsb + L.xexp);
+  a.epos = (int*)(wsb + L.epos);
   a.x16 = (const uint16_t*)(wsb + L.yslot);   // T*H fp16 fits in yslot, which only the down kernel writes
   hipError_t e = launch_prefill(a, g.fmt_ug, g.fmt_dn, topk_w, y, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("moe_expert_ffn_prefill", e);

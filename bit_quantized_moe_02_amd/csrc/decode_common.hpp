@@ -14,7 +14,7 @@ constexpr int kMaxSlots = 256;   // T * k <= 256
 
 // ---------------------------------------------------------------------------
 // Distinct experts of the T*k choices, in order of first appearance (slot
-// order).  Invalid ids (outside [0, E)) are skipped and counted.
+// order).  Invalid ids (outside [0, E)) are skipped.
 struct ExpertList {
   int n;
   int expert[kMaxSlots];
@@ -22,8 +22,7 @@ struct ExpertList {
   int slot_e[kMaxSlots];
 };
 
-__device__ inline void build_expert_list(const int32_t* topk_idx, int n_slots, int k, int E,
-                                  ExpertList* L, int* err_count) {
+__device__ inline void build_expert_list(const int32_t* topk_idx, int n_slots, int k, int E, ExpertList* L) {
   const int tid = threadIdx.x;
   for (int i = tid; i < n_slots; i += blockDim.x) {
     const int e = topk_idx[i];
@@ -58,11 +57,6 @@ __device__ inline void build_expert_list(const int32_t* topk_idx, int n_slots, i
       base += __popcll(b);
     }
     if (tid == 0) L->n = base;
-    if (err_count && tid == 0) {
-      int bad = 0;
-      for (int i = 0; i < n_slots; ++i) bad += (L->slot_e[i] < 0);
-      if (bad) atomicAdd(err_count, bad);
-    }
   }
   __syncthreads();
 }

@@ -71,6 +71,68 @@ __device__ __forceinline__ half8 bf16x8_to_half8(const u32x4& v) {
 }
 
 // ---------------------------------------------------------------------------
+// Per-token power-of-two scaling.  fp16 operands hold x and h in a range far
+// narrower than bf16's, so every token t gets an exponent
+//   e_t = floor(log2 max_i |x_ti|) - 1, clamped to [-kXExpMax, kXExpMax],
+// the routed GEMMs take fp16(x_t * 2^-e_t) (its largest value in [2, 4)),
+// and h is stored as fp16(h * 2^-2e_t): since |SiLU(g) u| <= |g| |u| and
+// g, u scale with x, the stored h does not depend on the scale of x.  Sums
+// are taken on the scaled values and the scale is removed in fp32 (exact:
+// a power of two), so outside fp16's range limits the result is the same as
+// with unscaled operands.
+constexpr int kXExpMax = 60;
+
+// Largest exponent field (bits 7..14) of the 8 bf16 values in v.
+__device__ __forceinline__ uint32_t bf16x8_max_efield(const u32x4& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, (v[i] >> 7) & 0xFFu);
+    m = max(m, (v[i] >> 23) & 0xFFu);
+  }
+  return m;
+}
+
+// e_t from the largest bf16 exponent field of the token (0 for a token of
+// zeros or subnormals, which gets the smallest exponent).
+__device__ __forceinline__ int x_exp_of_field(uint32_t efield) {
+  const int e = (int)efield - 128;
+  return e < -kXExpMax ? -kXExpMax : (e > kXExpMax ? kXExpMax : e);
+}
+
+// Largest exponent field over a wave (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// 8 bf16 (16 bytes) times 2^-e -> half8 (the multiplication is exact; the
+// fp16 conversion rounds once, only below fp16's normal range).
+__device__ __forceinline__ half8 bf16x8_to_half8_exp(const u32x4& v, int e) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_ldexpf(__builtin_bit_cast(float, v[i] << 16), -e);
+    const float hi = __builtin_ldexpf(__builtin_bit_cast(float, v[i] & 0xFFFF0000u), -e);
+    half2v h = {(_Float16)lo, (_Float16)hi};
+    r[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  return as_half8(r);
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+// h * 2^-2e as fp16, from the fp32 sums of gate and up taken over inputs
+// x * 2^-ea (ea = e for the scaled fp16 operands, 0 for raw bf16 ones):
+// g = gsum 2^ea, h 2^-2e = (SiLU(g) 2^-e) (usum 2^(ea - e)).  With e = ea = 0
+// this is fp16(SiLU(gsum) usum).
+__device__ __forceinline__ _Float16 h_of(float gsum, float usum, int ea, int e) {
+  const float g = __builtin_ldexpf(gsum, ea);
+  return (_Float16)(__builtin_ldexpf(silu_f(g), -e) * __builtin_ldexpf(usum, ea - e));
+}
+
+// ---------------------------------------------------------------------------
 // CB2.  Two LDS tables, each replicated 8 times so that the 8 lanes of an
 // LDS read phase always hit different bank groups: entry e of copy c sits at
 // byte (8*e + c) * 16.

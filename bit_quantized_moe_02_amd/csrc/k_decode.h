@@ -28,7 +28,7 @@ struct DecArgs {
   float* hsum;                // [T*k][I_pad/16][2]  (sum h, offset sum) per 16 rows
   float* ybuf;                // [T*k][H]   fp32 per-slot down outputs
   float* ysh;                 // [T][H]     fp32 shared-expert output
-  int* err_count;             // invalid expert ids seen
+  int* xexp;                  // [T] each token's exponent e (x enters fp16 as x 2^-e, h is stored as h 2^-2e)
   // Routing inside the single-token CB2 up/gate (null logits: topk_idx is
   // given).  The kernel ranks token t_route's top k from the router's logits
   // [T_route][E] and workgroup 0 writes them to topk_idx_out / topk_w_out

@@ -35,8 +35,6 @@ using namespace qmoe_dec;
 
 namespace {
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
-
 // ---------------------------------------------------------------------------
 // Up/gate.
 
@@ -44,6 +42,7 @@ struct UgShared {
   ExpertList L;
   int64_t item_lo, item_hi;
   float hv[kMaxT][16];
+  uint32_t xef[kMaxT];     // largest exponent field of each token's x
 };
 
 template <int FMT, int CPW>
@@ -65,18 +64,12 @@ __global__ __launch_bounds__(1024) void dec_upgate_kernel(DecArgs a) {
   const int T = a.T, k = a.k;
   const int n_chunks = a.H / 256;
 
-  build_expert_list(a.topk_idx, T * k, k, a.E, &S->L, a.err_count);
+  if (tid < kMaxT) S->xef[tid] = 0u;
+  build_expert_list(a.topk_idx, T * k, k, a.E, &S->L);
+  // each token's exponent (integer maxima in LDS: order-independent)
+  for (int i = tid; i < T * (a.H / 8); i += blockDim.x)
+    atomicMax(&S->xef[i / (a.H / 8)], bf16x8_max_efield(load16(a.x + 8 * (size_t)i)));
   if (FMT == MOE_FMT_CB2) cb2_fill_tables(a.codebook, val_tab, flip_tab, tid, blockDim.x);
-  if (FMT == MOE_FMT_K4) {
-    // per-token sums of x over each 32-column block (m >= T: 0)
-    for (int i = tid; i < (a.H / 32) * 16; i += blockDim.x) {
-      const int blk = i >> 4, m = i & 15;
-      float s = 0.f;
-      if (m < T)
-        for (int j = 0; j < 32; ++j) s += (float)(_Float16)bf2f(a.x[(size_t)m * a.H + blk * 32 + j]);
-      xsum[i] = s;
-    }
-  }
   const int64_t n_rt = a.I / 16, n_rts = a.Is / 16;
   const int64_t w_r = (int64_t)2 * a.tb_ug * n_chunks, w_s = (int64_t)2 * kBf16Tile * n_chunks;
   if (tid == 0) {
@@ -85,20 +78,36 @@ __global__ __launch_bounds__(1024) void dec_upgate_kernel(DecArgs a) {
     S->item_hi = item_start(blockIdx.x + 1, gridDim.x, n_rts, w_s, n_r, w_r);
   }
   __syncthreads();
+  if (blockIdx.x == 0 && tid < T) a.xexp[tid] = x_exp_of_field(S->xef[tid]);
+  if (FMT == MOE_FMT_K4) {
+    // per-token sums of x 2^-e over each 32-column block (m >= T: 0)
+    for (int i = tid; i < (a.H / 32) * 16; i += blockDim.x) {
+      const int blk = i >> 4, m = i & 15;
+      float s = 0.f;
+      if (m < T) {
+        const int xe = x_exp_of_field(S->xef[m]);
+        for (int j = 0; j < 32; ++j)
+          s += (float)(_Float16)__builtin_ldexpf(bf2f(a.x[(size_t)m * a.H + blk * 32 + j]), -xe);
+      }
+      xsum[i] = s;
+    }
+    __syncthreads();
+  }
   const int64_t item_lo = S->item_lo, item_hi = S->item_hi;
   if (item_lo >= item_hi) return;
 
-  // A operands: x[m][256 c + 32 kb + 8 qq + j] as fp16, m = lane % 16.
+  // A operands: x[m][256 c + 32 kb + 8 qq + j] 2^-e_m as fp16, m = lane % 16.
   half8 A[CPW][8];
   {
     const int m = lane & 15, qq = lane >> 4;
+    const int xe = x_exp_of_field(S->xef[m < T ? m : 0]);
     for (int cc = 0; cc < CPW; ++cc) {
       const int chunk = wave * CPW + cc;
       for (int kb = 0; kb < 8; ++kb) {
         u32x4 r = {0, 0, 0, 0};
         if (m < T && chunk < n_chunks) {
           const u32x4 raw = load16(a.x + (size_t)m * a.H + chunk * 256 + kb * 32 + qq * 8);
-          r = as_u32x4(bf16x8_to_half8(raw));
+          r = as_u32x4(bf16x8_to_half8_exp(raw, xe));
         }
         A[cc][kb] = as_half8(r);
       }
@@ -180,7 +189,8 @@ __global__ __launch_bounds__(1024) void dec_upgate_kernel(DecArgs a) {
         u += red[((size_t)w * 2) * 256 + l * 4 + i];
         g += red[((size_t)w * 2 + 1) * 256 + l * 4 + i];
       }
-      const _Float16 h16 = (_Float16)(silu(g) * u);
+      const int xe = x_exp_of_field(S->xef[m]);
+      const _Float16 h16 = h_of(g, u, xe, xe);
       S->hv[m][n] = (float)h16;
       const int64_t row = rt * 16 + n;
       if (shared) {
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(1024) void dec_down_kernel(DecArgs a) {
   const int T = a.T, k = a.k;
   const int n_chunks = a.I_pad / 256;
   const int n_chunks_s = a.Is_pad / 256;
-  build_expert_list(a.topk_idx, T * k, k, a.E, &S->L, nullptr);
+  build_expert_list(a.topk_idx, T * k, k, a.E, &S->L);
   const int64_t n_rt = a.H / 16;
   const int64_t n_rts = (a.Is > 0) ? a.H / 16 : 0;
   const int64_t w_r = (int64_t)a.tb_dn * n_chunks, w_s = (int64_t)kBf16Tile * n_chunks_s;
@@ -420,9 +430,10 @@ __global__ __launch_bounds__(1024) void dec_down_kernel(DecArgs a) {
   }
 }
 
-// y[t][h] = sum_j w[t][j] * ybuf[t*k + j][h] + ysh[t][h], j ascending.
+// y[t][h] = (sum_j w[t][j] * ybuf[t*k + j][h] + ysh[t][h]) 2^(2 e_t), j
+// ascending (h was stored times 2^-2e_t).
 __global__ void combine_kernel(const float* ybuf, const float* ysh, const int32_t* topk_idx,
-                               const float* topk_w, int T, int k, int H, int E, float* y) {
+                               const float* topk_w, const int* xexp, int T, int k, int H, int E, float* y) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)T * H) return;
   const int t = (int)(i / H), h = (int)(i % H);
@@ -433,7 +444,7 @@ __global__ void combine_kernel(const float* ybuf, const float* ysh, const int32_
     acc += topk_w[t * k + j] * ybuf[(size_t)(t * k + j) * H + h];
   }
   if (ysh) acc += ysh[(size_t)t * H + h];
-  y[i] = acc;
+  y[i] = __builtin_ldexpf(acc, 2 * xexp[t]);
 }
 
 }  // namespace
@@ -476,7 +487,7 @@ hipError_t launch_combine(const DecArgs& a, const int32_t* topk_idx, const float
   const int64_t n = (int64_t)a.T * a.H;
   return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&] {
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.ybuf,
-                       a.Is > 0 ? a.ysh : nullptr, topk_idx, topk_w, a.T, a.k, a.H, a.E, y);
+                       a.Is > 0 ? a.ysh : nullptr, topk_idx, topk_w, a.xexp, a.T, a.k, a.H, a.E, y);
   });
 }
 

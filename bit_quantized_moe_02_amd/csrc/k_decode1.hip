@@ -40,6 +40,10 @@ __device__ __forceinline__ int expert_id(const int32_t* topk_idx, int j) {
 __device__ __forceinline__ float choice_weight(const float* topk_w, int j) {
   return ((const __attribute__((address_space(4))) float*)topk_w)[j];
 }
+// The token's exponent, as the up/gate kernel wrote it (scalar load).
+__device__ __forceinline__ int token_exp(const int* xexp) {
+  return ((const __attribute__((address_space(4))) int*)xexp)[0];
+}
 
 // Raw buffer loads of a tile that may not exist: a load whose offset lies
 // past the descriptor's byte count returns zeros and touches no memory, so
@@ -57,8 +61,6 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int off) {
 }
 
 constexpr int kBatch = 8;        // row tiles reduced per barrier (up/gate)
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // Same weighted contiguous split of items as the multi-token kernels: item i
 // goes to the workgroup whose share of the total weight holds its midpoint.
@@ -110,25 +112,42 @@ __global__ __launch_bounds__(1024) void dec1_cb2_wide_upgate_kernel(DecArgs a) {
   const int k = a.k, n_chunks = a.H / 256;
   const int64_t n_rt = a.I / 16, n_rts = a.Is / 16;
   const int64_t w_r = (int64_t)2 * a.tb_ug * n_chunks, w_s = (int64_t)2 * kBf16Tile * n_chunks;
+  uint32_t* xef = reinterpret_cast<uint32_t*>(smem + 16);                     // [NW] largest x exponent field per wave
   if (tid == 0) {
     range[0] = item_start1(blockIdx.x, gridDim.x, n_rts, w_s, (int64_t)k * n_rt, w_r);
     range[1] = item_start1(blockIdx.x + 1, gridDim.x, n_rts, w_s, (int64_t)k * n_rt, w_r);
   }
+  // A operands: row 0 = x 2^-xe, rows 1..15 zero; raw bf16 until the
+  // token's exponent xe is known (every wave's chunks are needed for it)
+  u32x4 xraw[CPW][8];
+  const int qq = lane >> 4;
+  {
+    uint32_t ef = 0;
+    for (int cc = 0; cc < CPW; ++cc)
+      for (int kb = 0; kb < 8; ++kb) {
+        const int chunk = wave * CPW + cc;
+        u32x4 r = {0, 0, 0, 0};
+        if ((lane & 15) == 0 && chunk < n_chunks) r = load16(a.x + chunk * 256 + kb * 32 + qq * 8);
+        xraw[cc][kb] = r;
+        ef = max(ef, bf16x8_max_efield(r));
+      }
+    ef = wave_max_u32(ef);
+    if (lane == 0) xef[wave] = ef;
+  }
   cb2_fill_tables(a.codebook, val_tab, flip_tab, tid, blockDim.x);
   __syncthreads();
+  int xe;
+  {
+    uint32_t ef = 0;
+    for (int w = 0; w < NW; ++w) ef = max(ef, xef[w]);
+    xe = x_exp_of_field(ef);
+  }
+  if (blockIdx.x == 0 && tid == 0) a.xexp[0] = xe;
   const int64_t lo = range[0], hi = range[1];
   if (lo >= hi) return;
-
-  // A operands: row 0 = x, rows 1..15 zero.
   half8 A[CPW][8];
-  const int qq = lane >> 4;
   for (int cc = 0; cc < CPW; ++cc)
-    for (int kb = 0; kb < 8; ++kb) {
-      const int chunk = wave * CPW + cc;
-      u32x4 r = {0, 0, 0, 0};
-      if ((lane & 15) == 0 && chunk < n_chunks) r = as_u32x4(bf16x8_to_half8(load16(a.x + chunk * 256 + kb * 32 + qq * 8)));
-      A[cc][kb] = as_half8(r);
-    }
+    for (int kb = 0; kb < 8; ++kb) A[cc][kb] = bf16x8_to_half8_exp(xraw[cc][kb], xe);
   const bool wave_has_chunks = wave * CPW < n_chunks;
   const uint8_t* val_lane = val_tab + (lane & 7) * 16;
   const uint8_t* flip_lane = flip_tab + (lane & 7) * 16;
@@ -146,7 +165,7 @@ __global__ __launch_bounds__(1024) void dec1_cb2_wide_upgate_kernel(DecArgs a) {
         u += red[((b * NW + w) * 2 + 0) * 16 + n];
         g += red[((b * NW + w) * 2 + 1) * 16 + n];
       }
-      const _Float16 h16 = (_Float16)(silu(g) * u);
+      const _Float16 h16 = h_of(g, u, xe, xe);
       const float hv = (float)h16;
       if (item < n_rts) {
         a.hs[item * 16 + n] = h16;
@@ -308,7 +327,8 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* red_r = reinterpret_cast<float*>(smem + kTabRep * kCb2CombBytes);  // [kRedBatch][2][NW][32]
   float* red_s = red_r + kRedBatch * 2 * NW * 32;                         // [NW][2][8]
-  int* ids = reinterpret_cast<int*>(red_s + NW * 2 * 8);                  // [16] (Route)
+  uint32_t* xef = reinterpret_cast<uint32_t*>(red_s + NW * 2 * 8);        // [NW] largest x exponent field per wave
+  int* ids = reinterpret_cast<int*>(xef + NW);                            // [16] (Route)
   qmoe_route::TopkLds* tk = reinterpret_cast<qmoe_route::TopkLds*>(ids + 16);   // (Route)
 
   const int k = a.k, n_chunks = a.H / 256, n_rt = a.I / 16, n_rts = a.Is / 16;
@@ -338,6 +358,12 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
     for (int i = 0; i < 4; ++i) cbv[i] = cbp[i];
   }
   const u32x4 xr = load16(a.x + chunk * 256 + (m & 7) * 32 + qq * 8);    // used by lanes m < 8
+  {
+    // the token's exponent: each wave's largest field, combined after the
+    // first barrier below
+    const uint32_t ef = wave_max_u32(active ? bf16x8_max_efield(xr) : 0u);
+    if (lane == 0) xef[wave] = ef;
+  }
 
   // shared half tile loads: 2 matrices x 4 k-block pairs (zeros when the
   // workgroup has no shared item)
@@ -404,14 +430,6 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   };
   issue(P0, r_lo);
 
-  // block-diagonal activations: lane (qq, m) holds x block m (m < 8)
-  half8 A[8];
-  {
-    const u32x4 xh = active ? as_u32x4(bf16x8_to_half8(xr)) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int kb = 0; kb < 8; ++kb) A[kb] = as_half8(m == kb ? xh : z);
-  }
-
   // decode table, two steps: the 4 fp16 values of each (idx, half) pair
   // into a staging area, then the 16 sign variants of each, written by
   // consecutive lanes to consecutive entries (no bank conflicts)
@@ -423,6 +441,22 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
     val4[pr] = cb2_pair_values(v);
   }
   __syncthreads();
+
+  // the token's exponent xe; block-diagonal activations x 2^-xe: lane
+  // (qq, m) holds x block m (m < 8)
+  int xe;
+  {
+    uint32_t ef = 0;
+    for (int w = 0; w < NW; ++w) ef = max(ef, xef[w]);
+    xe = x_exp_of_field(ef);
+  }
+  if (blockIdx.x == 0 && tid == 0) a.xexp[0] = xe;
+  half8 A[8];
+  {
+    const u32x4 xh = active ? as_u32x4(bf16x8_to_half8_exp(xr, xe)) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int kb = 0; kb < 8; ++kb) A[kb] = as_half8(m == kb ? xh : z);
+  }
   for (int i = tid; i < 512 * 16 * kTabRep; i += blockDim.x) cb2_comb_put<kTabRep>(tab, i, val4);
   __syncthreads();
 
@@ -455,7 +489,7 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
         u += red_s[(w * 2 + 0) * 8 + tid];
         gg += red_s[(w * 2 + 1) * 8 + tid];
       }
-      a.hs[(su >> 1) * 16 + 8 * (su & 1) + tid] = (_Float16)(silu(gg) * u);
+      a.hs[(su >> 1) * 16 + 8 * (su & 1) + tid] = h_of(gg, u, xe, xe);
     }
     __syncthreads();
   }
@@ -489,7 +523,7 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
         gg += red_r[((b * 2 + 1) * NW + w) * 32 + n];
         gg += red_r[((b * 2 + 1) * NW + w) * 32 + 16 + n];
       }
-      const _Float16 h16 = (_Float16)(silu(gg) * u);
+      const _Float16 h16 = h_of(gg, u, xe, xe);
       const float hv = (float)h16;
       const int j = item / n_rt, rt = item - j * n_rt;
       a.h[(size_t)j * a.I + rt * 16 + n] = h16;
@@ -602,6 +636,7 @@ __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
   float* xsum = reinterpret_cast<float*>(smem + zero_off + 16);            // [H / 32]
   float* red_r = xsum + H / 32;                                            // [kRedBatch][2][NW][32]
   float* red_s = red_r + kRedBatch * 2 * NW * 32;                          // [NW][2][8]
+  uint32_t* xef = reinterpret_cast<uint32_t*>(red_s + NW * 2 * 8);         // [NW] largest x exponent field per wave
 
   const int G = gridDim.x, gi = blockIdx.x;
   const int U_s = 2 * n_rts, U_r = k * n_rt;
@@ -628,10 +663,25 @@ __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
   issue(P0, u_lo);
   issue(P1, u_lo + 1);
 
-  // x -> LDS (fp16) and its 32-column block sums
-  for (int i = tid; i < H / 8; i += blockDim.x)
-    *reinterpret_cast<u32x4*>(xs16 + 8 * i) = as_u32x4(bf16x8_to_half8(load16(a.x + 8 * i)));
+  // the token's exponent xe, then x 2^-xe -> LDS (fp16) and its 32-column
+  // block sums
+  {
+    uint32_t ef = 0;
+    for (int i = tid; i < H / 8; i += blockDim.x) ef = max(ef, bf16x8_max_efield(load16(a.x + 8 * i)));
+    ef = wave_max_u32(ef);
+    if (lane == 0) xef[wave] = ef;
+  }
   if (tid == 0) *reinterpret_cast<u32x4*>(smem + zero_off) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  int xe;
+  {
+    uint32_t ef = 0;
+    for (int w = 0; w < NW; ++w) ef = max(ef, xef[w]);
+    xe = x_exp_of_field(ef);
+  }
+  if (blockIdx.x == 0 && tid == 0) a.xexp[0] = xe;
+  for (int i = tid; i < H / 8; i += blockDim.x)
+    *reinterpret_cast<u32x4*>(xs16 + 8 * i) = as_u32x4(bf16x8_to_half8_exp(load16(a.x + 8 * i), xe));
   __syncthreads();
   for (int b = tid; b < H / 32; b += blockDim.x) {
     float v = 0.f;
@@ -688,7 +738,7 @@ __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
         u += red_s[(w * 2 + 0) * 8 + tid];
         gg += red_s[(w * 2 + 1) * 8 + tid];
       }
-      a.hs[rt * 16 + 8 * hr + tid] = (_Float16)(silu(gg) * u);
+      a.hs[rt * 16 + 8 * hr + tid] = h_of(gg, u, xe, xe);
     }
     __syncthreads();
   }
@@ -730,7 +780,7 @@ __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
         gg += red_r[((b * 2 + 1) * NW + w) * 32 + n];
         gg += red_r[((b * 2 + 1) * NW + w) * 32 + 16 + n];
       }
-      const _Float16 h16 = (_Float16)(silu(gg) * u);
+      const _Float16 h16 = h_of(gg, u, xe, xe);
       const float hv = (float)h16;
       const int j = item / n_rt, rt = item - j * n_rt;
       a.h[(size_t)j * a.I + rt * 16 + n] = h16;
@@ -773,7 +823,8 @@ __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
 }
 
 size_t dec1_k4_upgate_lds(int H, int nw) {
-  return (size_t)2 * H + 16 + (size_t)(H / 32) * 4 + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4;
+  return (size_t)2 * H + 16 + (size_t)(H / 32) * 4 + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4 +
+         (size_t)nw * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -978,7 +1029,7 @@ __global__ __launch_bounds__(1024) void dec1_k4_down_kernel(DecArgs a, const flo
   if (tid < 16) {
     float s = 0.f;
     for (int w = 0; w < NW; ++w) s += red[w * 16 + tid];
-    y[rt * 16 + tid] = s;
+    y[rt * 16 + tid] = __builtin_ldexpf(s, 2 * token_exp(a.xexp));     // h was stored times 2^-2e
   }
 }
 
@@ -1108,7 +1159,7 @@ __global__ __launch_bounds__(1024) void dec1_down_k2d_kernel(DecArgs a, const fl
   if (tid < 16) {
     float sum = 0.f;
     for (int w = 0; w < NW; ++w) sum += red[w * 16 + tid];
-    y[rt * 16 + tid] = sum;
+    y[rt * 16 + tid] = __builtin_ldexpf(sum, 2 * token_exp(a.xexp));   // h was stored times 2^-2e
   }
 }
 
@@ -1117,6 +1168,7 @@ __global__ __launch_bounds__(1024) void dec1_down_k2d_kernel(DecArgs a, const fl
 namespace qmoe {
 
 size_t dec1_cb2_wide_upgate_lds(int nw) { return 256 + 2 * kCb2TableBytes + (size_t)kBatch * nw * 2 * 16 * 4; }
+static_assert(16 + 16 * 4 <= 256, "range and exponent fields fit the first 256 bytes");
 
 size_t dec1_down_lds(const DecArgs& a, int fmt_dn, int nw) {
   if (fmt_dn == MOE_FMT_K2) return (size_t)nw * 16 * 4;  // direct loads: the reduction only
@@ -1128,7 +1180,7 @@ size_t dec1_down_lds(const DecArgs& a, int fmt_dn, int nw) {
 
 size_t dec1_cb2_upgate_lds(int nw, bool route) {
   return (size_t)kTabRep * kCb2CombBytes + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4 +
-         (route ? 16 * 4 + sizeof(qmoe_route::TopkLds) : 0);
+         (size_t)nw * 4 + (route ? 16 * 4 + sizeof(qmoe_route::TopkLds) : 0);
 }
 
 hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,

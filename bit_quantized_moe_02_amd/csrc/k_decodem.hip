@@ -39,8 +39,6 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMRB = 2;      // items per cross-wave reduction (up/gate)
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
-
 __device__ __forceinline__ float4v mfma_bf16(const u32x4& a, const u32x4& b, const float4v& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                   0, 0);
@@ -106,6 +104,8 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* red = reinterpret_cast<float*>(smem + kCb2CombBytes);             // [kMRB][NW][2][64][4]
   ExpertList* L = reinterpret_cast<ExpertList*>(red + kMRB * NW * 2 * 256);
+  uint32_t* xef = reinterpret_cast<uint32_t*>(L + 1);                      // [NW][16] largest x exponent fields
+  int* xe16 = reinterpret_cast<int*>(xef + NW * 16);                        // [16] exponent of token m
 
   const int T = a.T, k = a.k, n_chunks = a.H / 256, n_rt = a.I / 16, n_rts = a.Is / 16;
   const bool active = wave < n_chunks;        // idle waves (H < 1024) load chunk 0 and discard it
@@ -119,8 +119,18 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   int8_t cbv[4] = {0, 0, 0, 0};
   if (tid < 512)
     for (int i = 0; i < 4; ++i) cbv[i] = a.codebook[(tid >> 1) * 8 + 4 * (tid & 1) + i];
+  {
+    // each token's exponent: the wave's largest field of row m (the 4 lanes
+    // qq of row m), combined over the waves after a barrier below
+    uint32_t ef = 0;
+    for (int kb = 0; kb < 8; ++kb) ef = max(ef, bf16x8_max_efield(xr[kb]));
+    if (!active) ef = 0;
+    ef = max(ef, (uint32_t)__shfl_xor((int)ef, 16));
+    ef = max(ef, (uint32_t)__shfl_xor((int)ef, 32));
+    if (lane < 16) xef[wave * 16 + lane] = ef;
+  }
 
-  build_expert_list(a.topk_idx, T * k, k, a.E, L, a.err_count);
+  build_expert_list(a.topk_idx, T * k, k, a.E, L);
   const int64_t n_r = (int64_t)L->n * n_rt;
   const int64_t w_r = (int64_t)2 * kCb2Tile * n_chunks, w_s = (int64_t)2 * kBf16Tile * n_chunks;
   const int64_t lo = item_start(blockIdx.x, gridDim.x, n_rts, w_s, n_r, w_r);
@@ -160,6 +170,16 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   }
   __syncthreads();
   for (int i = tid; i < 512 * 16; i += blockDim.x) cb2_comb_put<1>(tab, i, val4);
+  int xe;                                                                   // exponent of this lane's row m
+  {
+    uint32_t ef = 0;
+    for (int w = 0; w < NW; ++w) ef = max(ef, xef[w * 16 + m]);
+    xe = x_exp_of_field(ef);
+  }
+  if (tid < 16) {
+    xe16[tid] = xe;
+    if (blockIdx.x == 0 && tid < T) a.xexp[tid] = xe;
+  }
   __syncthreads();
 
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -167,16 +187,18 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   // token chose the item's expert), h_s (shared)
   auto flush = [&](int64_t first, int nb) {
     __syncthreads();
-    if (tid < nb * 256) {
-      const int b = tid >> 8, mm = (tid >> 4) & 15, nn = tid & 15;
+    // (a 4-wave workgroup has 256 threads for nb * 256 outputs)
+    for (int o = tid; o < nb * 256; o += blockDim.x) {
+      const int b = o >> 8, mm = (o >> 4) & 15, nn = o & 15;
       const int cl = 16 * (mm >> 2) + nn, ci = mm & 3;
       float u = 0.f, g = 0.f;
       for (int w = 0; w < n_chunks; ++w) {
         u += red[(((b * NW + w) * 2 + 0) * 64 + cl) * 4 + ci];
         g += red[(((b * NW + w) * 2 + 1) * 64 + cl) * 4 + ci];
       }
-      const _Float16 h16 = (_Float16)(silu(g) * u);
       const int64_t item = first + b;
+      // (shared items took raw bf16 x, routed ones x 2^-e)
+      const _Float16 h16 = h_of(g, u, item < n_rts ? 0 : xe16[mm], xe16[mm]);
       if (mm < T) {
         if (item < n_rts) {
           a.hs[(size_t)mm * a.Is + item * 16 + nn] = h16;
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   }
   // routed items, the next two items' weights in flight
   half8 A[8];
-  for (int kb = 0; kb < 8; ++kb) A[kb] = active ? bf16x8_to_half8(xr[kb]) : as_half8(u32x4{0u, 0u, 0u, 0u});
+  for (int kb = 0; kb < 8; ++kb) A[kb] = active ? bf16x8_to_half8_exp(xr[kb], xe) : as_half8(u32x4{0u, 0u, 0u, 0u});
   auto compute = [&](const UgPayM& P, int64_t item) {
     float4v cu = zero, cg = zero;
     if (P.ok) {
@@ -283,7 +305,7 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
 
   const int n_rt = a.H / 16, n_rts = a.Is > 0 ? a.H / 16 : 0;
   const int m = lane & 15, qq = lane >> 4, n = lane & 15;
-  build_expert_list(a.topk_idx, T * k, k, a.E, L, nullptr);
+  build_expert_list(a.topk_idx, T * k, k, a.E, L);
   const int64_t n_r = (int64_t)L->n * n_rt;
   const int64_t w_r = (int64_t)kK2Tile * n_ck, w_s = (int64_t)kBf16Tile * n_cks;
   const int64_t lo = item_start(blockIdx.x, gridDim.x, n_rts, w_s, n_r, w_r);
@@ -456,8 +478,10 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
 // y[t][h] = sum_j w[t][j] * ybuf[t*k + j][h] + ysh[t][h] in j order (choices
 // with an invalid expert id skipped); one workgroup per token, 4 h per thread.
 __global__ __launch_bounds__(256) void decm_combine_kernel(const float* ybuf, const float* ysh, const int32_t* topk_idx,
-                                                           const float* topk_w, int k, int H, int E, float* y) {
+                                                           const float* topk_w, const int* xexp, int k, int H, int E,
+                                                           float* y) {
   const int t = blockIdx.x;
+  const int e2 = 2 * xexp[t];                  // h was stored times 2^-2e
   for (int h = 4 * threadIdx.x; h < H; h += 4 * blockDim.x) {
     float4v v[16];
     bool ok[16];
@@ -478,6 +502,7 @@ __global__ __launch_bounds__(256) void decm_combine_kernel(const float* ybuf, co
       const float4v sv = *reinterpret_cast<const float4v*>(ysh + (size_t)t * H + h);
       for (int q = 0; q < 4; ++q) acc[q] += sv[q];
     }
+    for (int q = 0; q < 4; ++q) acc[q] = __builtin_ldexpf(acc[q], e2);
     *reinterpret_cast<float4v*>(y + (size_t)t * H + h) = acc;
   }
 }
@@ -487,7 +512,7 @@ __global__ __launch_bounds__(256) void decm_combine_kernel(const float* ybuf, co
 namespace qmoe {
 
 size_t decm_upgate_lds(int nw) {
-  return (size_t)kCb2CombBytes + (size_t)kMRB * nw * 2 * 256 * 4 + sizeof(ExpertList);
+  return (size_t)kCb2CombBytes + (size_t)kMRB * nw * 2 * 256 * 4 + sizeof(ExpertList) + (size_t)nw * 16 * 4 + 16 * 4;
 }
 
 size_t decm_down_lds(const DecArgs& a, int nw) {
@@ -516,7 +541,7 @@ hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus,
   if (err != hipSuccess) return err;
   return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&] {
     hipLaunchKernelGGL(decm_combine_kernel, dim3((unsigned)a.T), dim3(256), 0, s, a.ybuf, a.Is > 0 ? a.ysh : nullptr,
-                       a.topk_idx, topk_w, a.k, a.H, a.E, y);
+                       a.topk_idx, topk_w, a.xexp, a.k, a.H, a.E, y);
   });
 }
 

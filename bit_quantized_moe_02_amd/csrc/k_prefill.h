@@ -27,6 +27,8 @@ struct PfArgs {
   _Float16* hs;                   // [T][Is]   fp16
   float* yslot;                   // [T*k][H]  fp32, grouped order
   float* ysh;                     // [T][H]    fp32
+  int* xexp;                      // [T]       each token's exponent e (x enters fp16 as x 2^-e, h = h 2^-2e)
+  int* epos;                      // [T*k]     e of the token at each grouped position
 };
 
 int pf_m_rows();

@@ -54,8 +54,6 @@ __device__ __forceinline__ float16v mfma32_bf(const u32x4& a, const u32x4& b, co
                                                   0, 0, 0);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
-
 // ---------------------------------------------------------------------------
 // A staging.  A 256-column chunk of kMRows token rows goes from global memory
 // straight into LDS through global_load_lds_dwordx4: one instruction writes
@@ -92,9 +90,15 @@ __device__ __forceinline__ void stage_rows(int* rows, int64_t m0, int64_t p_end,
   }
 }
 
+// 16 zero bytes in device memory: the DMA source of every 8-column piece
+// that lies past the end of a row.
+__device__ __attribute__((aligned(16))) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
+
 // Issues the DMA of columns [col0, col0 + 256) of rows[] (2-byte elements,
-// row stride ld) into buf.  Columns at or past col_valid read column
-// col_valid - 8 instead: the packed weights there are zero.
+// row stride ld) into buf.  Pieces at or past col_valid (the padding of a
+// row whose length is not a multiple of 256) are read from kZeroPiece: the
+// packed weights there need not be zero (a K4 sub-block of 32 columns can be
+// half padding, whose codes decode to small non-zero values).
 template <int NW>
 __device__ __forceinline__ void a_dma(uint8_t* buf, const uint16_t* src, int64_t ld, const int* rows, int col0,
                                       int col_valid) {
@@ -103,10 +107,10 @@ __device__ __forceinline__ void a_dma(uint8_t* buf, const uint16_t* src, int64_t
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) {
     const int r0 = 2 * (wave * kDmaPerWave + i), r = r0 + (lane >> 5);
-    int col = col0 + 8 * (((lane & 31) - r) & 31);
-    if (col >= col_valid) col = col_valid - 8;
-    __builtin_amdgcn_global_load_lds(src + (int64_t)rows[i] * ld + col,
-                                     (__attribute__((address_space(3))) void*)(buf + 512 * r0), 16, 0, 0);
+    const int col = col0 + 8 * (((lane & 31) - r) & 31);
+    const uint16_t* p = col < col_valid ? src + (int64_t)rows[i] * ld + col
+                                        : reinterpret_cast<const uint16_t*>(kZeroPiece);
+    __builtin_amdgcn_global_load_lds(p, (__attribute__((address_space(3))) void*)(buf + 512 * r0), 16, 0, 0);
   }
 }
 
@@ -452,7 +456,10 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
       for (int mt = 0; mt < MTA; ++mt)
         for (int i = 0; i < 16; ++i) {
           const int64_t p = m0 + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (p < p_end) a.h[p * a.I + row] = (_Float16)(silu(acc[1][b][mt][i]) * acc[0][b][mt][i]);
+          if (p < p_end) {
+            const int xe = a.epos[p];
+            a.h[p * a.I + row] = h_of(acc[1][b][mt][i], acc[0][b][mt][i], xe, xe);
+          }
         }
     }
   };
@@ -545,7 +552,7 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
     for (int mt = 0; mt < kMT; ++mt)
       for (int i = 0; i < 16; ++i) {
         const int64_t p = p_begin + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (p < p_end) a.hs[p * a.Is + row] = (_Float16)(silu(acc[1][b][mt][i]) * acc[0][b][mt][i]);
+        if (p < p_end) a.hs[p * a.Is + row] = h_of(acc[1][b][mt][i], acc[0][b][mt][i], 0, a.xexp[p]);   // raw bf16 x
       }
   }
 }
@@ -581,11 +588,39 @@ __global__ __launch_bounds__(64 * kUgWaves) void pf_upgate_kernel(PfArgs a) {
   }
 }
 
-// x (bf16) -> x16 (fp16), 8 values per thread: the routed experts' A operand.
-__global__ __launch_bounds__(256) void pf_x16_kernel(const uint16_t* x, uint16_t* x16, int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n8)
-    *reinterpret_cast<u32x4*>(x16 + 8 * i) = as_u32x4(bf16x8_to_half8(load16(x + 8 * i)));
+// One workgroup per token t: its exponent e_t (xexp[t], and epos at the
+// grouped positions of its choices) and x16[t] = fp16(x[t] 2^-e_t), the
+// routed experts' A operand.  Up to kX16Vec 8-value vectors per thread.
+constexpr int kX16Threads = 256, kX16Vec = 4;   // H <= 8192
+
+__global__ __launch_bounds__(kX16Threads) void pf_x16_kernel(const uint16_t* x, uint16_t* x16, int H, int k,
+                                                             const int32_t* slot_pos, int* xexp, int* epos) {
+  __shared__ uint32_t wmax[kX16Threads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, nv = H / 8;
+  const uint16_t* row = x + (size_t)t * H;
+  u32x4 v[kX16Vec];
+  uint32_t ef = 0;
+#pragma unroll
+  for (int i = 0; i < kX16Vec; ++i) {
+    const int c = tid + i * kX16Threads;
+    v[i] = c < nv ? load16(row + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    ef = max(ef, bf16x8_max_efield(v[i]));
+  }
+  ef = wave_max_u32(ef);
+  if ((tid & 63) == 0) wmax[tid >> 6] = ef;
+  __syncthreads();
+  for (int w = 0; w < kX16Threads / 64; ++w) ef = max(ef, wmax[w]);
+  const int xe = x_exp_of_field(ef);
+#pragma unroll
+  for (int i = 0; i < kX16Vec; ++i) {
+    const int c = tid + i * kX16Threads;
+    if (c < nv) *reinterpret_cast<u32x4*>(x16 + (size_t)t * H + 8 * c) = as_u32x4(bf16x8_to_half8_exp(v[i], xe));
+  }
+  if (tid == 0) xexp[t] = xe;
+  if (tid < k) {
+    const int p = slot_pos[(size_t)t * k + tid];
+    if (p >= 0) epos[p] = xe;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -767,9 +802,10 @@ __global__ __launch_bounds__(64 * kDnWaves) void pf_down_kernel(PfArgs a) {
 constexpr int kMaxK = 16;
 
 __global__ __launch_bounds__(256) void pf_combine_kernel(const float* yslot, const float* ysh,
-                                                         const int32_t* slot_pos, const float* topk_w, int T,
-                                                         int k, int H, float* y) {
+                                                         const int32_t* slot_pos, const float* topk_w,
+                                                         const int* xexp, int T, int k, int H, float* y) {
   const int t = blockIdx.x;
+  const int e2 = 2 * xexp[t];                  // h was stored times 2^-2e
   int pos[kMaxK];
   float wj[kMaxK];
 #pragma unroll
@@ -792,6 +828,7 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(const float* yslot, con
       const float4v sv = *reinterpret_cast<const float4v*>(ysh + (size_t)t * H + h);
       for (int q = 0; q < 4; ++q) acc[q] += sv[q];
     }
+    for (int q = 0; q < 4; ++q) acc[q] = __builtin_ldexpf(acc[q], e2);
     *reinterpret_cast<float4v*>(y + (size_t)t * H + h) = acc;
   }
 }
@@ -806,9 +843,9 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
                           hipStream_t s) {
   const int n_groups8 = (a.E + pf_shared_chunks(a) + 7) / 8 * 8;
   {
-    const int64_t n8 = (int64_t)a.T * a.H / 8;
-    hipLaunchKernelGGL(pf_x16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a.x,
-                       const_cast<uint16_t*>(a.x16), n8);
+    if (a.H / 8 > kX16Threads * kX16Vec) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pf_x16_kernel, dim3((unsigned)a.T), dim3(kX16Threads), 0, s, a.x, const_cast<uint16_t*>(a.x16),
+                       a.H, a.k, a.slot_pos, a.xexp, a.epos);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -834,7 +871,7 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
   }
   return launch_timed(MOE_KERNEL_PREFILL_COMBINE, s, [&] {
     hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)a.T), dim3(256), 0, s, a.yslot,
-                       a.Is > 0 ? a.ysh : nullptr, a.slot_pos, topk_w, a.T, a.k, a.H, y);
+                       a.Is > 0 ? a.ysh : nullptr, a.slot_pos, topk_w, a.xexp, a.T, a.k, a.H, y);
   });
 }
 

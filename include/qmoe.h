@@ -36,6 +36,18 @@
  *     aborts, exits or lets a C++ exception escape.
  *   Determinism: every result is a fixed-order computation (no atomics in
  *     any floating-point sum), so repeated calls give identical bits.
+ *   Range: the expert FFN calls give each token t an exponent
+ *     e_t = floor(log2 max_i |x_ti|) - 1, clamped to [-60, 60] (a token of
+ *     zeros gets -60).  Routed-expert GEMMs take x_t * 2^-e_t as fp16
+ *     operands (largest magnitude in [2, 4)), and h is stored as
+ *     fp16(h_t * 2^-2e_t); the power of two is removed again in fp32, which
+ *     is exact.  So tokens with max |x_t| from 2^-59 to 2^62 keep fp16's full
+ *     precision whatever their scale (sums must stay inside fp32's range);
+ *     values of x below
+ *     2^(e_t - 13) (about 2^-15 of the token's largest, or less) and of the
+ *     scaled h below 2^-14 lose precision on fp16's subnormal grid, and the
+ *     scaled h must stay below 65504 (it does for any weights with
+ *     |W_gate x_t 2^-e_t| |W_up x_t 2^-e_t| < 65504).
  */
 #ifndef QMOE_H
 #define QMOE_H
@@ -122,8 +134,11 @@ int moe_codebook_generate(uint64_t seed, int8_t* table_out);
 size_t moe_packed_bytes(int fmt, int64_t rows, int64_t k);
 
 /* Quantizes and packs a host fp32 matrix w [rows, k] (row-major) into
- * out (host, out_bytes >= moe_packed_bytes(fmt, rows, k)).  Columns beyond k
- * up to the next multiple of 256 are taken as zero.
+ * out (host, out_bytes >= moe_packed_bytes(fmt, rows, k)): the quantized
+ * expert matrices of [digest] "Model weights" (CB2 for up/gate, K2 for down)
+ * and [osrepos] "Q4KExperts" (K4), and the unquantized shared expert (BF16,
+ * [upppp] "asymmetric 2-bit quantization").  Columns beyond k up to the next
+ * multiple of 256 are taken as zero.
  *   CB2: per 32 weights s = fp16(max|w| / 0.75) (fp64 quotient, one rounding
  *        to fp16); per group the lowest index e minimizing
  *        sum_{j=0..7} (|w_j| - s*|T[e][j]|/4)^2 (fp64, j ascending); flip bit j
@@ -136,7 +151,9 @@ size_t moe_packed_bytes(int fmt, int64_t rows, int64_t k);
  *   BF16: each value rounded to bf16 (nearest, ties to even).
  * n_threads <= 0 uses all hardware threads.  Errors: MOE_ERR_INVALID_ARG for
  * NULL pointers, bad shapes, non-finite weights, |w| too large for an fp16
- * scale, a missing codebook (CB2) or out_bytes too small. */
+ * scale (CB2 s, K-quant d or dmin would round to infinity), a missing or
+ * malformed codebook (CB2) or out_bytes too small; every check runs before
+ * the first byte of out is written. */
 int moe_quantize_pack(int fmt, const float* w, int64_t rows, int64_t k,
                       const int8_t* codebook, void* out, size_t out_bytes,
                       int n_threads);
@@ -194,9 +211,11 @@ size_t moe_group_workspace_bytes(int32_t T, int32_t k, int32_t E);
  * -- the per-expert token lists that sparse activation works on ([digest]
  * overview).  Outputs (device int32): expert_offsets [E+1] (exclusive scan of
  * per-expert counts), sorted_slots [T*k] (slots ordered by expert, slot order
- * kept within an expert), slot_pos [T*k] (inverse of sorted_slots).  Expert
- * ids outside [0, E) make the call's kernels count them in the workspace and
- * drop the slot (its position is left -1). */
+ * kept within an expert), slot_pos [T*k] (inverse of sorted_slots).  A slot
+ * whose expert id lies outside [0, E) is dropped (its slot_pos is -1) and
+ * counted: the int32 at byte 0 of ws accumulates the number of such slots
+ * (atomically, over calls); zero it before the call to read one call's
+ * count.  The rest of ws needs no initialization. */
 int moe_group_tokens(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
                      int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_pos,
                      void* ws, size_t ws_bytes, void* stream);
@@ -205,21 +224,27 @@ int moe_group_tokens(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
  * (prefill != 0: the grouped prefill path; else decode, T <= 16). */
 size_t moe_ffn_workspace_bytes(const moe_weights* w, int32_t T, int32_t k, int prefill);
 
-/* Expert FFN for 1..16 tokens (decode / draft verification):
+/* Expert FFN for 1..16 tokens (decode / draft verification): the routed
+ * experts with quantized weights plus the unquantized shared expert
+ * ([digest] "Model weights"; [upppp] "asymmetric 2-bit quantization"), run
+ * only for the k experts each token chose (sparse activation, [digest]
+ * overview):
  *   y[t] = sum_j topk_w[t,j] * FFN_{topk_idx[t,j]}(x[t]) + FFN_shared(x[t]),
  *   FFN(x) = W_down (SiLU(W_gate x) * (W_up x)), summed j = 0..k-1 then the
  *   shared expert.  x_bf16 device bf16 [T, H]; y device fp32 [T, H]
- *   (overwritten).  The intermediate h is fp16; sums are fp32.  Up to 3
+ *   (overwritten).  The intermediate h is fp16 (scaled per token, see
+ *   "Range" above); sums are fp32.  Up to 3
  *   tokens run the single-token kernels once per token, which decode the
  *   weights exactly (scales applied to fp32 block sums); for T >= 4 a layer
  *   with CB2 up/gate, hidden <= 4096 and inter, shared_inter <= 2048 takes
  *   batched kernels that read each distinct expert once and fold the CB2
  *   scales into fp16 weights (one rounding per weight, as
  *   moe_expert_ffn_prefill does); their K2 down weights stay exact.  A choice whose
- *   expert id lies outside [0, E) contributes nothing; a token may name one
- *   expert in several choices (each contributes).  The first bytes of ws
- *   hold h as fp16 [T*k, inter] (slot order) after the call.  Limits:
- *   1 <= T <= 16, 1 <= k <= 16. */
+ *   expert id lies outside [0, E) contributes nothing (and is not counted);
+ *   a token may name one expert in several choices (each contributes).  ws
+ *   needs no initialization; its first bytes hold h * 2^-2e_t as fp16
+ *   [T*k, inter] (slot order) after the call.  Limits: 1 <= T <= 16,
+ *   1 <= k <= 16. */
 int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
                           const int32_t* topk_idx, const float* topk_w, float* y,
                           void* ws, size_t ws_bytes, void* stream);
@@ -227,9 +252,11 @@ int moe_expert_ffn_decode(const moe_weights* w, const void* x_bf16, int32_t T, i
 /* Workspace bytes of moe_layer_decode (0 for invalid arguments). */
 size_t moe_layer_decode_workspace_bytes(const moe_weights* w, int32_t T, int32_t k);
 
-/* One decode step of the whole layer: moe_route then moe_expert_ffn_decode
- * in one call, with the same results (topk_idx, topk_w and y as those two
- * calls give; topk_* are outputs here).  One token on a CB2 layer with
+/* One decode step of the whole layer ([digest] "Model weights": unquantized
+ * router, quantized routed experts, unquantized shared expert; batch-1
+ * generation as the pages benchmark it): moe_route then
+ * moe_expert_ffn_decode in one call, with the same results (topk_idx, topk_w
+ * and y as those two calls give; topk_* are outputs here).  One token on a CB2 layer with
  * hidden <= 4096 and E <= 64*max(4, hidden/256) has its experts ranked
  * inside the up/gate kernel, from the router's logits, while the shared
  * expert's weights already stream; other shapes run the router's top-k
@@ -241,11 +268,13 @@ int moe_layer_decode(const moe_weights* w, const float* w_router, const float* l
                      const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx, float* topk_w,
                      float* y, void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFN for a prefill chunk (any T >= 1), same result as the decode
+/* Expert FFN for a prefill chunk (any T >= 1; the pages prefill prompts in
+ * chunks of 2048 tokens, [blog] server logs), same result as the decode
  * call, computed as grouped GEMMs over moe_group_tokens' output (device
  * int32 arrays as that call writes them).  Dequantized weights and h are
- * fp16 MFMA operands; sums are fp32.  The first bytes of ws hold h as fp16
- * [T*k, inter] in grouped (sorted_slots) order after the call. */
+ * fp16 MFMA operands; sums are fp32.  ws needs no initialization; its first
+ * bytes hold h * 2^-2e_t as fp16 [T*k, inter] in grouped (sorted_slots)
+ * order after the call. */
 int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
                            const int32_t* topk_idx, const float* topk_w,
                            const int32_t* expert_offsets, const int32_t* sorted_slots,

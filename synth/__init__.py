@@ -158,11 +158,12 @@ def shared_weight_bits(w: Workload, which: str) -> np.ndarray:
     return to_bf16_bits(normal_f32(w.seed, tag, 0, shape, WEIGHT_STD))
 
 
-def activations_bits(w: Workload, n_tokens: int, step: int = 0) -> np.ndarray:
-    """bf16 bit patterns of the layer input x [n_tokens, H], N(0, 1).
+def activations_bits(w: Workload, n_tokens: int, step: int = 0, scale: float = 1.0) -> np.ndarray:
+    """bf16 bit patterns of the layer input x [n_tokens, H], N(0, scale^2)
+    (the fp32 draw times `scale`, then rounded to bf16).
 
     Step s of a multi-step workload is an independent draw (index = step)."""
-    return to_bf16_bits(normal_f32(w.seed, w.x_tag, step, (n_tokens, w.hidden), 1.0))
+    return to_bf16_bits(normal_f32(w.seed, w.x_tag, step, (n_tokens, w.hidden), scale))
 
 
 def activations_f32(w: Workload, n_tokens: int, step: int = 0) -> np.ndarray:

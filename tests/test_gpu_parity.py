@@ -47,7 +47,7 @@ def _route(q, layer, xb, k):
     E = layer.n_experts
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(q.moe_route_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
+    ws = torch.full((q.moe_route_workspace_bytes(T, E),), 0xFF, dtype=torch.uint8, device="cuda")
     q.moe_route(_bf16(xb), layer.router, layer.bias, T, H, E, k, idx, w, ws)
     return idx, w
 
@@ -55,8 +55,8 @@ def _route(q, layer, xb, k):
 def _decode(q, layer, xb, idx, w, k):
     import torch
     T = xb.shape[0]
-    y = torch.empty((T, layer.hidden), dtype=torch.float32, device="cuda")
-    ws = torch.empty(q.moe_ffn_workspace_bytes(layer.w, T, k, False), dtype=torch.uint8, device="cuda")
+    y = torch.full((T, layer.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((q.moe_ffn_workspace_bytes(layer.w, T, k, False),), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes
     q.moe_expert_ffn_decode(layer.w, _bf16(xb), T, k, idx, w, y, ws)
     torch.cuda.synchronize()
     return y, ws
@@ -71,8 +71,8 @@ def _prefill(q, layer, xb, idx, w, k):
     sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
     gws = torch.zeros(q.moe_group_workspace_bytes(T, k, E), dtype=torch.uint8, device="cuda")
     q.moe_group_tokens(idx, T, k, E, off, ss, sp, gws)
-    y = torch.empty((T, layer.hidden), dtype=torch.float32, device="cuda")
-    ws = torch.empty(q.moe_ffn_workspace_bytes(layer.w, T, k, True), dtype=torch.uint8, device="cuda")
+    y = torch.full((T, layer.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((q.moe_ffn_workspace_bytes(layer.w, T, k, True),), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes
     q.moe_expert_ffn_prefill(layer.w, _bf16(xb), T, k, idx, w, off, ss, sp, y, ws)
     torch.cuda.synchronize()
     return y, ws, (off, ss, sp)
@@ -307,7 +307,10 @@ def test_decode_tiny_full_layer(q):
     from layer_fixture import oracle_expert
     import torch
     h = ws[: wl.tokens * wl.top_k * wl.inter * 2].view(torch.float16)
-    h = h.float().cpu().numpy().reshape(wl.tokens * wl.top_k, wl.inter)
+    h = h.float().cpu().numpy().reshape(wl.tokens * wl.top_k, wl.inter).astype(np.float64)
+    # stored as fp16(h 2^-2e), e = floor(log2 max|x_t|) - 1 per token
+    e = np.clip(((xb.astype(np.int64) >> 7) & 0xFF).max(axis=1) - 128, -60, 60)
+    h *= np.repeat(2.0 ** (2 * e), wl.top_k)[:, None]
     for t in range(wl.tokens):
         for j in range(wl.top_k):
             wu, wg, _ = oracle_expert(wl, int(o_idx[t, j]))
