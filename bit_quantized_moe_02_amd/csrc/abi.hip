@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/qmoe.h"
@@ -344,28 +345,110 @@ extern "C" size_t moe_layer_decode_workspace_bytes(const moe_weights* w, int32_t
   return align_up(dec_layout(g, T, k).total) + align_up(route_logit_floats(T, g.E) * 4);
 }
 
+namespace {
+
+// Checks of moe_layer_decode beyond check_decode (the workspace aside).
+int check_layer_decode(const char* who, const moe_weights* w, Geometry* g, const float* w_router,
+                       const void* x_bf16, int32_t T, int32_t k, const void* topk_idx, const void* topk_w,
+                       const float* y, const void* ws) {
+  int rc = check_decode(who, w, g, x_bf16, T, k, topk_idx, topk_w, y, ws);
+  if (rc != MOE_OK) return rc;
+  if (!w_router) return fail(MOE_ERR_INVALID_ARG, std::string(who) + ": NULL router");
+  if (!aligned16(w_router)) return fail(MOE_ERR_INVALID_ARG, std::string(who) + ": w_router must be 16-byte aligned");
+  return MOE_OK;
+}
+
+int run_layer_decode(const char* who, const moe_weights* w, const Geometry& g, const float* w_router,
+                     const float* logit_bias, const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx,
+                     float* topk_w, float* y, uint8_t* wsb, hipStream_t s);
+
+}  // namespace
+
 extern "C" int moe_layer_decode(const moe_weights* w, const float* w_router, const float* logit_bias,
                                 const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx, float* topk_w,
                                 float* y, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
   Geometry g;
-  int rc = check_decode("moe_layer_decode", w, &g, x_bf16, T, k, topk_idx, topk_w, y, ws);
+  int rc = check_layer_decode("moe_layer_decode", w, &g, w_router, x_bf16, T, k, topk_idx, topk_w, y, ws);
   if (rc != MOE_OK) return rc;
-  if (!w_router) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: NULL router");
-  if (!aligned16(w_router)) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: w_router must be 16-byte aligned");
-  if (g.E > 1024) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: E <= 1024");
-  const size_t off_logits = align_up(dec_layout(g, T, k).total);
   if (ws_bytes < moe_layer_decode_workspace_bytes(w, T, k))
     return fail(MOE_ERR_WORKSPACE, "moe_layer_decode: workspace too small (need " +
                                        std::to_string(moe_layer_decode_workspace_bytes(w, T, k)) + ")");
-  uint8_t* wsb = (uint8_t*)ws;
-  hipStream_t s = (hipStream_t)stream;
+  return run_layer_decode("moe_layer_decode", w, g, w_router, logit_bias, x_bf16, T, k, topk_idx, topk_w, y,
+                          (uint8_t*)ws, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// moe_layer_decode_noalloc: the same step with its workspace in a file-scope
+// device array.  The array's name is a host-side stand-in in host code; its
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is ever handed to a kernel.
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(const char* who, uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(who, e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, std::string(who) + ": device index beyond " + std::to_string(kMaxDevices));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(who, e);
+    if (!p) return fail(MOE_ERR_HIP, std::string(who) + ": no device address for the scratch array");
+    g_scratch_ptr[dev] = (uint8_t*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_layer_decode_noalloc(const moe_weights* w, const float* w_router, const float* logit_bias,
+                                        const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx,
+                                        float* topk_w, float* y, void* stream) {
+  clear_error();
+  static const char* who = "moe_layer_decode_noalloc";
+  Geometry g;
+  // (an aligned non-null stand-in for ws: the scratch array replaces it)
+  int rc = check_layer_decode(who, w, &g, w_router, x_bf16, T, k, topk_idx, topk_w, y,
+                              reinterpret_cast<const void*>(kAlign));
+  if (rc != MOE_OK) return rc;
+  const size_t need = moe_layer_decode_workspace_bytes(w, T, k);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, std::string(who) + ": this layer and T need " + std::to_string(need) +
+                                       " bytes of scratch, more than the " + std::to_string(kScratchBytes) +
+                                       " the library holds; use moe_layer_decode with a workspace");
+  uint8_t* sp = nullptr;
+  rc = scratch_address(who, &sp);
+  if (rc != MOE_OK) return rc;
+  return run_layer_decode(who, w, g, w_router, logit_bias, x_bf16, T, k, topk_idx, topk_w, y, sp,
+                          (hipStream_t)stream);
+}
+
+namespace {
+
+int run_layer_decode(const char* who, const moe_weights* w, const Geometry& g, const float* w_router,
+                     const float* logit_bias, const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx,
+                     float* topk_w, float* y, uint8_t* wsb, hipStream_t s) {
+  const size_t off_logits = align_up(dec_layout(g, T, k).total);
   float* logits = (float*)(wsb + off_logits);
   hipError_t e = launch_route_logits((const uint16_t*)x_bf16, w_router, logit_bias, T, g.H, g.E, logits, s);
-  if (e != hipSuccess) return hip_fail("moe_layer_decode (router)", e);
+  if (e != hipSuccess) return hip_fail(who, e);
   const DecRoute route{logits, route_logit_parts(T, g.H)};
-  return run_decode("moe_layer_decode", w, g, x_bf16, T, k, topk_idx, topk_w, y, wsb, s, &route);
+  return run_decode(who, w, g, x_bf16, T, k, topk_idx, topk_w, y, wsb, s, &route);
 }
+
+}  // namespace
 
 extern "C" int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, int32_t T, int32_t k,
                                       const int32_t* topk_idx, const float* topk_w,
@@ -451,3 +534,4 @@ extern "C" int moe_debug_dequant(int fmt, const void* packed, int64_t rows, int6
   if (e != hipSuccess) return hip_fail("moe_debug_dequant", e);
   return MOE_OK;
 }
+

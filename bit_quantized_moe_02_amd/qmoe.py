@@ -36,8 +36,9 @@ EXPORTED = [
     "moe_route_workspace_bytes", "moe_route", "moe_group_workspace_bytes",
     "moe_group_tokens", "moe_ffn_workspace_bytes", "moe_expert_ffn_decode",
     "moe_expert_ffn_prefill", "moe_layer_decode_workspace_bytes", "moe_layer_decode",
-    "moe_debug_dequant", "moe_profile_next_launch", "moe_last_error",
+    "moe_debug_dequant", "moe_profile_next_launch", "moe_last_error", "moe_layer_decode_noalloc",
 ]
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 MOE_KERNEL = {"route_logits": 0, "route_topk": 1, "decode_upgate": 2, "decode_down": 3,
               "decode_combine": 4, "group": 5, "prefill_upgate": 6, "prefill_down": 7,
@@ -85,6 +86,8 @@ def _load():
         "moe_layer_decode_workspace_bytes": (sz, [ctypes.POINTER(MoeWeights), i32, i32]),
         "moe_layer_decode": (ctypes.c_int, [ctypes.POINTER(MoeWeights), vp, vp, vp, i32, i32, vp, vp, vp,
                                             vp, sz, vp]),
+        "moe_layer_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeWeights), vp, vp, vp, i32, i32, vp, vp, vp,
+                                                    vp]),
         "moe_debug_dequant": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp, vp]),
         "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, vp, vp]),
         "moe_last_error": (ctypes.c_char_p, []),
@@ -204,6 +207,17 @@ def moe_expert_ffn_decode(w: MoeWeights, x_bf16, T, k, topk_idx, topk_w, y, ws, 
 
 def moe_layer_decode_workspace_bytes(w: MoeWeights, T: int, k: int) -> int:
     return int(lib.moe_layer_decode_workspace_bytes(ctypes.byref(w), T, k))
+
+
+def moe_layer_decode_noalloc(w: MoeWeights, w_router, logit_bias, x_bf16, T, k, topk_idx, topk_w, y, stream=None):
+    """moe_layer_decode with the library's own device scratch (allocates nothing)."""
+    E, H = w.n_experts, w.hidden
+    _check(lib.moe_layer_decode_noalloc(ctypes.byref(w), _dev(w_router, "w_router", torch.float32, E * H),
+                                        _dev(logit_bias, "logit_bias", torch.float32, E, optional=True),
+                                        _dev(x_bf16, "x_bf16", torch.bfloat16, T * H), T, k,
+                                        _dev(topk_idx, "topk_idx", torch.int32, T * k),
+                                        _dev(topk_w, "topk_w", torch.float32, T * k),
+                                        _dev(y, "y", torch.float32, T * H), _stream(stream)))
 
 
 def moe_layer_decode(w: MoeWeights, w_router, logit_bias, x_bf16, T, k, topk_idx, topk_w, y, ws, stream=None):

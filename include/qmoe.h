@@ -268,6 +268,23 @@ int moe_layer_decode(const moe_weights* w, const float* w_router, const float* l
                      const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx, float* topk_w,
                      float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, the same results, with its workspace in an
+ * array the library holds in device memory, MOE_NOALLOC_SCRATCH_BYTES
+ * (8 MiB) per GPU, kept until the process ends.  The call allocates nothing.
+ * Arguments as for moe_layer_decode without ws / ws_bytes.  Every call on one
+ * GPU uses that GPU's one array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe.  Errors:
+ * as moe_layer_decode; MOE_ERR_WORKSPACE when
+ * moe_layer_decode_workspace_bytes(w, T, k) exceeds the array (nothing is
+ * enqueued).  The array's contents are not preserved between calls. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_layer_decode_noalloc(const moe_weights* w, const float* w_router, const float* logit_bias,
+                             const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx, float* topk_w,
+                             float* y, void* stream);
+
 /* Expert FFN for a prefill chunk (any T >= 1; the pages prefill prompts in
  * chunks of 2048 tokens, [blog] server logs), same result as the decode
  * call, computed as grouped GEMMs over moe_group_tokens' output (device

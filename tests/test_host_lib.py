@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(q):
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     lib = ctypes.CDLL(q.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -212,6 +212,16 @@ def test_device_call_argument_errors(q):
     assert lay(ctypes.byref(w), P + 4, None, P, 1, 8, P, P, P, P, lws, None) == 1   # router alignment
     assert lay(ctypes.byref(w), P, None, P, 17, 8, P, P, P, P, 1 << 30, None) == 1  # T > 16
     assert lay(ctypes.byref(w2), P, None, P, 1, 8, P, P, P, P, lws, None) == 2      # mixed formats
+    # the allocation-free step: argument checks, and a layer whose workspace
+    # exceeds the library's array is refused before any GPU call
+    na = lib.moe_layer_decode_noalloc
+    assert na(ctypes.byref(w), None, None, P, 1, 8, P, P, P, None) == 1            # no router
+    assert na(ctypes.byref(w), P, None, P, 17, 8, P, P, P, None) == 1              # T > 16
+    assert na(ctypes.byref(w2), P, None, P, 1, 8, P, P, P, None) == 2              # mixed formats
+    wbig = _fake_weights(q, hidden=8192, inter=64, shared_inter=0, n_experts=16, fmt_up=3, fmt_gate=3, fmt_down=3)
+    assert q.moe_layer_decode_workspace_bytes(wbig, 16, 16) > q.MOE_NOALLOC_SCRATCH_BYTES
+    assert na(ctypes.byref(wbig), P, None, P, 16, 16, P, P, P, None) == 3
+    assert "scratch" in q.moe_last_error()
     w3 = _fake_weights(q, hidden=4000)
     assert dec(ctypes.byref(w3), P, 1, 8, P, P, P, P, ws, None) == 1
     w4 = _fake_weights(q, up=P + 8)
