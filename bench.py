@@ -1,18 +1,36 @@
 """Benchmark of the routed 2-bit MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_b1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
 
-A step is one pass of the whole hot path over one batch: route (router GEMV,
-top-k) and the expert FFN (decode: up/gate + SiLU, down, combine; prefill:
-grouping, grouped up/gate GEMM, grouped down GEMM, combine).  Inputs and
-weights are resident in HBM before timing starts.  Decode workloads rotate
-over --instances copies of the layer's weights so that consecutive steps do
-not find the previous step's experts in the 256 MB last-level cache.
+The headline metric is MoE-layer tokens/s at batch-1 decode and at a
+2048-token prefill chunk, each with its roofline fraction (HBM for decode,
+MFMA for prefill).  The default run (--workload headline) measures both and
+prints them in ONE JSON line:
 
-Prints one JSON line: whole-layer tokens/s, the dominant kernel's roofline
-(HBM for decode, MFMA for prefill; its duration measured with HIP events
-around that kernel on its stream inside the timed region) and the fp64 CPU
-oracle's tokens/s on a bounded sample of the same workload.
+  value / ms_per_step / roofline   decode_b1: K single-token steps, each one
+                                   moe_layer_decode call (router, top-k, expert
+                                   FFN, combine), replayed from one captured
+                                   HIP graph; the dominant kernel's roofline
+                                   over the bytes it streams (routed experts +
+                                   bf16 shared expert), against 8 TB/s and
+                                   against a measured streaming read of the
+                                   same byte count.
+  decode_quantized_only            the same layer and tokens without the shared
+                                   expert (I_s = 0): %HBM over the quantized
+                                   expert bytes alone.
+  prefill_2048                     the 2048-token chunk: route, group, grouped
+                                   GEMMs, combine; tokens/s and the dominant
+                                   GEMM's MFMA fraction.
+  cpu_baseline                     the fp64 CPU oracle on a bounded sample.
+
+A step is one pass of the whole hot path over one batch.  Inputs and weights
+are resident in HBM before timing starts.  Decode rotates over --instances
+copies of the weights so that a step never finds the previous step's experts
+in the 256 MB last-level cache.  Kernel durations come from HIP events that
+hipExtLaunchKernel records at each kernel dispatch's start and end (the
+library's moe_profile_next_launch hook), in a pass that launches the same
+steps one by one on the stream the kernels run on; events captured into a
+graph carry no timestamps.  --workload W measures one other workload alone.
 """
 from __future__ import annotations
 
@@ -37,23 +55,22 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch (read + written) of the dominant kernels, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the counts the same
 # counters gave for an elementwise pass of known size (FETCH x 2.0, WRITE x 1.0);
-# the summaries are profiles/<workload>_counters.md.  Each entry holds a digest
-# of the kernel sources it was measured on: when the sources differ, the figure
-# no longer describes the kernel and "traffic" is reported as null.
-MEASURED_TRAFFIC = {
-    ("decode_b1", "decode_upgate"): ("abb06f880411c12b:66c6882cc36e9a40", 76.28e6 + 0.049e6),
-    ("decode_b1", "decode_down"): ("abb06f880411c12b:66c6882cc36e9a40", 39.33e6 + 0.016e6),
-    ("prefill_2048", "prefill_upgate"): ("073ea6d28936fe05:66c6882cc36e9a40", 1761.42e6 + 75.497e6),
-    ("prefill_2048", "prefill_down"): ("073ea6d28936fe05:66c6882cc36e9a40", 1015.51e6 + 301.990e6),
-}
-TRAFFIC_SOURCES = {"decode": ["k_decode1.hip", "device_common.hpp"], "prefill": ["k_prefill.hip", "device_common.hpp"]}
+# the summaries are under profiles/.  Each entry holds a digest of every source
+# that feeds the kernel: when the sources differ, the figure no longer
+# describes the kernel and "traffic" is reported as null.
+MEASURED_TRAFFIC: dict = {}
+KERNEL_SOURCES = ["abi.hip", "device_common.hpp", "route_common.hpp", "decode_common.hpp", "launch_util.h",
+                  "k_decode.h", "k_prefill.h", "k_decode1.hip", "k_decodem.hip", "k_decode.hip", "k_prefill.hip",
+                  "k_route.hip", "k_misc.hip"]
 
 
-def source_digest(kind):
+def source_digest():
     import hashlib
     d = os.path.join(ROOT, "bit_quantized_moe_02_amd", "csrc")
-    return ":".join(hashlib.sha256(open(os.path.join(d, f), "rb").read()).hexdigest()[:16]
-                    for f in TRAFFIC_SOURCES[kind])
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 # The decode call runs the single-token kernels once per token up to this
@@ -70,18 +87,13 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--steps", type=int, default=None, help="timed decode steps (prefill: at most 50)")
     p.add_argument("--warmup", type=int, default=None)
-    p.add_argument("--workload", default="decode_b1", choices=sorted(DECODE | PREFILL))
+    p.add_argument("--workload", default="headline", choices=["headline"] + sorted(DECODE | PREFILL))
     p.add_argument("--instances", type=int, default=None,
                    help="layer copies rotated over the decode steps (default 4 for decode, 1 for prefill)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--no-kernel-events", action="store_true",
-                   help="time the steps without the per-kernel events")
-    p.add_argument("--eager", action="store_true",
-                   help="launch every step from Python instead of replaying one captured HIP graph "
-                        "(decode workloads; prefill always runs eagerly)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="also run one elementwise pass (torch.neg) over MIB MiB: a kernel of known "
                         "traffic that the hardware byte counters are scaled by")
@@ -139,11 +151,19 @@ def build_layer(wl, instances):
     return layers, (nb_up, nb_dn)
 
 
+def without_shared(layer, wl):
+    """The same routed experts and router with the shared expert left out."""
+    from bit_quantized_moe_02_amd import qmoe
+    t = layer.tensors
+    return qmoe.DeviceLayer(wl.n_experts, wl.hidden, wl.inter, 0, wl.fmts, t["up"], t["gate"], t["down"],
+                            codebook=t["codebook"], router=t["router"], bias=t["bias"])
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle as it stands, on a bounded sample
 
 
-def cpu_baseline(wl, seconds):
+def cpu_baseline(wl, seconds, max_tokens=8):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle as O
     cores = len(os.sched_getaffinity(0))
@@ -156,13 +176,11 @@ def cpu_baseline(wl, seconds):
                        for w in ("up", "gate", "down"))
     # sample tokens: the workload's own inputs, in order
     if wl.name in DECODE:
-        per_step = wl.tokens
         xs = [synth.bf16_bits_to_f32(synth.activations_bits(wl, wl.tokens, step=s)).astype(np.float64)
-              for s in range(8)]
+              for s in range(max_tokens)]
     else:
         full = synth.bf16_bits_to_f32(synth.activations_bits(wl, wl.tokens)).astype(np.float64)
-        per_step = 1
-        xs = [full[i:i + 1] for i in range(8)]
+        xs = [full[i:i + 1] for i in range(max_tokens)]
     fields = {}
 
     def fields_of(e):   # oracle quantization of an expert (set-up, not timed)
@@ -196,6 +214,214 @@ def cpu_baseline(wl, seconds):
 
 
 # ---------------------------------------------------------------------------
+# Timing
+
+
+class Events:
+    """Reusable torch events for the per-kernel dispatch timestamps."""
+
+    def __init__(self, names, n):
+        import torch
+        self.ev = {kn: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                        for _ in range(n)] for kn in names}
+        for kn in names:          # torch creates the HIP event on its first record
+            for a, b in self.ev[kn]:
+                a.record()
+                b.record()
+
+    def arm(self, i):
+        from bit_quantized_moe_02_amd import qmoe
+        for kn, lst in self.ev.items():
+            qmoe.moe_profile_next_launch(kn, *lst[i])
+
+    def seconds(self, kn):
+        return np.array([a.elapsed_time(b) for a, b in self.ev[kn]]) * 1e-3
+
+
+def time_decode(wl, layers, steps, warmup, label):
+    """K steps of moe_layer_decode replayed from one HIP graph, then the same
+    steps launched one by one with dispatch events on every kernel."""
+    import torch
+    from bit_quantized_moe_02_amd import qmoe
+    E, H, k, T = wl.n_experts, wl.hidden, wl.top_k, wl.tokens
+    inst = len(layers)
+    n_x = min(steps + warmup, wl.steps)
+    xs = torch.stack([torch.from_numpy(synth.activations_bits(wl, T, step=s).view(np.int16)).view(torch.bfloat16)
+                      for s in range(n_x)]).cuda()
+    n_total = steps + warmup
+    idx_all = torch.empty((n_total, T, k), dtype=torch.int32, device="cuda")
+    w_all = torch.empty((n_total, T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qmoe.moe_layer_decode_workspace_bytes(layers[0].w, T, k), dtype=torch.uint8, device="cuda")
+    kernels = ["route_logits", "decode_upgate", "decode_down"]
+    ev = Events(kernels, steps)
+
+    def step(s, timed):
+        layer = layers[s % inst]
+        if timed is not None:
+            ev.arm(timed)
+        qmoe.moe_layer_decode(layer.w, layer.router, layer.bias, xs[s % n_x], T, k, idx_all[s], w_all[s], y, ws)
+
+    for s in range(warmup):
+        step(s, None)
+    torch.cuda.synchronize()
+    # The K timed steps are captured back to back into one HIP graph (each
+    # step: route + expert FFN of its own token, with its own input row, layer
+    # copy and output slots), so host launch overhead -- which a whole-model
+    # decode graph spreads over all its layers -- stays out of the per-layer
+    # figure.  One untimed replay uploads the graph first.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(warmup + i, None)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    log(f"[bench] {label}: {steps} steps in {1e3 * (t1 - t0):.2f} ms (graph)")
+    te0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, i)
+    torch.cuda.synchronize()
+    te1 = time.perf_counter()
+    del graph
+    return {"seconds": t1 - t0, "durs": {kn: ev.seconds(kn) for kn in kernels},
+            "idx": idx_all[warmup:].cpu().numpy(), "eager_tps": steps * T / (te1 - te0)}
+
+
+def decode_work(wl, idx_h, nb_up, nb_dn):
+    """Algorithmic bytes per timed launch of the up/gate and down kernels and
+    the quantized expert bytes alone, from the routing each step made."""
+    T, k, H, I, Is = wl.tokens, wl.top_k, wl.hidden, wl.inter, wl.shared_inter
+    w = {"decode_upgate": [], "decode_down": [], "route_logits": [], "quant_upgate": [], "quant_down": []}
+    for s in range(idx_h.shape[0]):
+        # up to DEC_PER_TOKEN_MAX tokens the library runs the single-token
+        # kernels once per token and the events time the first token's
+        # launch; beyond, one launch covers the whole batch
+        Tl = 1 if T <= DEC_PER_TOKEN_MAX else T
+        d = len(np.unique(idx_h[s][:Tl]))
+        w["quant_upgate"].append(d * 2 * nb_up)
+        w["quant_down"].append(d * nb_dn)
+        # up/gate: both matrices of the distinct routed experts + shared, x in, h out
+        w["decode_upgate"].append(d * 2 * nb_up + 2 * Is * H * 2 + Tl * H * 2 + Tl * k * I * 2 + Tl * Is * 2)
+        # down: the distinct routed down matrices + shared, h in, y out
+        w["decode_down"].append(d * nb_dn + H * Is * 2 + Tl * k * I * 2 + Tl * Is * 2 + Tl * H * 4)
+        # router: fp32 weights + x in, logits out
+        w["route_logits"].append(wl.n_experts * H * 4 + T * H * 2 + T * wl.n_experts * 4)
+    return {kn: np.array(v, dtype=np.float64) for kn, v in w.items()}
+
+
+def kernel_stats(durs, work, scale, peak):
+    ach = work.sum() / durs.sum() / scale
+    return {"avg_us": round(float(durs.mean()) * 1e6, 2), "achieved": round(float(ach), 1),
+            "frac": round(float(ach / peak), 4), "work_per_launch": float(work.mean())}
+
+
+def read_ceiling(nbytes, reps=24):
+    """Rate of the library's streaming-read kernel over `nbytes` (rounded to
+    16), rotating over enough buffers that the 256 MB last-level cache holds
+    none of them, timed with dispatch events: GB/s (best grid of 2, 4 or 8
+    workgroups per compute unit)."""
+    import torch
+    from bit_quantized_moe_02_amd import qmoe
+    nbytes = (int(nbytes) + 15) // 16 * 16
+    nbuf = max(2, -(-(512 << 20) // nbytes))
+    bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device="cuda") for i in range(nbuf)]
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = None
+    for per_cu in (2, 4, 8):
+        ev = Events(["read"], reps)
+        for i in range(4):                                   # warm-up
+            qmoe.moe_measure_read(bufs[i % nbuf], out, per_cu * cus)
+        for i in range(reps):
+            ev.arm(i)
+            qmoe.moe_measure_read(bufs[(i + 4) % nbuf], out, per_cu * cus)
+        torch.cuda.synchronize()
+        d = ev.seconds("read")
+        gbs = nbytes / d.mean() / 1e9
+        if best is None or gbs > best["GB/s"]:
+            best = {"GB/s": round(float(gbs), 1), "avg_us": round(float(d.mean()) * 1e6, 2), "bytes": nbytes,
+                    "workgroups_per_cu": per_cu}
+    del bufs
+    return best
+
+
+def time_prefill(wl, layer, steps, warmup):
+    """Route, group and the prefill expert FFN of one chunk, K times, launched
+    eagerly (a step is ~1.6 ms, so host launch cost stays out of the way),
+    with dispatch events on the two GEMM kernels."""
+    import torch
+    from bit_quantized_moe_02_amd import qmoe
+    E, H, k, T = wl.n_experts, wl.hidden, wl.top_k, wl.tokens
+    x = torch.from_numpy(synth.activations_bits(wl, T).view(np.int16)).view(torch.bfloat16).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    rws = torch.empty(qmoe.moe_route_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(qmoe.moe_ffn_workspace_bytes(layer.w, T, k, True), dtype=torch.uint8, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    ss = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    gws = torch.zeros(qmoe.moe_group_workspace_bytes(T, k, E), dtype=torch.uint8, device="cuda")
+    kernels = ["prefill_upgate", "prefill_down"]
+    ev = Events(kernels, steps)
+
+    def step(timed):
+        qmoe.moe_route(x, layer.router, layer.bias, T, H, E, k, idx, w, rws)
+        qmoe.moe_group_tokens(idx, T, k, E, off, ss, sp, gws)
+        if timed is not None:
+            ev.arm(timed)
+        qmoe.moe_expert_ffn_prefill(layer.w, x, T, k, idx, w, off, ss, sp, y, ws)
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    I, Is = wl.inter, wl.shared_inter
+    work = {"prefill_upgate": np.full(steps, 2.0 * 2 * (T * k) * I * H + 2.0 * 2 * T * Is * H),
+            "prefill_down": np.full(steps, 2.0 * (T * k) * I * H + 2.0 * T * Is * H)}
+    per = {kn: kernel_stats(ev.seconds(kn), work[kn], 1e12, MFMA_F16_PEAK_TFLOPS) for kn in kernels}
+    dom = max(kernels, key=lambda kn: per[kn]["avg_us"])
+    roof = {"bound": "mfma", "achieved": per[dom]["achieved"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": per[dom]["frac"], "traffic": traffic_of(wl.name, dom), "traffic_unit": "bytes per launch",
+            "kernel": dom, "avg_us": per[dom]["avg_us"], "flops_per_launch": per[dom]["work_per_launch"]}
+    useful = work["prefill_upgate"][0] + work["prefill_down"][0]
+    return {"value": round(steps * T / (t1 - t0), 1), "unit": "tokens/s", "steps": steps, "warmup": warmup,
+            "ms_per_step": round((t1 - t0) * 1e3 / steps, 4), "launch": "eager",
+            "mfma_frac_whole_step": round(useful / ((t1 - t0) / steps) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "roofline": roof, "kernels": per}
+
+
+def traffic_of(workload, kernel):
+    rec = MEASURED_TRAFFIC.get((workload, kernel))
+    if rec is not None and rec[0] == source_digest():
+        return rec[1]
+    return None
+
+
+def decode_config(wl, instances):
+    return {"workload": wl.name, "hidden": wl.hidden, "inter": wl.inter, "experts": wl.n_experts,
+            "top_k": wl.top_k, "shared_inter": wl.shared_inter, "tokens_per_step": wl.tokens,
+            "formats": "/".join(f.upper() for f in wl.fmts), "layer_instances": instances, "launch": "hip_graph",
+            "entry": "moe_layer_decode",
+            "decode_kernels": "single-token, once per token" if wl.tokens <= DEC_PER_TOKEN_MAX else "batched"}
+
+
+def decode_report(wl, res, nb_up, nb_dn, steps, ceilings=None):
+    work = decode_work(wl, res["idx"], nb_up, nb_dn)
+    per = {kn: kernel_stats(res["durs"][kn], work[kn], 1e9, HBM_PEAK_GBS) for kn in res["durs"]}
+    if ceilings:
+        for kn, c in ceilings.items():
+            per[kn]["read_ceiling_GBs"] = c["GB/s"]
+            per[kn]["frac_of_ceiling"] = round(per[kn]["achieved"] / c["GB/s"], 4)
+    return per, work
 
 
 def main():
@@ -206,56 +432,7 @@ def main():
               "the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
-    from bit_quantized_moe_02_amd import qmoe
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    wl = synth.WORKLOADS[args.workload]
-    decode = wl.name in DECODE
-    steps = args.steps if args.steps is not None else (1000 if decode else 20)
-    warmup = args.warmup if args.warmup is not None else (50 if decode else 3)
-    instances = args.instances if args.instances is not None else (4 if decode else 1)
-    E, H, I, Is, k, T = wl.n_experts, wl.hidden, wl.inter, wl.shared_inter, wl.top_k, wl.tokens
-
-    layers, (nb_up, nb_dn) = build_layer(wl, instances)
-    # inputs: one independent draw per step (decode), one chunk (prefill)
-    n_x = min(steps + warmup, wl.steps) if decode else 1
-    xs = torch.stack([torch.from_numpy(synth.activations_bits(wl, T, step=s).view(np.int16)).view(torch.bfloat16)
-                      for s in range(n_x)]).cuda()
-    n_total = steps + warmup
-    idx_all = torch.empty((n_total, T, k), dtype=torch.int32, device="cuda")
-    w_all = torch.empty((n_total, T, k), dtype=torch.float32, device="cuda")
-    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    rws = torch.empty(qmoe.moe_route_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
-    if decode:     # the whole decode step in one call (router, top-k, experts, combine)
-        ws = torch.empty(qmoe.moe_layer_decode_workspace_bytes(layers[0].w, T, k), dtype=torch.uint8, device="cuda")
-    else:
-        ws = torch.empty(qmoe.moe_ffn_workspace_bytes(layers[0].w, T, k, True), dtype=torch.uint8, device="cuda")
-    if not decode:
-        off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-        ss = torch.empty(T * k, dtype=torch.int32, device="cuda")
-        sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
-        gws = torch.zeros(qmoe.moe_group_workspace_bytes(T, k, E), dtype=torch.uint8, device="cuda")
-    kernels = ["decode_upgate", "decode_down"] if decode else ["prefill_upgate", "prefill_down"]
-    ev = {kn: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-          for kn in kernels}
-    for kn in kernels:       # torch creates the HIP event on its first record
-        for a, b in ev[kn]:
-            a.record()
-            b.record()
-
-    def step(s, timed_kernel):
-        layer = layers[s % instances]
-        x = xs[s % n_x]
-        if not decode:
-            qmoe.moe_route(x, layer.router, layer.bias, T, H, E, k, idx_all[s], w_all[s], rws)
-        if timed_kernel is not None:
-            for kn in kernels:
-                qmoe.moe_profile_next_launch(kn, *ev[kn][timed_kernel])
-        if decode:
-            qmoe.moe_layer_decode(layer.w, layer.router, layer.bias, x, T, k, idx_all[s], w_all[s], y, ws)
-        else:
-            qmoe.moe_group_tokens(idx_all[s], T, k, E, off, ss, sp, gws)
-            qmoe.moe_expert_ffn_prefill(layer.w, x, T, k, idx_all[s], w_all[s], off, ss, sp, y, ws)
-
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -264,105 +441,93 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.calibrate_copy} MiB done")
         del src, dst
-    for s in range(warmup):
-        step(s, None)
-    torch.cuda.synchronize()
-    use_graph = decode and not args.eager
-    eager_tps = None
-    if use_graph:
-        # The K timed steps are captured back to back into one HIP graph (each
-        # step: route + expert FFN of its own token, with its own input row,
-        # layer copy and output slots), so host launch overhead -- which a
-        # whole-model decode graph spreads over all its layers -- stays out of
-        # the per-layer figure.  One untimed replay uploads the graph first.
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(steps):
-                step(warmup + i, None)
-        graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        graph.replay()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        if not args.no_kernel_events:
-            # Events recorded inside a graph carry no usable timestamps, so the
-            # kernel durations come from a second timed region: the same K
-            # steps launched one by one, with HIP events around each kernel on
-            # the stream it runs on.
-            te0 = time.perf_counter()
-            for i in range(steps):
-                step(warmup + i, i)
-            torch.cuda.synchronize()
-            eager_tps = steps * T / (time.perf_counter() - te0)
-    else:
-        t0 = time.perf_counter()
-        for i in range(steps):
-            step(warmup + i, None if args.no_kernel_events else i)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / steps
-    tokens_per_s = steps * T / (t1 - t0)
+    name = args.workload
+    head = name == "headline"
+    dname = "decode_b1" if head else name
+    out = None
 
-    # dominant kernel: algorithmic work per launch from the routing each step made
-    idx_h = idx_all[warmup:].cpu().numpy()
-    roof, per_kernel = None, None
-    if not args.no_kernel_events:
-        durs = {kn: np.array([a.elapsed_time(b) for a, b in ev[kn]]) * 1e-3 for kn in kernels}   # s
-        # algorithmic work per launch, from the routing each step made
-        if decode:
-            work = {kn: [] for kn in kernels}
-            for s in range(steps):
-                # up to DEC_PER_TOKEN_MAX tokens the library runs the single-token
-                # kernels once per token and the events time the first token's
-                # launch; beyond, one launch covers the whole batch
-                Tl = 1 if T <= DEC_PER_TOKEN_MAX else T
-                d = len(np.unique(idx_h[s][:Tl]))
-                # up/gate: both matrices of the distinct routed experts + shared, x in, h out
-                work["decode_upgate"].append(d * 2 * nb_up + 2 * Is * H * 2 + Tl * H * 2 + Tl * k * I * 2 + Tl * Is * 2)
-                # down: the distinct routed down matrices + shared, h in, y out
-                work["decode_down"].append(d * nb_dn + H * Is * 2 + Tl * k * I * 2 + Tl * Is * 2 + Tl * H * 4)
-            unit, peak, bound, scale = "GB/s", HBM_PEAK_GBS, "hbm", 1e9
+    if head or name in DECODE:
+        wl = synth.WORKLOADS[dname]
+        steps = args.steps if args.steps is not None else 1000
+        warmup = args.warmup if args.warmup is not None else 50
+        instances = args.instances if args.instances is not None else 4
+        layers, (nb_up, nb_dn) = build_layer(wl, instances)
+        res = time_decode(wl, layers, steps, warmup, wl.name)
+        per, work = decode_report(wl, res, nb_up, nb_dn, steps)
+        dom = max(["decode_upgate", "decode_down"], key=lambda kn: res["durs"][kn].sum())
+        ceil = read_ceiling(per[dom]["work_per_launch"])
+        per[dom]["read_ceiling_GBs"] = ceil["GB/s"]
+        per[dom]["frac_of_ceiling"] = round(per[dom]["achieved"] / ceil["GB/s"], 4)
+        step_us = res["seconds"] / steps * 1e6
+        out = {
+            "metric": METRIC, "value": round(steps * wl.tokens / res["seconds"], 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(step_us * 1e-3, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": decode_config(wl, instances),
+            "roofline": {"bound": "hbm", "achieved": per[dom]["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": per[dom]["frac"], "traffic": traffic_of(wl.name, dom),
+                         "traffic_unit": "bytes per launch", "kernel": dom, "avg_us": per[dom]["avg_us"],
+                         "bytes_per_launch": per[dom]["work_per_launch"],
+                         "read_ceiling": ceil, "frac_of_read_ceiling": per[dom]["frac_of_ceiling"]},
+            "kernels": per,
+            "kernel_timing": {"events": "hipExtLaunchKernel dispatch start/end", "launch": "one by one",
+                              "sum_of_kernel_us": round(sum(float(res["durs"][kn].mean()) for kn in res["durs"]) * 1e6,
+                                                        2),
+                              "graph_step_us": round(step_us, 2),
+                              "eager_tokens_per_s": round(res["eager_tps"], 1)},
+        }
+        if head or wl.shared_inter == 0:
+            # %HBM over the quantized expert bytes alone (no shared expert)
+            if head:
+                wq = synth.WORKLOADS["decode_b1_noshared"]
+                qlayers = [without_shared(l, wl) for l in layers]
+                rq = time_decode(wq, qlayers, steps, warmup, wq.name)
+            else:
+                wq, rq = wl, res
+            wk = decode_work(wq, rq["idx"], nb_up, nb_dn)
+            q = {}
+            for kn, wkey in (("decode_upgate", "quant_upgate"), ("decode_down", "quant_down")):
+                d = rq["durs"][kn]
+                c = read_ceiling(wk[wkey].mean())
+                ach = wk[wkey].sum() / d.sum() / 1e9
+                q[kn] = {"avg_us": round(float(d.mean()) * 1e6, 2), "quantized_bytes": float(wk[wkey].mean()),
+                         "achieved": round(float(ach), 1), "frac": round(float(ach / HBM_PEAK_GBS), 4),
+                         "read_ceiling_GBs": c["GB/s"], "frac_of_ceiling": round(float(ach / c["GB/s"]), 4)}
+            qb = wk["quant_upgate"].sum() + wk["quant_down"].sum()
+            qs = rq["durs"]["decode_upgate"].sum() + rq["durs"]["decode_down"].sum()
+            out["decode_quantized_only"] = {
+                "workload": wq.name, "tokens_per_s": round(steps * wq.tokens / rq["seconds"], 1),
+                "ms_per_step": round(rq["seconds"] / steps * 1e3, 5),
+                "quantized_bytes_per_token": float(qb / steps),
+                "frac_hbm_expert_kernels": round(float(qb / qs / 1e9 / HBM_PEAK_GBS), 4),
+                "kernels": q}
+        if not args.no_cpu_baseline:
+            log("[bench] timing the CPU oracle (decode) ...")
+            out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        del layers
+
+    if head or name in PREFILL:
+        pwl = synth.WORKLOADS["prefill_2048" if head else name]
+        psteps = min(args.steps, 50) if args.steps is not None else 20
+        pwarm = min(args.warmup, 5) if args.warmup is not None else 3
+        players, _ = build_layer(pwl, 1)
+        pre = time_prefill(pwl, players[0], psteps, pwarm)
+        pre["config"] = {"workload": pwl.name, "hidden": pwl.hidden, "inter": pwl.inter, "experts": pwl.n_experts,
+                         "top_k": pwl.top_k, "shared_inter": pwl.shared_inter, "tokens_per_step": pwl.tokens,
+                         "formats": "/".join(f.upper() for f in pwl.fmts)}
+        if not args.no_cpu_baseline:
+            log("[bench] timing the CPU oracle (prefill) ...")
+            pre["cpu_baseline"] = cpu_baseline(pwl, min(args.cpu_seconds, 10.0), max_tokens=6)
+        if head:
+            out[pwl.name] = pre
         else:
-            work = {"prefill_upgate": [2.0 * 2 * (T * k) * I * H + 2.0 * 2 * T * Is * H] * steps,
-                    "prefill_down": [2.0 * (T * k) * I * H + 2.0 * T * Is * H] * steps}
-            unit, peak, bound, scale = "TFLOP/s", MFMA_F16_PEAK_TFLOPS, "mfma", 1e12
-        per_kernel = {}
-        for kn in kernels:
-            w = np.array(work[kn], dtype=np.float64)
-            ach = w.sum() / durs[kn].sum() / scale
-            per_kernel[kn] = {"avg_us": round(float(durs[kn].mean()) * 1e6, 2), "achieved": round(ach, 1),
-                              "frac": round(ach / peak, 4), "work_per_launch": float(w.mean())}
-        dom = max(kernels, key=lambda kn: durs[kn].sum())
-        traffic = None
-        rec = MEASURED_TRAFFIC.get((wl.name, dom))
-        if rec is not None and rec[0] == source_digest("decode" if decode else "prefill"):
-            traffic = rec[1]
-        roof = {"bound": bound, "achieved": per_kernel[dom]["achieved"], "peak": peak, "unit": unit,
-                "frac": per_kernel[dom]["frac"], "traffic": traffic, "traffic_unit": "bytes per launch",
-                "kernel": dom,
-                "avg_us": per_kernel[dom]["avg_us"],
-                ("bytes_per_launch" if decode else "flops_per_launch"): per_kernel[dom]["work_per_launch"]}
-
-    out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": wl.name, "hidden": H, "inter": I, "experts": E, "top_k": k, "shared_inter": Is,
-                   "tokens_per_step": T, "formats": "/".join(f.upper() for f in wl.fmts),
-                   "layer_instances": instances, "launch": "hip_graph" if use_graph else "eager",
-                   **({"entry": "moe_layer_decode",
-                       "decode_kernels": "single-token, once per token" if T <= DEC_PER_TOKEN_MAX else "batched"}
-                      if decode else {})},
-        "roofline": roof,
-        "kernels": per_kernel,
-        "kernel_events_pass": None if per_kernel is None else {
-            "launch": "eager" if use_graph else "same as timed region",
-            "tokens_per_s": None if eager_tps is None else round(eager_tps, 1)},
-    }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle ...")
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+            out = {"metric": METRIC, "value": pre["value"], "unit": "tokens/s", "n_gpus": 1, "steps": psteps,
+                   "warmup": pwarm, "ms_per_step": pre["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+                   "vs_baseline": None, "dtype": "f16", "data": "synthetic", "config": pre.pop("config"),
+                   "roofline": pre["roofline"], "kernels": pre["kernels"],
+                   "mfma_frac_whole_step": pre["mfma_frac_whole_step"]}
+            if "cpu_baseline" in pre:
+                out["cpu_baseline"] = pre["cpu_baseline"]
     print(json.dumps(out), flush=True)
 
 

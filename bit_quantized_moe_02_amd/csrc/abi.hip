@@ -511,7 +511,7 @@ extern "C" int moe_profile_next_launch(int kernel_id, void* start_event, void* s
     hk.n = 0;
     return MOE_OK;
   }
-  if (kernel_id < MOE_KERNEL_ROUTE_LOGITS || kernel_id > MOE_KERNEL_PREFILL_COMBINE)
+  if (kernel_id < MOE_KERNEL_ROUTE_LOGITS || kernel_id > MOE_KERNEL_READ)
     return fail(MOE_ERR_INVALID_ARG, "moe_profile_next_launch: unknown kernel id");
   if (!start_event || !stop_event) return fail(MOE_ERR_INVALID_ARG, "moe_profile_next_launch: NULL event");
   if (hk.n >= ProfileHook::kMax) return fail(MOE_ERR_INVALID_ARG, "moe_profile_next_launch: too many pending");
@@ -535,3 +535,13 @@ extern "C" int moe_debug_dequant(int fmt, const void* packed, int64_t rows, int6
   return MOE_OK;
 }
 
+extern "C" int moe_measure_read(const void* src, size_t bytes, uint32_t* out, int blocks, void* stream) {
+  clear_error();
+  if (!src || !out) return fail(MOE_ERR_INVALID_ARG, "moe_measure_read: NULL pointer");
+  if (!aligned16(src) || bytes == 0 || bytes % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_measure_read: src must be 16-byte aligned and bytes a positive multiple of 16");
+  if (blocks < 0 || blocks > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "moe_measure_read: blocks out of range");
+  hipError_t e = launch_read(src, bytes, out, blocks > 0 ? blocks : 4 * n_cus(), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("moe_measure_read", e);
+  return MOE_OK;
+}

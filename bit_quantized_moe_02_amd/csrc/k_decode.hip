@@ -470,7 +470,7 @@ hipError_t launch_dec_upgate(const DecArgs& a, int fmt, int cpw, int grid, hipSt
   else fn = cpw == 1 ? dec_upgate_kernel<MOE_FMT_K4, 1> : dec_upgate_kernel<MOE_FMT_K4, 2>;
   hipError_t err = ensure_dyn_lds((const void*)fn);
   if (err != hipSuccess) return err;
-  return launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] { hipLaunchKernelGGL(fn, dim3(grid), block, lds, s, a); });
+  return launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) { hipExtLaunchKernelGGL(fn, dim3(grid), block, lds, s, ev0_, ev1_, 0, a); });
 }
 
 hipError_t launch_dec_down(const DecArgs& a, int fmt, int grid, hipStream_t s) {
@@ -479,14 +479,14 @@ hipError_t launch_dec_down(const DecArgs& a, int fmt, int grid, hipStream_t s) {
   hipError_t err = ensure_dyn_lds((const void*)fn);
   if (err != hipSuccess) return err;
   return launch_timed(MOE_KERNEL_DECODE_DOWN, s,
-                      [&] { hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * a.nw_dn), lds, s, a); });
+                      [&](hipEvent_t ev0_, hipEvent_t ev1_) { hipExtLaunchKernelGGL(fn, dim3(grid), dim3(64 * a.nw_dn), lds, s, ev0_, ev1_, 0, a); });
 }
 
 hipError_t launch_combine(const DecArgs& a, const int32_t* topk_idx, const float* topk_w, float* y,
                           hipStream_t s) {
   const int64_t n = (int64_t)a.T * a.H;
-  return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&] {
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.ybuf,
+  return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+    hipExtLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ev0_, ev1_, 0, a.ybuf,
                        a.Is > 0 ? a.ysh : nullptr, topk_idx, topk_w, a.xexp, a.T, a.k, a.H, a.E, y);
   });
 }

@@ -1195,8 +1195,8 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* to
     err = ensure_dyn_lds((const void*)dec1_k4_upgate_kernel);
     if (err != hipSuccess) return err;
     const size_t lds = dec1_k4_upgate_lds(a.H, nw);
-    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
-      hipLaunchKernelGGL(dec1_k4_upgate_kernel, dim3(grid), dim3(64 * nw), lds, s, a);
+    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+      hipExtLaunchKernelGGL(dec1_k4_upgate_kernel, dim3(grid), dim3(64 * nw), lds, s, ev0_, ev1_, 0, a);
     });
   } else if (fmt_ug == MOE_FMT_CB2 && n_chunks <= 16) {
     const int nw = n_chunks < 4 ? 4 : n_chunks;
@@ -1208,8 +1208,8 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* to
     err = ensure_dyn_lds((const void*)fk);
     if (err != hipSuccess) return err;
     const size_t lds = dec1_cb2_upgate_lds(nw, route);
-    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
-      hipLaunchKernelGGL(fk, dim3(grid), dim3(64 * nw), lds, s, a);
+    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+      hipExtLaunchKernelGGL(fk, dim3(grid), dim3(64 * nw), lds, s, ev0_, ev1_, 0, a);
     });
   } else {
     // CB2 with 17 to 32 K-chunks (K4 layers take dec1_k4_upgate_kernel at every H)
@@ -1220,8 +1220,8 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* to
     err = ensure_dyn_lds((const void*)dec1_cb2_wide_upgate_kernel);
     if (err != hipSuccess) return err;
     const size_t lds_ug = dec1_cb2_wide_upgate_lds(nw_ug);
-    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
-      hipLaunchKernelGGL(dec1_cb2_wide_upgate_kernel, dim3(grid_ug), dim3(64 * nw_ug), lds_ug, s, a);
+    err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+      hipExtLaunchKernelGGL(dec1_cb2_wide_upgate_kernel, dim3(grid_ug), dim3(64 * nw_ug), lds_ug, s, ev0_, ev1_, 0, a);
     });
   }
   if (err != hipSuccess) return err;
@@ -1233,8 +1233,8 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* to
   err = ensure_dyn_lds((const void*)fd);
   if (err != hipSuccess) return err;
   const size_t lds_dn = dec1_down_lds(a, fmt_dn, nw_dn);
-  return launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&] {
-    hipLaunchKernelGGL(fd, dim3(a.H / 16), dim3(64 * nw_dn), lds_dn, s, a, topk_w, y);
+  return launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+    hipExtLaunchKernelGGL(fd, dim3(a.H / 16), dim3(64 * nw_dn), lds_dn, s, ev0_, ev1_, 0, a, topk_w, y);
   });
 }
 

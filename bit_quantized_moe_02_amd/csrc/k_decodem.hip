@@ -529,18 +529,18 @@ hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus,
   if (nw_ug > 16 || nw_dn > 8) return hipErrorInvalidValue;   // H <= 4096, I and I_s <= 2048
   hipError_t err = ensure_dyn_lds((const void*)decm_upgate_kernel);
   if (err != hipSuccess) return err;
-  err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&] {
-    hipLaunchKernelGGL(decm_upgate_kernel, dim3(cus), dim3(64 * nw_ug), decm_upgate_lds(nw_ug), s, a);
+  err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+    hipExtLaunchKernelGGL(decm_upgate_kernel, dim3(cus), dim3(64 * nw_ug), decm_upgate_lds(nw_ug), s, ev0_, ev1_, 0, a);
   });
   if (err != hipSuccess) return err;
   err = ensure_dyn_lds((const void*)decm_down_kernel);
   if (err != hipSuccess) return err;
-  err = launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&] {
-    hipLaunchKernelGGL(decm_down_kernel, dim3(cus), dim3(64 * nw_dn), decm_down_lds(a, nw_dn), s, a);
+  err = launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+    hipExtLaunchKernelGGL(decm_down_kernel, dim3(cus), dim3(64 * nw_dn), decm_down_lds(a, nw_dn), s, ev0_, ev1_, 0, a);
   });
   if (err != hipSuccess) return err;
-  return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&] {
-    hipLaunchKernelGGL(decm_combine_kernel, dim3((unsigned)a.T), dim3(256), 0, s, a.ybuf, a.Is > 0 ? a.ysh : nullptr,
+  return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+    hipExtLaunchKernelGGL(decm_combine_kernel, dim3((unsigned)a.T), dim3(256), 0, s, ev0_, ev1_, 0, a.ybuf, a.Is > 0 ? a.ysh : nullptr,
                        a.topk_idx, topk_w, a.xexp, a.k, a.H, a.E, y);
   });
 }

@@ -202,9 +202,42 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* topk_idx, in
   if (lane == 0 && bad) atomicAdd(err_count, bad);
 }
 
+// Streaming read of n16 16-byte vectors: each is loaded once, coalesced, with
+// kReadUnroll loads in flight per thread, and the XOR of every word goes to
+// *out (an integer XOR: order-independent) so no load can be dropped.  A
+// plain HBM-bound kernel whose rate is the measured ceiling of the
+// bandwidth-bound decode kernels at the same byte count.
+constexpr int kReadUnroll = 8;
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* src, int64_t n16, uint32_t* out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+  if ((threadIdx.x & 63) == 0 && acc) atomicXor(out, acc);
+}
+
 }  // namespace
 
 namespace qmoe {
+
+hipError_t launch_read(const void* src, size_t bytes, uint32_t* out, int blocks, hipStream_t s) {
+  return launch_timed(MOE_KERNEL_READ, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+    hipExtLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, s, ev0_, ev1_, 0, (const u32x4*)src,
+                          (int64_t)(bytes / 16), out);
+  });
+}
 
 hipError_t launch_dequant(int fmt, const uint8_t* packed, int64_t rows, int64_t kp, const int8_t* codebook,
                           float* out, hipStream_t s) {
@@ -234,8 +267,8 @@ hipError_t launch_group(const int32_t* topk_idx, int n_slots, int E, int32_t* of
   const size_t lds = group_lds(E);
   hipError_t err = ensure_dyn_lds((const void*)group_kernel);
   if (err != hipSuccess) return err;
-  return launch_timed(MOE_KERNEL_GROUP, s, [&] {
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(64 * kGroupWaves), lds, s, topk_idx, n_slots, E, offsets,
+  return launch_timed(MOE_KERNEL_GROUP, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+    hipExtLaunchKernelGGL(group_kernel, dim3(1), dim3(64 * kGroupWaves), lds, s, ev0_, ev1_, 0, topk_idx, n_slots, E, offsets,
                        sorted_slots, slot_pos, err_count);
   });
 }

@@ -857,7 +857,7 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
     hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
     err = launch_timed(MOE_KERNEL_PREFILL_UPGATE, s,
-                       [&] { hipLaunchKernelGGL(fn, grid, dim3(64 * kUgWaves), lds, s, a); });
+                       [&](hipEvent_t ev0_, hipEvent_t ev1_) { hipExtLaunchKernelGGL(fn, grid, dim3(64 * kUgWaves), lds, s, ev0_, ev1_, 0, a); });
     if (err != hipSuccess) return err;
   }
   {
@@ -866,11 +866,11 @@ hipError_t launch_prefill(const PfArgs& a, int fmt_ug, int fmt_dn, const float* 
     hipError_t err = ensure_dyn_lds((const void*)fn);
     if (err != hipSuccess) return err;
     err = launch_timed(MOE_KERNEL_PREFILL_DOWN, s,
-                       [&] { hipLaunchKernelGGL(fn, grid, dim3(64 * kDnWaves), (size_t)kStageBytes, s, a); });
+                       [&](hipEvent_t ev0_, hipEvent_t ev1_) { hipExtLaunchKernelGGL(fn, grid, dim3(64 * kDnWaves), (size_t)kStageBytes, s, ev0_, ev1_, 0, a); });
     if (err != hipSuccess) return err;
   }
-  return launch_timed(MOE_KERNEL_PREFILL_COMBINE, s, [&] {
-    hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)a.T), dim3(256), 0, s, a.yslot,
+  return launch_timed(MOE_KERNEL_PREFILL_COMBINE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
+    hipExtLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)a.T), dim3(256), 0, s, ev0_, ev1_, 0, a.yslot,
                        a.Is > 0 ? a.ysh : nullptr, a.slot_pos, topk_w, a.xexp, a.T, a.k, a.H, y);
   });
 }

@@ -282,12 +282,12 @@ int route_logit_parts(int T, int) { return T > 16 ? kLogitSplit : 1; }
 hipError_t launch_route_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H, int E,
                                float* logits, hipStream_t s) {
   const int n_parts = std::min(kMaxLogitParts, (H + 511) / 512);
-  return launch_timed(MOE_KERNEL_ROUTE_LOGITS, s, [&] {
+  return launch_timed(MOE_KERNEL_ROUTE_LOGITS, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
     if (T <= 16) {
-      hipLaunchKernelGGL(logits_small_kernel, dim3(E), dim3(64 * n_parts), 0, s, x, wr, bias, T, H, E, logits);
+      hipExtLaunchKernelGGL(logits_small_kernel, dim3(E), dim3(64 * n_parts), 0, s, ev0_, ev1_, 0, x, wr, bias, T, H, E, logits);
     } else {
       const int blocks = (E + kLbE - 1) / kLbE * ((T + kLbT - 1) / kLbT) * kLogitSplit;
-      hipLaunchKernelGGL(logits_bf16x3_kernel, dim3(blocks), dim3(256), 0, s, x, wr, bias, T, H, E, kLogitSplit,
+      hipExtLaunchKernelGGL(logits_bf16x3_kernel, dim3(blocks), dim3(256), 0, s, ev0_, ev1_, 0, x, wr, bias, T, H, E, kLogitSplit,
                          logits);
     }
   });
@@ -306,11 +306,11 @@ hipError_t launch_route_topk(const float* logits, int n_parts, int T, int E, int
       : nq <= 4 ? (split ? topk_kernel<4, kLogitSplit> : topk_kernel<4, 1>)
       : nq <= 8 ? (split ? topk_kernel<8, kLogitSplit> : topk_kernel<8, 1>)
                 : (split ? topk_kernel<16, kLogitSplit> : topk_kernel<16, 1>);
-  return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&] {
+  return launch_timed(MOE_KERNEL_ROUTE_TOPK, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
     if (T <= 16 && n_parts == 1)
-      hipLaunchKernelGGL(topk_rank_kernel, dim3(T), dim3(kTopkRankThreads), 0, s, logits, E, k, topk_idx, topk_w);
+      hipExtLaunchKernelGGL(topk_rank_kernel, dim3(T), dim3(kTopkRankThreads), 0, s, ev0_, ev1_, 0, logits, E, k, topk_idx, topk_w);
     else
-      hipLaunchKernelGGL(fk, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), 0, s, logits, T, E, k,
+      hipExtLaunchKernelGGL(fk, dim3((T + kTopkWaves - 1) / kTopkWaves), dim3(64 * kTopkWaves), 0, s, ev0_, ev1_, 0, logits, T, E, k,
                          topk_idx, topk_w);
   });
 }

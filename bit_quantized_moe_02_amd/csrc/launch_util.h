@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <mutex>
 #include <set>
@@ -26,8 +27,13 @@ inline hipError_t ensure_dyn_lds(const void* fn) {
   return e;
 }
 
+// Runs launch(start, stop): the launch passes the two events to
+// hipExtLaunchKernel, which records the kernel dispatch's own start and end
+// times in them (null events: a plain launch).  The events come from a
+// pending moe_profile_next_launch request for this kernel, which is consumed.
 template <typename F>
 hipError_t launch_timed(int kernel_id, hipStream_t s, F&& launch) {
+  (void)s;
   ProfileHook& hk = profile_hook();
   int slot = -1;
   for (int i = 0; i < hk.n; ++i)
@@ -35,11 +41,10 @@ hipError_t launch_timed(int kernel_id, hipStream_t s, F&& launch) {
       slot = i;
       break;
     }
-  void* stop = nullptr;
+  hipEvent_t start = nullptr, stop = nullptr;
   if (slot >= 0) {
-    hipError_t e = hipEventRecord((hipEvent_t)hk.start[slot], s);
-    if (e != hipSuccess) return e;
-    stop = hk.stop[slot];
+    start = (hipEvent_t)hk.start[slot];
+    stop = (hipEvent_t)hk.stop[slot];
     for (int i = slot + 1; i < hk.n; ++i) {   // consume the entry
       hk.kernel_id[i - 1] = hk.kernel_id[i];
       hk.start[i - 1] = hk.start[i];
@@ -47,10 +52,8 @@ hipError_t launch_timed(int kernel_id, hipStream_t s, F&& launch) {
     }
     --hk.n;
   }
-  launch();
-  hipError_t e = hipGetLastError();
-  if (stop && e == hipSuccess) e = hipEventRecord((hipEvent_t)stop, s);
-  return e;
+  launch(start, stop);
+  return hipGetLastError();
 }
 
 }  // namespace qmoe

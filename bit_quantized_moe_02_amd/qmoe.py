@@ -37,12 +37,13 @@ EXPORTED = [
     "moe_group_tokens", "moe_ffn_workspace_bytes", "moe_expert_ffn_decode",
     "moe_expert_ffn_prefill", "moe_layer_decode_workspace_bytes", "moe_layer_decode",
     "moe_debug_dequant", "moe_profile_next_launch", "moe_last_error", "moe_layer_decode_noalloc",
+    "moe_measure_read",
 ]
 MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 MOE_KERNEL = {"route_logits": 0, "route_topk": 1, "decode_upgate": 2, "decode_down": 3,
               "decode_combine": 4, "group": 5, "prefill_upgate": 6, "prefill_down": 7,
-              "prefill_combine": 8}
+              "prefill_combine": 8, "read": 9}
 
 
 class QmoeError(RuntimeError):
@@ -90,6 +91,7 @@ def _load():
                                                     vp]),
         "moe_debug_dequant": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp, vp]),
         "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, vp, vp]),
+        "moe_measure_read": (ctypes.c_int, [vp, sz, vp, ctypes.c_int, vp]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -256,6 +258,12 @@ def moe_profile_next_launch(kernel, start_event, stop_event):
     kid = MOE_KERNEL.get(kernel, kernel)
     ev = lambda e: None if e is None else (e.cuda_event if hasattr(e, "cuda_event") else e)
     _check(lib.moe_profile_next_launch(kid, ev(start_event), ev(stop_event)))
+
+
+def moe_measure_read(src, out, blocks=0, stream=None):
+    """Streaming read of the whole uint8 device tensor `src`; XOR of its words into out (int32 [1])."""
+    _check(lib.moe_measure_read(_dev(src, "src", torch.uint8), src.numel(), _dev(out, "out", torch.int32, 1),
+                                blocks, _stream(stream)))
 
 
 def moe_last_error() -> str:

@@ -314,16 +314,28 @@ int moe_debug_dequant(int fmt, const void* packed, int64_t rows, int64_t k,
 #define MOE_KERNEL_PREFILL_UPGATE 6
 #define MOE_KERNEL_PREFILL_DOWN 7
 #define MOE_KERNEL_PREFILL_COMBINE 8
+#define MOE_KERNEL_READ 9
 
 /* Makes the next launch of kernel `kernel_id` by this thread record the HIP
  * events start_event / stop_event (hipEvent_t as void*, owned by the caller)
- * on its stream immediately before and after itself, so that
- * hipEventElapsedTime gives that one kernel's duration.  Up to 8 requests
+ * at the start and the end of that kernel's execution (hipExtLaunchKernel's
+ * dispatch events), so that hipEventElapsedTime gives that one kernel's
+ * duration.  Up to 8 requests
  * (for different or repeated ids) can be pending; each is consumed by the
  * next launch of its kernel.  kernel_id -1 drops all pending requests.
  * Returns MOE_ERR_INVALID_ARG for an unknown id, NULL events or more than 8
  * pending requests. */
 int moe_profile_next_launch(int kernel_id, void* start_event, void* stop_event);
+
+/* Measurement: reads `bytes` of device memory at src once (16-byte vectors,
+ * coalesced, streaming) with `blocks` workgroups of 256 threads (0: four per
+ * compute unit) and XORs every 32-bit word into *out (device uint32, not
+ * reset: zero it first to read the XOR of the buffer).  Its rate is the
+ * measured ceiling that the bandwidth-bound decode kernels are compared with
+ * at the same byte count (kernel id MOE_KERNEL_READ for
+ * moe_profile_next_launch).  src 16-byte aligned, bytes a positive multiple
+ * of 16; MOE_ERR_INVALID_ARG otherwise. */
+int moe_measure_read(const void* src, size_t bytes, uint32_t* out, int blocks, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* moe_last_error(void);
