@@ -93,6 +93,7 @@ def parse():
     p.add_argument("--instances", type=int, default=None,
                    help="layer copies rotated over the decode steps (default 4 for decode, 1 for prefill)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--skip-prefill", action="store_true", help="headline: decode parts only")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="also run one elementwise pass (torch.neg) over MIB MiB: a kernel of known "
@@ -506,7 +507,7 @@ def main():
             out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
         del layers
 
-    if head or name in PREFILL:
+    if (head and not args.skip_prefill) or name in PREFILL:
         pwl = synth.WORKLOADS["prefill_2048" if head else name]
         psteps = min(args.steps, 50) if args.steps is not None else 20
         pwarm = min(args.warmup, 5) if args.warmup is not None else 3

@@ -64,6 +64,7 @@ int check_weights(const moe_weights* w, Geometry* g, const char* fn) {
   if (!aligned16(w->up) || !aligned16(w->gate) || !aligned16(w->down))
     return fail(MOE_ERR_INVALID_ARG, f + ": expert weights must be 16-byte aligned");
   if (cb2 && !w->codebook) return fail(MOE_ERR_INVALID_ARG, f + ": CB2 weights need the codebook");
+  if (cb2 && !aligned16(w->codebook)) return fail(MOE_ERR_INVALID_ARG, f + ": the codebook must be 16-byte aligned");
   if (w->shared_inter > 0) {
     if (!w->shared_up || !w->shared_gate || !w->shared_down)
       return fail(MOE_ERR_INVALID_ARG, f + ": shared expert pointer is NULL");

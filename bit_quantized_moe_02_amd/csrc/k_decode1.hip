@@ -56,6 +56,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Streaming weight loads: non-temporal (each weight byte is read once).
+__device__ __forceinline__ u32x4 bload16_nt(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
@@ -300,8 +307,9 @@ __device__ __forceinline__ void cb2_pay_load(Cb2Pay& p, const DecArgs& a, int e,
   const size_t t_off = (size_t)e * a.expert_bytes + ((size_t)rt * n_chunks + chunk) * kCb2Tile;
   for (int mat = 0; mat < 2; ++mat) {
     const uint8_t* tile = (mat ? a.gate : a.up) + t_off;
-    p.code[mat] = load16(tile + 16 * lane);
-    const uint2 sp = *reinterpret_cast<const uint2*>(tile + 1024 + 16 * n + 8 * (g & 1));
+    p.code[mat] = load16_nt(tile + 16 * lane);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 sp = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + 1024 + 16 * n + 8 * (g & 1)));
     p.sc[mat][0] = sp.x;
     p.sc[mat][1] = sp.y;
   }
@@ -358,12 +366,6 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
     for (int i = 0; i < 4; ++i) cbv[i] = cbp[i];
   }
   const u32x4 xr = load16(a.x + chunk * 256 + (m & 7) * 32 + qq * 8);    // used by lanes m < 8
-  {
-    // the token's exponent: each wave's largest field, combined after the
-    // first barrier below
-    const uint32_t ef = wave_max_u32(active ? bf16x8_max_efield(xr) : 0u);
-    if (lane == 0) xef[wave] = ef;
-  }
 
   // shared half tile loads: 2 matrices x 4 k-block pairs (zeros when the
   // workgroup has no shared item)
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
       const uint8_t* tile = valid ? (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kBf16Tile
                                   : reinterpret_cast<const uint8_t*>(a.x);
       const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kBf16Tile : 0);
-      for (int p = 0; p < 4; ++p) sraw[mat][p] = bload16(rs, 1024 * (2 * p + (n >> 3)) + 16 * (16 * qq + r));
+      for (int p = 0; p < 4; ++p) sraw[mat][p] = bload16_nt(rs, 1024 * (2 * p + (n >> 3)) + 16 * (16 * qq + r));
     }
   };
   issue_shared(s_lo, s_lo < s_hi);
@@ -429,6 +431,13 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
     }
   };
   issue(P0, r_lo);
+  {
+    // the token's exponent: each wave's largest field, combined after the
+    // next barrier (computed only now: its wait for x must not come before
+    // the weight loads are issued)
+    const uint32_t ef = wave_max_u32(active ? bf16x8_max_efield(xr) : 0u);
+    if (lane == 0) xef[wave] = ef;
+  }
 
   // decode table, two steps: the 4 fp16 values of each (idx, half) pair
   // into a staging area, then the 16 sign variants of each, written by

@@ -119,16 +119,6 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   int8_t cbv[4] = {0, 0, 0, 0};
   if (tid < 512)
     for (int i = 0; i < 4; ++i) cbv[i] = a.codebook[(tid >> 1) * 8 + 4 * (tid & 1) + i];
-  {
-    // each token's exponent: the wave's largest field of row m (the 4 lanes
-    // qq of row m), combined over the waves after a barrier below
-    uint32_t ef = 0;
-    for (int kb = 0; kb < 8; ++kb) ef = max(ef, bf16x8_max_efield(xr[kb]));
-    if (!active) ef = 0;
-    ef = max(ef, (uint32_t)__shfl_xor((int)ef, 16));
-    ef = max(ef, (uint32_t)__shfl_xor((int)ef, 32));
-    if (lane < 16) xef[wave * 16 + lane] = ef;
-  }
 
   build_expert_list(a.topk_idx, T * k, k, a.E, L);
   const int64_t n_r = (int64_t)L->n * n_rt;
@@ -159,6 +149,17 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   };
   UgPayM P0, P1, P2;
   if (hi > n_rts) issue(P0);
+  {
+    // each token's exponent: the wave's largest field of row m (the 4 lanes
+    // qq of row m), combined over the waves after the next barrier (computed
+    // only now: its wait for x must not come before the first weight loads)
+    uint32_t ef = 0;
+    for (int kb = 0; kb < 8; ++kb) ef = max(ef, bf16x8_max_efield(xr[kb]));
+    if (!active) ef = 0;
+    ef = max(ef, (uint32_t)__shfl_xor((int)ef, 16));
+    ef = max(ef, (uint32_t)__shfl_xor((int)ef, 32));
+    if (lane < 16) xef[wave * 16 + lane] = ef;
+  }
 
   // CB2 table (the pair values staged in the reduction area)
   uint2* val4 = reinterpret_cast<uint2*>(red);
