@@ -16,6 +16,7 @@ Functions, in the order a layer uses them:
   codebook(seed)                 SplitMix64 table of 256 signed 8-vectors
   cb2_quantize / cb2_dequantize  2-bit codebook format (CB2)
   kq_quantize / kq_dequantize    K-quant super-block formats (K2, K4)
+  q8_quantize / q8_dequantize    8-bit blocks of 32 (Q8, shared expert)
   pack_* / unpack_*              byte layout of the 16x256 weight tiles
   route                          softmax over experts, top-k, renormalize
   group                          stable grouping of (token, slot) by expert
@@ -38,6 +39,7 @@ import numpy as np
 __all__ = [
     "splitmix64", "codebook", "f16", "bf16_round", "f32_round",
     "cb2_quantize", "cb2_dequantize", "kq_params", "kq_quantize", "kq_dequantize",
+    "q8_quantize", "q8_dequantize",
     "quantize_matrix", "dequantize_matrix", "pack_matrix", "unpack_matrix",
     "tile_bytes", "packed_bytes", "route", "group", "silu", "expert_ffn",
     "moe_layer", "dense_ffn", "cb2_search_numpy", "cb2_search",
@@ -290,6 +292,40 @@ def kq_dequantize(f: dict, fmt: str) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Q8: the 8-bit format the pages keep for shared-expert tensors (upppp.jp
+# article, "asymmetric 2-bit quantization": shared experts, projections and
+# the output layer stay at Q8_0 or F16; osrepos summary, the "Q8Shared" model
+# file name).  Blocks of 32 consecutive weights along K, one signed code q
+# per weight and one fp16 scale d per block: weight = d * q.
+# Readings (the pages name the format only): d = fp16(max|w| / 127) (fp64
+# quotient, one rounding to fp16); q = sign(w) * min(127, floor(|w|/d + 1/2))
+# with the quotient in fp64, i.e. the nearest code, ties away from zero,
+# clamped to the symmetric range -127..127 (q = 0 when d = 0).
+
+
+def q8_quantize(w: np.ndarray) -> dict:
+    """Quantize fp32 rows [R, K] (K % 32 == 0) to Q8 fields:
+    q int8 [R, K], d fp64 [R, K/32] (fp16 values)."""
+    w = np.asarray(w, dtype=np.float32)
+    R, K = w.shape
+    assert K % 32 == 0
+    x = w.astype(np.float64).reshape(R, K // 32, 32)
+    d = f16(np.abs(x).max(axis=2) / 127.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        mag = np.where(d[..., None] == 0, 0.0,
+                       np.minimum(127.0, np.floor(np.abs(x) / d[..., None] + 0.5)))
+    q = np.where(x < 0, -mag, mag)
+    return {"q": q.reshape(R, K).astype(np.int8), "d": d}
+
+
+def q8_dequantize(f: dict) -> np.ndarray:
+    """Q8 fields -> fp64 [R, K] holding d*q (exact: an 11-bit significand
+    times a 7-bit integer, so also exact in fp32)."""
+    q = f["q"].astype(np.float64)
+    return q * np.repeat(f["d"], 32, axis=1)
+
+
+# ---------------------------------------------------------------------------
 # Whole matrices (rows = output features, K = reduction dimension).
 
 
@@ -311,6 +347,8 @@ def quantize_matrix(fmt: str, w: np.ndarray, table: np.ndarray | None = None) ->
         f = cb2_quantize(w, table)
     elif fmt in ("k2", "k4"):
         f = kq_quantize(w, fmt)
+    elif fmt == "q8":
+        f = q8_quantize(w)
     elif fmt == "bf16":
         v = w.astype(np.float64)
         assert np.array_equal(bf16_round(v), v), "bf16 format takes bf16 values"
@@ -328,6 +366,8 @@ def dequantize_matrix(f: dict, table: np.ndarray | None = None, k: int | None = 
         w = cb2_dequantize(f, table)
     elif fmt in ("k2", "k4"):
         w = kq_dequantize(f, fmt)
+    elif fmt == "q8":
+        w = q8_dequantize(f)
     else:
         w = f["w"]
     return w if k is None else w[:, :k]
@@ -341,7 +381,7 @@ def dequantize_matrix(f: dict, table: np.ndarray | None = None, k: int | None = 
 # (n, kb, qq, j=0..7) of every kb.  The tile sizes and field orders are the
 # ones include/qmoe.h defines.
 
-TILE_BYTES = {"cb2": 1280, "k2": 1344, "k4": 2304, "bf16": 8192}
+TILE_BYTES = {"cb2": 1280, "k2": 1344, "k4": 2304, "bf16": 8192, "q8": 4352}
 
 
 def tile_bytes(fmt: str) -> int:
@@ -434,6 +474,17 @@ def pack_matrix(f: dict) -> np.ndarray:
         dd = np.moveaxis(dd.reshape(R // 16, 16, K // 256, 2), 2, 1).astype("<u2")
         dd = dd.view(np.uint8).reshape(R // 16, K // 256, 64)
         return np.concatenate([qb, scb, dd], axis=2)
+    if fmt == "q8":
+        q = f["q"].astype(np.int8)
+        R, K = q.shape
+        lanes = _lanes(q, R, K)                                      # [.., 64, kb, j]
+        # 16-byte piece i of a lane holds k-blocks a and a + 2, a = 4*(i % 2) + i // 2
+        pieces = np.stack([np.concatenate([lanes[..., a, :], lanes[..., a + 2, :]], axis=-1)
+                           for a in (0, 4, 1, 5)], axis=2)           # [.., piece, 64, 16]
+        qb = pieces.view(np.uint8).reshape(R // 16, K // 256, 4096)
+        sc = _f16_bits(f["d"]).reshape(R // 16, 16, K // 256, 8)
+        sc = np.moveaxis(sc, 2, 1).astype("<u2").view(np.uint8).reshape(R // 16, K // 256, 256)
+        return np.concatenate([qb, sc], axis=2)
     if fmt == "bf16":
         w = f["w"]
         R, K = w.shape
@@ -493,6 +544,15 @@ def unpack_matrix(fmt: str, packed: np.ndarray, rows: int, k: int) -> dict:
         return {"fmt": fmt, "q": q, "sc": vals[..., :8].reshape(R, K // 32),
                 "m": vals[..., 8:].reshape(R, K // 32),
                 "d": _f16_from_bits(dd[..., 0]), "dmin": _f16_from_bits(dd[..., 1])}
+    if fmt == "q8":
+        pieces = t[..., :4096].copy().view(np.int8).reshape(R // 16, K // 256, 4, 64, 16)
+        q = np.zeros((R // 16, K // 256, 64, 8, 8), dtype=np.int8)
+        for i, a in enumerate((0, 4, 1, 5)):
+            q[..., a, :] = pieces[:, :, i, :, :8]
+            q[..., a + 2, :] = pieces[:, :, i, :, 8:]
+        sc = t[..., 4096:].copy().view("<u2").reshape(R // 16, K // 256, 16, 8)
+        sc = np.moveaxis(sc, 1, 2).reshape(R, K // 32)
+        return {"fmt": fmt, "q": _unlanes(q, R, K), "d": _f16_from_bits(sc)}
     if fmt == "bf16":
         b = t.copy().view("<u2").reshape(R // 16, K // 256, 8, 64, 8)   # kb, lane, j
         b = np.moveaxis(b, 2, 3)                                         # lane, kb, j

@@ -47,7 +47,18 @@ MUTATIONS = {
     "kq_dequant_no_f32_rounding": ("out = f32_round(dscq - dm)", "out = dscq - dm"),
     "kq_dequant_scale_per_superblock": ("sc = np.repeat(f[\"sc\"].astype(np.float64), B, axis=1)",
                                         "sc = np.repeat(f[\"sc\"].astype(np.float64)[:, ::-1], B, axis=1)"),
+    # Q8
+    "q8_scale_divisor": ("d = f16(np.abs(x).max(axis=2) / 127.0)", "d = f16(np.abs(x).max(axis=2) / 128.0)"),
+    "q8_ties_to_even": ("np.minimum(127.0, np.floor(np.abs(x) / d[..., None] + 0.5)))",
+                        "np.minimum(127.0, np.rint(np.abs(x) / d[..., None])))"),
+    "q8_truncated_codes": ("np.minimum(127.0, np.floor(np.abs(x) / d[..., None] + 0.5)))",
+                           "np.minimum(127.0, np.floor(np.abs(x) / d[..., None])))"),
+    "q8_clamp_128": ("np.minimum(127.0, np.floor(np.abs(x) / d[..., None] + 0.5)))",
+                     "np.minimum(128.0, np.floor(np.abs(x) / d[..., None] + 0.5)))"),
+    "q8_sign_dropped": ("q = np.where(x < 0, -mag, mag)", "q = mag"),
+    "q8_dequant_block_16": ('return q * np.repeat(f["d"], 32, axis=1)', 'return q * np.repeat(f["d"], 16, axis=1)[:, :q.shape[1]]'),
     # packing
+    "pack_q8_piece_order": ("for a in (0, 4, 1, 5)], axis=2)", "for a in (0, 1, 4, 5)], axis=2)"),
     "pack_k2_code_shift": ("shift = 2 * (4 * (kb % 2) + j // 2) + 16 * (j % 2)       # bit of (kb, j)",
                            "shift = 2 * (4 * (kb % 2) + j // 2) + 8 * (j % 2)       # bit of (kb, j)"),
     "pack_k4_scale_bit_order": ("bits[..., b // 8] |= (bit << (b % 8)).astype(np.uint8)",

@@ -380,6 +380,86 @@ def test_kquant_dequant_exact_against_rationals(fmt):
 
 
 # ---------------------------------------------------------------------------
+# Q8 (8-bit blocks of 32, shared expert)
+
+
+def test_worked_q8_blocks():
+    g = _golden("worked_examples.json")
+    for ex in g["q8"]:
+        w = np.zeros((1, 32), dtype=np.float32)
+        if "w" in ex:
+            w[0, :len(ex["w"])] = ex["w"]
+        else:
+            w[0, :len(ex["w_units_2^-25"])] = [v * 2.0 ** -25 for v in ex["w_units_2^-25"]]
+        f = O.q8_quantize(w)
+        n = len(ex["q"])
+        assert float(f["d"][0, 0]) == _f16_hex(ex["d_f16_hex"]), ex["name"]
+        assert list(f["q"][0, :n]) == ex["q"], ex["name"]
+        assert not f["q"][0, n:].any()
+        assert list(O.q8_dequantize(f)[0, :n]) == ex["decoded"], ex["name"]
+
+
+def _q8_blocks():
+    """Blocks of 32 with normal and fp16-subnormal scales, exact ties, zeros."""
+    rng = np.random.default_rng(21)
+    rows = [rng.standard_normal(32) * 0.02, rng.standard_normal(32) * 3.0,
+            rng.standard_normal(32) * 1e-6, rng.standard_normal(32) * 3e-7,
+            np.zeros(32), np.r_[np.zeros(31), -1e-3]]
+    # a block whose elements sit exactly on half steps of its own scale
+    d = float(np.float16(0.5 / 127))
+    ties = np.array([0.5] + [d * (k + 0.5) * (-1) ** k for k in range(31)])
+    rows.append(ties)
+    return np.array(rows).astype(np.float32)
+
+
+def test_q8_scale_is_nearest_fp16_of_max_over_127():
+    """d is the fp16 nearest to max|w|/127 among its fp16 neighbours (exact
+    rational distances), ties to the even significand."""
+    w = _q8_blocks()
+    f = O.q8_quantize(w)
+    for r in range(w.shape[0]):
+        target = Fraction(float(np.abs(w[r].astype(np.float64)).max())) / 127
+        cands = _f16_neighbors(float(target))
+        win = _nearest_ties_even(target, cands)
+        if len(win) == 2:
+            win = [c for c in win if int(np.float16(c).view(np.uint16)) % 2 == 0]
+        assert float(f["d"][r, 0]) == win[0], r
+
+
+def test_q8_codes_are_nearest_of_all_codes():
+    """Brute force over the 255 codes: q minimizes |w - d c| exactly, ties
+    to the code of larger magnitude; with a normal scale the largest |w| of
+    a block takes |q| = 127."""
+    w = _q8_blocks()
+    f = O.q8_quantize(w)
+    for r in range(w.shape[0]):
+        d = Fraction(float(f["d"][r, 0]))
+        for k in range(32):
+            x = Fraction(float(w[r, k]))
+            if d == 0:
+                assert f["q"][r, k] == 0
+                continue
+            best = min(range(-127, 128), key=lambda c: (abs(x - d * c), -abs(c)))
+            assert int(f["q"][r, k]) == best, (r, k, int(f["q"][r, k]), best)
+        if d >= Fraction(2) ** -14:
+            assert np.abs(f["q"][r].astype(int)).max() == 127, r
+
+
+def test_q8_error_bound_and_exact_roundtrip():
+    rng = np.random.default_rng(22)
+    w = (rng.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    f = O.q8_quantize(w)
+    dq = O.q8_dequantize(f)
+    d = np.repeat(f["d"], 32, axis=1)
+    assert np.all(np.abs(dq - w) <= d / 2)
+    # values already on the grid, with the code 127 in each block, come back unchanged
+    g = O.q8_quantize(dq.astype(np.float32))
+    assert np.array_equal(g["q"], f["q"]) and np.array_equal(g["d"], f["d"])
+    # dequantized values are exact fp32 numbers
+    assert np.array_equal(dq.astype(np.float32).astype(np.float64), dq)
+
+
+# ---------------------------------------------------------------------------
 # Byte layout
 
 
@@ -443,9 +523,26 @@ def test_layout_single_weight_positions():
     base = (1 * (K // 256) + 1) * 8192
     off = base + 1 * 1024 + lane * 16 + 4 * 2
     assert p[off] == 0x80 and p[off + 1] == 0x3F and np.count_nonzero(p) == 2
+    # Q8: (kb=1, j=4) sits in 16-byte piece 2 (k-blocks 1 and 3), first half:
+    # byte 2*1024 + lane*16 + 4; the scale of (n, kb) at 4096 + n*16 + kb*2
+    c = {"fmt": "q8", "q": np.zeros((R, K), np.int8), "d": np.zeros((R, K // 32))}
+    c["q"][r, k] = -5
+    c["d"][r, k // 32] = 1.0
+    p = O.pack_matrix(c).reshape(-1)
+    base = (1 * (K // 256) + 1) * 4352
+    assert p[base + 2 * 1024 + lane * 16 + 4] == 0xFB
+    assert p[base + 4096 + 5 * 16 + 2 * 1 + 1] == 0x3C and np.count_nonzero(p) == 2
+    c["q"][r, k] = 0
+    c["q"][r, k + 64] = 7                # kb = 3: piece 2, second half
+    p = O.pack_matrix(c).reshape(-1)
+    assert p[base + 2 * 1024 + lane * 16 + 8 + 4] == 7
+    c["q"][r, k + 64] = 0
+    c["q"][r, k + 128] = 9               # kb = 5: piece 3, first half
+    p = O.pack_matrix(c).reshape(-1)
+    assert p[base + 3 * 1024 + lane * 16 + 4] == 9
 
 
-@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4", "bf16"])
+@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4", "bf16", "q8"])
 def test_pack_unpack_roundtrip(fmt):
     rng = np.random.default_rng(10)
     table = O.codebook(0)
