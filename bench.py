@@ -30,7 +30,8 @@ in the 256 MB last-level cache.  Kernel durations come from HIP events that
 hipExtLaunchKernel records at each kernel dispatch's start and end (the
 library's moe_profile_next_launch hook), in a pass that launches the same
 steps one by one on the stream the kernels run on; events captured into a
-graph carry no timestamps.  --workload W measures one other workload alone.
+graph carry no timestamps.  --workload W measures one other workload alone
+(the *_q8 workloads store the shared expert in the 8-bit Q8 format).
 """
 from __future__ import annotations
 
@@ -83,8 +84,9 @@ def source_digest():
 # The decode call runs the single-token kernels once per token up to this
 # many tokens (kDecPerTokenMax in csrc/abi.hip).
 DEC_PER_TOKEN_MAX = 3
-DECODE = {"decode_b1", "decode_b16_hot", "k4_h7168_decode", "decode_b1_noshared", "draft_verify_t3"}
-PREFILL = {"prefill_2048", "k4_h7168_prefill"}
+DECODE = {"decode_b1", "decode_b16_hot", "k4_h7168_decode", "decode_b1_noshared", "draft_verify_t3",
+          "decode_b1_q8", "k4_h7168_decode_q8"}
+PREFILL = {"prefill_2048", "k4_h7168_prefill", "prefill_2048_q8"}
 
 
 def log(msg):
@@ -140,7 +142,10 @@ def build_layer(wl, instances):
     sh = [None, None, None]
     if Is > 0:
         for i, which in enumerate(("up", "gate", "down")):
-            sh[i] = dev(qmoe.moe_quantize_pack("bf16", synth.bf16_bits_to_f32(synth.shared_weight_bits(wl, which))))
+            if wl.fmt_shared == "q8":
+                sh[i] = dev(qmoe.moe_quantize_pack("q8", synth.shared_weight_f32(wl, which)))
+            else:
+                sh[i] = dev(qmoe.moe_quantize_pack("bf16", synth.bf16_bits_to_f32(synth.shared_weight_bits(wl, which))))
     router = dev(synth.router_weight(wl))
     bias = synth.logit_bias(wl)
     bias = dev(bias) if bias is not None else None
@@ -154,7 +159,7 @@ def build_layer(wl, instances):
             router = router.clone()
         layers.append(qmoe.DeviceLayer(E, H, I, Is, wl.fmts, d_up, d_gate, d_down, codebook=cbd,
                                        shared_up=sh[0], shared_gate=sh[1], shared_down=sh[2], router=router,
-                                       bias=bias))
+                                       bias=bias, shared_fmt=wl.fmt_shared))
     torch.cuda.synchronize()
     return layers, (nb_up, nb_dn)
 
@@ -179,7 +184,11 @@ def cpu_baseline(wl, seconds, max_tokens=8):
     wr = synth.router_weight(wl)
     bias = synth.logit_bias(wl)
     shared = None
-    if wl.shared_inter:
+    if wl.shared_inter and wl.fmt_shared == "q8":
+        shared = tuple(O.dequantize_matrix(O.quantize_matrix("q8", synth.shared_weight_f32(wl, w)),
+                                           k=wl.hidden if w != "down" else wl.shared_inter)
+                       for w in ("up", "gate", "down"))
+    elif wl.shared_inter:
         shared = tuple(synth.bf16_bits_to_f32(synth.shared_weight_bits(wl, w)).astype(np.float64)
                        for w in ("up", "gate", "down"))
     # sample tokens: the workload's own inputs, in order
@@ -299,10 +308,20 @@ def time_decode(wl, layers, steps, warmup, label):
             "idx": idx_all[warmup:].cpu().numpy(), "eager_tps": steps * T / (te1 - te0)}
 
 
+def shared_bytes(wl):
+    """Packed bytes of the shared expert's up (= gate) and down matrices."""
+    if wl.shared_inter == 0:
+        return 0, 0
+    from bit_quantized_moe_02_amd import qmoe
+    return (qmoe.moe_packed_bytes(wl.fmt_shared, wl.shared_inter, wl.hidden),
+            qmoe.moe_packed_bytes(wl.fmt_shared, wl.hidden, wl.shared_inter))
+
+
 def decode_work(wl, idx_h, nb_up, nb_dn):
     """Algorithmic bytes per timed launch of the up/gate and down kernels and
     the quantized expert bytes alone, from the routing each step made."""
     T, k, H, I, Is = wl.tokens, wl.top_k, wl.hidden, wl.inter, wl.shared_inter
+    nb_su, nb_sd = shared_bytes(wl)
     w = {"decode_upgate": [], "decode_down": [], "route_logits": [], "quant_upgate": [], "quant_down": []}
     for s in range(idx_h.shape[0]):
         # up to DEC_PER_TOKEN_MAX tokens the library runs the single-token
@@ -313,9 +332,9 @@ def decode_work(wl, idx_h, nb_up, nb_dn):
         w["quant_upgate"].append(d * 2 * nb_up)
         w["quant_down"].append(d * nb_dn)
         # up/gate: both matrices of the distinct routed experts + shared, x in, h out
-        w["decode_upgate"].append(d * 2 * nb_up + 2 * Is * H * 2 + Tl * H * 2 + Tl * k * I * 2 + Tl * Is * 2)
+        w["decode_upgate"].append(d * 2 * nb_up + 2 * nb_su + Tl * H * 2 + Tl * k * I * 2 + Tl * Is * 2)
         # down: the distinct routed down matrices + shared, h in, y out
-        w["decode_down"].append(d * nb_dn + H * Is * 2 + Tl * k * I * 2 + Tl * Is * 2 + Tl * H * 4)
+        w["decode_down"].append(d * nb_dn + nb_sd + Tl * k * I * 2 + Tl * Is * 2 + Tl * H * 4)
         # router: fp32 weights + x in, logits out
         w["route_logits"].append(wl.n_experts * H * 4 + T * H * 2 + T * wl.n_experts * 4)
     return {kn: np.array(v, dtype=np.float64) for kn, v in w.items()}
@@ -417,7 +436,9 @@ def traffic_of(workload, kernel):
 def decode_config(wl, instances):
     return {"workload": wl.name, "hidden": wl.hidden, "inter": wl.inter, "experts": wl.n_experts,
             "top_k": wl.top_k, "shared_inter": wl.shared_inter, "tokens_per_step": wl.tokens,
-            "formats": "/".join(f.upper() for f in wl.fmts), "layer_instances": instances, "launch": "hip_graph",
+            "formats": "/".join(f.upper() for f in wl.fmts),
+            "shared_format": wl.fmt_shared.upper() if wl.shared_inter else None,
+            "layer_instances": instances, "launch": "hip_graph",
             "entry": "moe_layer_decode",
             "decode_kernels": "single-token, once per token" if wl.tokens <= DEC_PER_TOKEN_MAX else "batched"}
 
@@ -522,7 +543,8 @@ def main():
         pre = time_prefill(pwl, players[0], psteps, pwarm)
         pre["config"] = {"workload": pwl.name, "hidden": pwl.hidden, "inter": pwl.inter, "experts": pwl.n_experts,
                          "top_k": pwl.top_k, "shared_inter": pwl.shared_inter, "tokens_per_step": pwl.tokens,
-                         "formats": "/".join(f.upper() for f in pwl.fmts)}
+                         "formats": "/".join(f.upper() for f in pwl.fmts),
+                         "shared_format": pwl.fmt_shared.upper() if pwl.shared_inter else None}
         if not args.no_cpu_baseline:
             log("[bench] timing the CPU oracle (prefill) ...")
             pre["cpu_baseline"] = cpu_baseline(pwl, min(args.cpu_seconds, 10.0), max_tokens=6)

@@ -41,7 +41,7 @@ int n_cus() {
 // sizes.
 struct Geometry {
   int E, H, I, Is, I_pad, Is_pad;
-  int fmt_ug, fmt_dn;
+  int fmt_ug, fmt_dn, fmt_s;
   size_t up_bytes, down_bytes;
 };
 
@@ -65,6 +65,8 @@ int check_weights(const moe_weights* w, Geometry* g, const char* fn) {
     return fail(MOE_ERR_INVALID_ARG, f + ": expert weights must be 16-byte aligned");
   if (cb2 && !w->codebook) return fail(MOE_ERR_INVALID_ARG, f + ": CB2 weights need the codebook");
   if (cb2 && !aligned16(w->codebook)) return fail(MOE_ERR_INVALID_ARG, f + ": the codebook must be 16-byte aligned");
+  if (w->fmt_shared != MOE_FMT_BF16 && w->fmt_shared != MOE_FMT_Q8)
+    return fail(MOE_ERR_UNSUPPORTED, f + ": fmt_shared must be MOE_FMT_BF16 or MOE_FMT_Q8");
   if (w->shared_inter > 0) {
     if (!w->shared_up || !w->shared_gate || !w->shared_down)
       return fail(MOE_ERR_INVALID_ARG, f + ": shared expert pointer is NULL");
@@ -79,6 +81,7 @@ int check_weights(const moe_weights* w, Geometry* g, const char* fn) {
   g->Is_pad = (int)pad256(w->shared_inter > 0 ? w->shared_inter : 1);
   g->fmt_ug = w->fmt_up;
   g->fmt_dn = w->fmt_down;
+  g->fmt_s = w->fmt_shared;
   g->up_bytes = moe_packed_bytes(w->fmt_up, w->inter, w->hidden);
   g->down_bytes = moe_packed_bytes(w->fmt_down, w->hidden, w->inter);
   return MOE_OK;
@@ -252,6 +255,8 @@ int run_decode(const char* who, const moe_weights* w, const Geometry& g, const v
   a.sup = (const uint8_t*)w->shared_up;
   a.sgate = (const uint8_t*)w->shared_gate;
   a.sdown = (const uint8_t*)w->shared_down;
+  a.fmt_s = g.fmt_s;
+  a.tb_s = tile_bytes(g.fmt_s);
   a.codebook = w->codebook;
   a.h = (_Float16*)(wsb + L.h);
   a.hs = (_Float16*)(wsb + L.hs);
@@ -492,6 +497,8 @@ extern "C" int moe_expert_ffn_prefill(const moe_weights* w, const void* x_bf16, 
   a.sup = (const uint8_t*)w->shared_up;
   a.sgate = (const uint8_t*)w->shared_gate;
   a.sdown = (const uint8_t*)w->shared_down;
+  a.fmt_s = g.fmt_s;
+  a.tb_s = tile_bytes(g.fmt_s);
   a.codebook = w->codebook;
   a.h = (_Float16*)(wsb + L.h);
   a.hs = (_Float16*)(wsb + L.hs);

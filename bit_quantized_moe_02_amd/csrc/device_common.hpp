@@ -1,5 +1,5 @@
 // Device helpers shared by the libqmoe kernels: vector types, the fp16 MFMA,
-// and the per-lane decoders of the CB2 / K2 / K4 / BF16 tiles that
+// and the per-lane decoders of the CB2 / K2 / K4 / BF16 / Q8 tiles that
 // include/qmoe.h defines.
 //
 // Every decoder produces the MFMA B operand of one lane for one k-block kb:
@@ -29,6 +29,7 @@ constexpr int kCb2Tile = 1280;
 constexpr int kK2Tile = 1344;
 constexpr int kK4Tile = 2304;
 constexpr int kBf16Tile = 8192;
+constexpr int kQ8Tile = 4352;
 
 __device__ __forceinline__ float4v mfma_f16(const half8& a, const half8& b, const float4v& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -68,6 +69,38 @@ __device__ __forceinline__ half8 bf16x8_to_half8(const u32x4& v) {
   r.z = bf16x2_to_f16x2(v.z);
   r.w = bf16x2_to_f16x2(v.w);
   return as_half8(r);
+}
+
+// ---------------------------------------------------------------------------
+// Q8 tiles (8-bit codes, one fp16 scale d per 32 weights: w = d q).
+// Byte offset of the 8 codes of (n, kb, qq) = lane c's k-block kb: 16-byte
+// piece 2*(kb%2) + kb/4 holds k-blocks a and a + 2 of every lane.
+__device__ __forceinline__ int q8_code_off(int kb, int c) {
+  return 1024 * (2 * (kb & 1) + (kb >> 2)) + 16 * c + 8 * ((kb >> 1) & 1);
+}
+// Byte offset of row n's 8 fp16 scales (k-block kb at +2 kb).
+__device__ __forceinline__ int q8_scale_off(int n) { return 4096 + 16 * n; }
+
+// 8 signed 8-bit codes (two dwords, j = 0..7) -> their exact fp16 values:
+// code b becomes the byte b ^ 0x80 = b + 128 in the mantissa of fp16 1024
+// (0x64 in the high byte), i.e. 1152 + b, and 1152 is subtracted (exact).
+__device__ __forceinline__ half8 q8_codes(uint32_t w0, uint32_t w1) {
+  const uint32_t b0 = w0 ^ 0x80808080u, b1 = w1 ^ 0x80808080u;
+  const uint32_t hi = 0x64646464u;
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(hi, b0, 0x04010400u);   // bytes 0, 1 of b0 under 0x64
+  r.y = __builtin_amdgcn_perm(hi, b0, 0x04030402u);   // bytes 2, 3
+  r.z = __builtin_amdgcn_perm(hi, b1, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(hi, b1, 0x04030402u);
+  const _Float16 o = (_Float16)1152.0f;
+  return as_half8(r) - half8{o, o, o, o, o, o, o, o};
+}
+
+// fp16(d q) for the 8 codes: the fp16 product of two fp16 numbers is the
+// exact product rounded once, the fp16 value of the dequantized weight.
+__device__ __forceinline__ half8 q8_fold(uint32_t w0, uint32_t w1, uint32_t d_bits) {
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)d_bits);
+  return q8_codes(w0, w1) * half8{d, d, d, d, d, d, d, d};
 }
 
 // ---------------------------------------------------------------------------

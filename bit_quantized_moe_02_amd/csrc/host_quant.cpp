@@ -1,5 +1,5 @@
 // Host side of libqmoe: the CB2 codebook, fp64 -> fp16 rounding, the CB2 /
-// K2 / K4 quantizers and the tile packers, plus the thread-local error
+// K2 / K4 / Q8 quantizers and the tile packers, plus the thread-local error
 // string.  No HIP dependency: this file builds with the host compiler alone.
 //
 // The formats and quantizer rules are the ones include/qmoe.h defines; the
@@ -42,6 +42,7 @@ int tile_bytes(int fmt) {
     case MOE_FMT_K2: return 1344;
     case MOE_FMT_K4: return 2304;
     case MOE_FMT_BF16: return 8192;
+    case MOE_FMT_Q8: return 4352;
     default: return 0;
   }
 }
@@ -302,6 +303,35 @@ void pack_tile_k4(const float* rows, int64_t stride, uint8_t* tile) {
   }
 }
 
+// Q8: per 32 weights d = fp16(max|w| / 127); q = nearest code to w/d with
+// ties away from zero, clamped to -127..127.  Codes of (n, kb, qq) go to the
+// 16-byte piece i of lane 16*qq + n that holds k-blocks 4*(i%2) + i/2 and that
+// plus 2 (i = 2*(kb%2) + kb/4, second half when (kb/2) % 2 == 1).
+bool pack_tile_q8(const float* rows, int64_t stride, uint8_t* tile) {
+  for (int n = 0; n < 16; ++n) {
+    const float* r = rows + n * stride;
+    for (int kb = 0; kb < 8; ++kb) {
+      const float* blk = r + 32 * kb;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) amax = std::max(amax, fabs((double)blk[i]));
+      const uint16_t dh = f16_nonneg_zero(amax / 127.0);
+      if ((dh & 0x7C00) == 0x7C00) return false;      // scale not representable
+      put16(tile + 4096 + 16 * n + 2 * kb, dh);
+      const double d = f16_to_f64(dh);
+      const int piece = 2 * (kb % 2) + kb / 4, half = (kb / 2) % 2;
+      for (int i = 0; i < 32; ++i) {
+        const double x = (double)blk[i];
+        double mag = 0.0;
+        if (d != 0.0) mag = std::min(127.0, floor(fabs(x) / d + 0.5));
+        const int q = x < 0.0 ? -(int)mag : (int)mag;
+        const int qq = i / 8, j = i % 8, lane = 16 * qq + n;
+        tile[1024 * piece + 16 * lane + 8 * half + j] = (uint8_t)(int8_t)q;
+      }
+    }
+  }
+  return true;
+}
+
 void pack_tile_bf16(const float* rows, int64_t stride, uint8_t* tile) {
   for (int n = 0; n < 16; ++n)
     for (int kk = 0; kk < 256; ++kk) {
@@ -334,15 +364,15 @@ extern "C" int moe_codebook_generate(uint64_t seed, int8_t* table_out) {
 }
 
 // True when some fp16 scale of the packed matrix would not be finite: CB2's
-// s = fp16(max|w| / 0.75) over a 32-weight group, or a K-quant super-block's
+// s = fp16(max|w| / 0.75) or Q8's d = fp16(max|w| / 127) over a 32-weight group, or a K-quant super-block's
 // d = fp16(max_s a_s / S) or dmin = fp16(max_s b_s / S).  fp16 rounding is
 // monotone, so the largest group or sub-block decides; columns past k are the
 // zeros the packers pad with.  Checked before any output byte is written.
 static bool scale_overflows(int fmt, const float* w, int64_t rows, int64_t k) {
-  if (fmt == MOE_FMT_CB2) {
+  if (fmt == MOE_FMT_CB2 || fmt == MOE_FMT_Q8) {
     double amax = 0.0;
     for (int64_t i = 0; i < rows * k; ++i) amax = std::max(amax, fabs((double)w[i]));
-    return (f16_nonneg_zero(amax / 0.75) & 0x7C00) == 0x7C00;
+    return (f16_nonneg_zero(amax / (fmt == MOE_FMT_CB2 ? 0.75 : 127.0)) & 0x7C00) == 0x7C00;
   }
   if (fmt != MOE_FMT_K2 && fmt != MOE_FMT_K4) return false;
   const KqParams p = fmt == MOE_FMT_K2 ? KqParams{16, 3, 15} : KqParams{32, 15, 63};
@@ -417,6 +447,9 @@ extern "C" int moe_quantize_pack(int fmt, const float* w, int64_t rows, int64_t 
             break;
           case MOE_FMT_K2: pack_tile_k2(src, kp, tile); break;
           case MOE_FMT_K4: pack_tile_k4(src, kp, tile); break;
+          case MOE_FMT_Q8:
+            if (!pack_tile_q8(src, kp, tile)) ok[tid] = 0;
+            break;
           default: pack_tile_bf16(src, kp, tile); break;
         }
       }

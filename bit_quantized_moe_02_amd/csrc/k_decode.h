@@ -12,13 +12,14 @@ struct DecArgs {
   int T, H, I, Is, I_pad, Is_pad, k, E;
   int nw_ug, nw_dn;           // waves per workgroup of the two kernels
   int tb_ug, tb_dn;           // tile bytes of the routed up/gate and down formats
+  int fmt_s, tb_s;            // shared expert: MOE_FMT_BF16 or MOE_FMT_Q8, and its tile bytes
   const int32_t* topk_idx;    // [T][k]
   const uint8_t* up;          // routed experts, packed, expert-major
   const uint8_t* gate;
   const uint8_t* down;
   size_t expert_bytes;        // bytes of one packed up (= gate) matrix
   size_t expert_bytes_down;   // bytes of one packed down matrix
-  const uint8_t* sup;         // shared expert, BF16 tiles (or null)
+  const uint8_t* sup;         // shared expert, BF16 or Q8 tiles (or null)
   const uint8_t* sgate;
   const uint8_t* sdown;
   const int8_t* codebook;     // CB2 table (device)

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(1024) void dec_upgate_kernel(DecArgs a) {
     atomicMax(&S->xef[i / (a.H / 8)], bf16x8_max_efield(load16(a.x + 8 * (size_t)i)));
   if (FMT == MOE_FMT_CB2) cb2_fill_tables(a.codebook, val_tab, flip_tab, tid, blockDim.x);
   const int64_t n_rt = a.I / 16, n_rts = a.Is / 16;
-  const int64_t w_r = (int64_t)2 * a.tb_ug * n_chunks, w_s = (int64_t)2 * kBf16Tile * n_chunks;
+  const int64_t w_r = (int64_t)2 * a.tb_ug * n_chunks, w_s = (int64_t)2 * a.tb_s * n_chunks;
   if (tid == 0) {
     const int64_t n_r = (int64_t)S->L.n * n_rt;
     S->item_lo = item_start(blockIdx.x, gridDim.x, n_rts, w_s, n_r, w_r);
@@ -137,7 +137,16 @@ __global__ __launch_bounds__(1024) void dec_upgate_kernel(DecArgs a) {
         for (int cc = 0; cc < CPW; ++cc) {
           const int chunk = wave * CPW + cc;
           if (chunk >= n_chunks) break;
-          if (shared) {
+          if (shared && a.fmt_s == MOE_FMT_Q8) {
+            // exact codes, each k-block's dots times row n's scale in fp32
+            const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kQ8Tile;
+            const u32x4 scl = load16(tile + q8_scale_off(lane & 15));
+            for (int kb = 0; kb < 8; ++kb) {
+              const uint32_t* cp = reinterpret_cast<const uint32_t*>(tile + q8_code_off(kb, lane));
+              const float4v c = mfma_f16(A[cc][kb], q8_codes(cp[0], cp[1]), zero);
+              acc[mat] += h2f((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu) * c;
+            }
+          } else if (shared) {
             const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kBf16Tile;
             for (int kb = 0; kb < 8; ++kb) {
               const half8 b = bf16x8_to_half8(load16(tile + 1024 * kb + 16 * lane));
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(1024) void dec_down_kernel(DecArgs a) {
   build_expert_list(a.topk_idx, T * k, k, a.E, &S->L);
   const int64_t n_rt = a.H / 16;
   const int64_t n_rts = (a.Is > 0) ? a.H / 16 : 0;
-  const int64_t w_r = (int64_t)a.tb_dn * n_chunks, w_s = (int64_t)kBf16Tile * n_chunks_s;
+  const int64_t w_r = (int64_t)a.tb_dn * n_chunks, w_s = (int64_t)a.tb_s * n_chunks_s;
   if (tid == 0) {
     const int64_t n_r = (int64_t)S->L.n * n_rt;
     S->item_lo = item_start(blockIdx.x, gridDim.x, n_rts, w_s, n_r, w_r);
@@ -307,14 +316,23 @@ __global__ __launch_bounds__(1024) void dec_down_kernel(DecArgs a) {
     const int Kvalid = shared ? a.Is : a.I;
     for (int chunk = wave; chunk < nck; chunk += NW) {
       if (shared) {
-        const uint8_t* tile = a.sdown + ((size_t)rt * n_chunks_s + chunk) * kBf16Tile;
+        const bool q8 = a.fmt_s == MOE_FMT_Q8;
+        const uint8_t* tile = a.sdown + ((size_t)rt * n_chunks_s + chunk) * a.tb_s;
+        const u32x4 scl = q8 ? load16(tile + q8_scale_off(n)) : u32x4{0u, 0u, 0u, 0u};
         for (int kb = 0; kb < 8; ++kb) {
           const int col = chunk * 256 + kb * 32 + g4 * 8;
           u32x4 ar = {0, 0, 0, 0};
           const int m = n;  // A row = lane % 16
           if (m < n_tok && col < Kvalid) ar = load16(a.hs + (size_t)S->tok[m] * a.Is + col);
-          const half8 b = bf16x8_to_half8(load16(tile + 1024 * kb + 16 * lane));
-          acc = mfma_f16(as_half8(ar), b, acc);
+          if (q8) {
+            // exact codes, the k-block's dots times row n's scale in fp32
+            const uint32_t* cp = reinterpret_cast<const uint32_t*>(tile + q8_code_off(kb, lane));
+            const float4v c = mfma_f16(as_half8(ar), q8_codes(cp[0], cp[1]), zero);
+            acc += h2f((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu) * c;
+          } else {
+            const half8 b = bf16x8_to_half8(load16(tile + 1024 * kb + 16 * lane));
+            acc = mfma_f16(as_half8(ar), b, acc);
+          }
         }
       } else if (FMT == MOE_FMT_K4) {
         const uint8_t* tile = a.down + (size_t)e * a.expert_bytes_down + ((size_t)rt * n_chunks + chunk) * kK4Tile;

@@ -69,6 +69,115 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, int off) {
 
 constexpr int kBatch = 8;        // row tiles reduced per barrier (up/gate)
 
+// ---------------------------------------------------------------------------
+// Shared-expert tiles, BF16 or Q8 (SF = MOE_FMT_BF16 / MOE_FMT_Q8).  Q8
+// weights enter the MFMA as their exact 8-bit codes and the per-32 scales
+// are applied in fp32 to block dots that each cover one k-block, so the
+// single-token paths use the Q8 weights exactly, as they do the BF16 ones.
+template <int SF>
+constexpr int shared_tile_bytes() { return SF == MOE_FMT_Q8 ? kQ8Tile : kBf16Tile; }
+
+// Half row tile (rows r = 8 hr + (n & 7)) of one matrix: lanes n < 8 take
+// row r's even k-blocks, lanes n >= 8 its odd ones, so that A_{2p} | A_{2p+1}
+// feeds one MFMA per k-block pair p.  BF16: v[p] = the lane's 8 weights of
+// k-block 2p + n/8.  Q8: v[0], v[1] = its two 16-byte code pieces (k-blocks
+// {0,2}, {4,6} for n < 8, {1,3}, {5,7} for n >= 8), sc = row r's 8 scales.
+struct ShHalf {
+  u32x4 v[4];
+  u32x4 sc;
+};
+
+template <int SF, typename Ld>
+__device__ __forceinline__ void sh_half_load(ShHalf& S, Ld ld, int n, int qq, int r) {
+  const int c = 16 * qq + r;
+  if constexpr (SF == MOE_FMT_Q8) {
+    S.v[0] = ld(1024 * (2 * (n >> 3)) + 16 * c);
+    S.v[1] = ld(1024 * (2 * (n >> 3) + 1) + 16 * c);
+    S.sc = ld(q8_scale_off(r));
+  } else {
+    for (int p = 0; p < 4; ++p) S.v[p] = ld(1024 * (2 * p + (n >> 3)) + 16 * c);
+  }
+}
+
+// The half tile times the activations; the lane's part of row r (lanes
+// g < 2, others 0): the caller adds lanes n, n ^ 8 and g = 0, 1.  After the
+// four MFMAs C[kb][n] holds the dot of k-block kb alone (even kb in lanes
+// n < 8, odd kb in lanes n >= 8), which is where a Q8 scale applies.
+template <int SF, typename Ap>
+__device__ __forceinline__ float sh_half_dot(const ShHalf& S, Ap a_pair, int n, int g) {
+  float4v c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    half8 b;
+    if constexpr (SF == MOE_FMT_Q8) {
+      const u32x4 pc = S.v[p >> 1];
+      b = (p & 1) ? q8_codes(pc.z, pc.w) : q8_codes(pc.x, pc.y);
+    } else {
+      b = bf16x8_to_half8(S.v[p]);
+    }
+    c = mfma_f16(a_pair(p), b, c);
+  }
+  float t;
+  if constexpr (SF == MOE_FMT_Q8) {
+    // lane (g, n): k-blocks 4g, 4g+2 (n < 8) or 4g+1, 4g+3 (n >= 8)
+    const uint32_t w0 = (g & 1) ? S.sc.z : S.sc.x, w1 = (g & 1) ? S.sc.w : S.sc.y;
+    const int sh = (n >> 3) ? 16 : 0;
+    const float d0 = h2f((w0 >> sh) & 0xFFFFu), d1 = h2f((w1 >> sh) & 0xFFFFu);
+    t = (n < 8) ? fmaf(d1, c[2], d0 * c[0]) : fmaf(d1, c[3], d0 * c[1]);
+  } else {
+    t = (n < 8) ? c[0] + c[2] : c[1] + c[3];
+  }
+  return g >= 2 ? 0.f : t;
+}
+
+// Half a K-chunk (k-blocks kb0 .. kb0+3, kb0 = 0 or 4) of row n of a down
+// tile, for the lane c = 16 g4 + n.  BF16: v[q] = the lane's 8 weights of
+// k-block kb0 + q.  Q8: v[0] = the piece of k-blocks kb0, kb0+2, v[1] = that
+// of kb0+1, kb0+3, sc = row n's 8 scales.
+struct ShQuarter {
+  u32x4 v[4];
+  u32x4 sc;
+};
+
+template <int SF, typename Ld>
+__device__ __forceinline__ void sh_dn_load(ShQuarter& S, Ld ld, int kb0, int lane) {
+  if constexpr (SF == MOE_FMT_Q8) {
+    const int h = kb0 >> 2;
+    S.v[0] = ld(1024 * h + 16 * lane);
+    S.v[1] = ld(1024 * (h + 2) + 16 * lane);
+    S.sc = ld(q8_scale_off(lane & 15));
+  } else {
+    for (int q = 0; q < 4; ++q) S.v[q] = ld(1024 * (kb0 + q) + 16 * lane);
+  }
+}
+
+// B operand of k-block kb0 + q.
+template <int SF>
+__device__ __forceinline__ half8 sh_dn_b(const ShQuarter& S, int q) {
+  if constexpr (SF == MOE_FMT_Q8) {
+    const u32x4 pc = S.v[q & 1];
+    return (q >> 1) ? q8_codes(pc.z, pc.w) : q8_codes(pc.x, pc.y);
+  } else {
+    return bf16x8_to_half8(S.v[q]);
+  }
+}
+
+// Row n's sum from the accumulated C.  BF16: the activations sit in A row 0
+// for every q, so C[0][n] is the sum.  Q8: those of k-block kb0 + q sit in
+// row q, C[q][n] is that block's dot, scaled here (rows >= 4 are zero).
+template <int SF>
+__device__ __forceinline__ float sh_dn_sum(const ShQuarter& S, const float4v& c, int kb0) {
+  if constexpr (SF == MOE_FMT_Q8) {
+    const uint32_t w0 = kb0 ? S.sc.z : S.sc.x, w1 = kb0 ? S.sc.w : S.sc.y;
+    float v = h2f(w0 & 0xFFFFu) * c[0];
+    v = fmaf(h2f(w0 >> 16), c[1], v);
+    v = fmaf(h2f(w1 & 0xFFFFu), c[2], v);
+    return fmaf(h2f(w1 >> 16), c[3], v);
+  } else {
+    return c[0];
+  }
+}
+
 // Same weighted contiguous split of items as the multi-token kernels: item i
 // goes to the workgroup whose share of the total weight holds its midpoint.
 __device__ int64_t item_start1(int64_t g, int64_t G, int64_t n_s, int64_t w_s, int64_t n_r, int64_t w_r) {
@@ -107,6 +216,7 @@ __device__ __forceinline__ void ug_load(UgPay& p, const DecArgs& a, int e, int64
     }
 }
 
+template <int SF>
 __global__ __launch_bounds__(1024) void dec1_cb2_wide_upgate_kernel(DecArgs a) {
   constexpr int CPW = kCpw;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -118,7 +228,7 @@ __global__ __launch_bounds__(1024) void dec1_cb2_wide_upgate_kernel(DecArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, NW = blockDim.x >> 6;
   const int k = a.k, n_chunks = a.H / 256;
   const int64_t n_rt = a.I / 16, n_rts = a.Is / 16;
-  const int64_t w_r = (int64_t)2 * a.tb_ug * n_chunks, w_s = (int64_t)2 * kBf16Tile * n_chunks;
+  const int64_t w_r = (int64_t)2 * a.tb_ug * n_chunks, w_s = (int64_t)2 * shared_tile_bytes<SF>() * n_chunks;
   uint32_t* xef = reinterpret_cast<uint32_t*>(smem + 16);                     // [NW] largest x exponent field per wave
   if (tid == 0) {
     range[0] = item_start1(blockIdx.x, gridDim.x, n_rts, w_s, (int64_t)k * n_rt, w_r);
@@ -208,15 +318,32 @@ __global__ __launch_bounds__(1024) void dec1_cb2_wide_upgate_kernel(DecArgs a) {
       for (int cc = 0; cc < CPW; ++cc) {
         const int chunk = wave * CPW + cc;
         if (chunk >= n_chunks) break;
-        u32x4 raw[2][8];
-        for (int mat = 0; mat < 2; ++mat) {
-          const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)item * n_chunks + chunk) * kBf16Tile;
-          for (int kb = 0; kb < 8; ++kb) raw[mat][kb] = load16(tile + 1024 * kb + 16 * lane);
-        }
-        for (int mat = 0; mat < 2; ++mat) {
-          float4v c = zero;
-          for (int kb = 0; kb < 8; ++kb) c = mfma_f16(A[cc][kb], bf16x8_to_half8(raw[mat][kb]), c);
-          v[mat] += c[0];
+        if constexpr (SF == MOE_FMT_Q8) {
+          // codes exact in the MFMA, then each k-block's dot times its scale
+          u32x4 raw[2][4], scl[2];
+          for (int mat = 0; mat < 2; ++mat) {
+            const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)item * n_chunks + chunk) * kQ8Tile;
+            for (int i = 0; i < 4; ++i) raw[mat][i] = load16(tile + 1024 * i + 16 * lane);
+            scl[mat] = load16(tile + q8_scale_off(lane & 15));
+          }
+          for (int mat = 0; mat < 2; ++mat)
+            for (int kb = 0; kb < 8; ++kb) {
+              const u32x4 pc = raw[mat][2 * (kb & 1) + (kb >> 2)];
+              const half8 b = ((kb >> 1) & 1) ? q8_codes(pc.z, pc.w) : q8_codes(pc.x, pc.y);
+              const float4v c = mfma_f16(A[cc][kb], b, zero);
+              v[mat] = fmaf(h2f((scl[mat][kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu), c[0], v[mat]);
+            }
+        } else {
+          u32x4 raw[2][8];
+          for (int mat = 0; mat < 2; ++mat) {
+            const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)item * n_chunks + chunk) * kBf16Tile;
+            for (int kb = 0; kb < 8; ++kb) raw[mat][kb] = load16(tile + 1024 * kb + 16 * lane);
+          }
+          for (int mat = 0; mat < 2; ++mat) {
+            float4v c = zero;
+            for (int kb = 0; kb < 8; ++kb) c = mfma_f16(A[cc][kb], bf16x8_to_half8(raw[mat][kb]), c);
+            v[mat] += c[0];
+          }
         }
       }
     }
@@ -327,7 +454,7 @@ __device__ __forceinline__ float cb2_scaled(const float4v& c, const uint32_t sc[
 // Route: the token's top k are ranked here from the router's partial
 // logits (every workgroup ranks them; workgroup 0 writes them out) while the
 // shared expert's tiles are already in flight.  E <= the workgroup's threads.
-template <bool Route>
+template <bool Route, int SF>
 __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tab = smem;                                                     // [0, kTabRep x 64 KB)
@@ -367,17 +494,18 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   }
   const u32x4 xr = load16(a.x + chunk * 256 + (m & 7) * 32 + qq * 8);    // used by lanes m < 8
 
-  // shared half tile loads: 2 matrices x 4 k-block pairs (zeros when the
-  // workgroup has no shared item)
-  u32x4 sraw[2][4];
+  // shared half tile loads of both matrices (zeros when the workgroup has
+  // no shared item)
+  constexpr int kSTile = shared_tile_bytes<SF>();
+  ShHalf sraw[2];
   auto issue_shared = [&](int su, bool valid) {
     const int rt = su >> 1, hr = su & 1;
     const int r = 8 * hr + (n & 7);
     for (int mat = 0; mat < 2; ++mat) {
-      const uint8_t* tile = valid ? (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kBf16Tile
+      const uint8_t* tile = valid ? (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kSTile
                                   : reinterpret_cast<const uint8_t*>(a.x);
-      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kBf16Tile : 0);
-      for (int p = 0; p < 4; ++p) sraw[mat][p] = bload16_nt(rs, 1024 * (2 * p + (n >> 3)) + 16 * (16 * qq + r));
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kSTile : 0);
+      sh_half_load<SF>(sraw[mat], [&](int off) { return bload16_nt(rs, off); }, n, qq, r);
     }
   };
   issue_shared(s_lo, s_lo < s_hi);
@@ -476,13 +604,8 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
     if (su != s_lo) issue_shared(su, true);
     float v[2];
     for (int mat = 0; mat < 2; ++mat) {
-      float4v c = zero;
-      for (int p = 0; p < 4; ++p) {
-        const half8 Ap = as_half8(as_u32x4(A[2 * p]) | as_u32x4(A[2 * p + 1]));
-        c = mfma_f16(Ap, bf16x8_to_half8(sraw[mat][p]), c);
-      }
-      float t = (n < 8) ? c[0] + c[2] : c[1] + c[3];
-      if (g >= 2) t = 0.f;
+      float t = sh_half_dot<SF>(
+          sraw[mat], [&](int p) { return as_half8(as_u32x4(A[2 * p]) | as_u32x4(A[2 * p + 1])); }, n, g);
       t += __shfl_xor(t, 8);
       t += __shfl_xor(t, 16);
       v[mat] = t;
@@ -634,6 +757,7 @@ __device__ __forceinline__ float k4_scaled(const float4v& c, const uint32_t s[3]
   return v;
 }
 
+template <int SF>
 __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
@@ -719,18 +843,15 @@ __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
     for (int kp = 0; kp < n_kp; ++kp) {
       const int chunk = kp * 16 + wave;
       if (chunk >= n_chunks) continue;
-      u32x4 sraw[2][4];
+      ShHalf sraw[2];
       for (int mat = 0; mat < 2; ++mat) {
-        const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * kBf16Tile;
-        for (int p = 0; p < 4; ++p) sraw[mat][p] = load16(tile + 1024 * (2 * p + (n >> 3)) + 16 * (16 * qq + r));
+        const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)rt * n_chunks + chunk) * shared_tile_bytes<SF>();
+        sh_half_load<SF>(sraw[mat], [&](int off) { return load16(tile + off); }, n, qq, r);
       }
       half8 Ap[4];
       for (int p = 0; p < 4; ++p) Ap[p] = a_pair(chunk, p);
       for (int mat = 0; mat < 2; ++mat) {
-        float4v c = zero;
-        for (int p = 0; p < 4; ++p) c = mfma_f16(Ap[p], bf16x8_to_half8(sraw[mat][p]), c);
-        float t = (n < 8) ? c[0] + c[2] : c[1] + c[3];
-        if (g >= 2) t = 0.f;
+        float t = sh_half_dot<SF>(sraw[mat], [&](int p) { return Ap[p]; }, n, g);
         t += __shfl_xor(t, 8);
         t += __shfl_xor(t, 16);
         v[mat] += t;
@@ -861,6 +982,7 @@ __device__ __forceinline__ void dn_load4(DnPay4& p, __amdgpu_buffer_rsrc_t tile,
 constexpr int kDnUnits = 4;    // routed units held in registers per wave
 constexpr int kStageVec = 6;   // staged 16-byte vectors per thread per pass
 
+template <int SF>
 __global__ __launch_bounds__(1024) void dec1_k4_down_kernel(DecArgs a, const float* topk_w, float* y) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
@@ -903,15 +1025,16 @@ __global__ __launch_bounds__(1024) void dec1_k4_down_kernel(DecArgs a, const flo
       dn_load4(P[i], tile_rsrc(tile, ue[i] >= 0 ? (int)tb : 0), lane);
     }
   };
-  u32x4 sraw[4];
+  constexpr int kSTile = shared_tile_bytes<SF>();
+  ShQuarter sraw;
   int s_kc = -1, s_kb0 = 0;
   auto issue_shared = [&](int su) {
     const bool valid = su < n_sunits;
     s_kc = valid ? su >> 1 : -1;
     s_kb0 = 4 * (su & 1);
-    const uint8_t* tile = valid ? a.sdown + ((size_t)rt * n_cks + s_kc) * kBf16Tile : a.down;
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kBf16Tile : 0);
-    for (int q = 0; q < 4; ++q) sraw[q] = bload16(rs, 1024 * (s_kb0 + q) + 16 * lane);
+    const uint8_t* tile = valid ? a.sdown + ((size_t)rt * n_cks + s_kc) * kSTile : a.down;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kSTile : 0);
+    sh_dn_load<SF>(sraw, [&](int off) { return bload16(rs, off); }, s_kb0, lane);
   };
 
   // ---- staging of the activations: h vectors, per-16-row sums, shared h
@@ -1025,10 +1148,12 @@ __global__ __launch_bounds__(1024) void dec1_k4_down_kernel(DecArgs a, const flo
     float4v c = zero;
     const _Float16* hbase = hss + s_kc * 256 + g4 * 8;
     for (int q = 0; q < 4; ++q) {
-      const uint8_t* src = (m == 0) ? reinterpret_cast<const uint8_t*>(hbase + (s_kb0 + q) * 32) : zero16;
-      c = mfma_f16(as_half8(load16(src)), bf16x8_to_half8(sraw[q]), c);
+      // BF16: every k-block's activations in A row 0; Q8: k-block kb0 + q's in row q
+      const bool feeds_q = m == (SF == MOE_FMT_Q8 ? q : 0);
+      const uint8_t* src = feeds_q ? reinterpret_cast<const uint8_t*>(hbase + (s_kb0 + q) * 32) : zero16;
+      c = mfma_f16(as_half8(load16(src)), sh_dn_b<SF>(sraw, q), c);
     }
-    acc += c[0];
+    acc += sh_dn_sum<SF>(sraw, c, s_kb0);
   }
   // sum the 4 lanes of each output row, then the waves in order
   acc += __shfl_xor(acc, 16);
@@ -1054,6 +1179,7 @@ struct DnDirect {
   float xo;           // lane l < 32: value l of the chunk's 16 (X, O) pairs, else 0
 };
 
+template <int SF>
 __global__ __launch_bounds__(1024) void dec1_down_k2d_kernel(DecArgs a, const float* topk_w, float* y) {
   extern __shared__ __align__(16) uint8_t smem[];
   float* red = reinterpret_cast<float*>(smem);                              // [NW][16]
@@ -1102,20 +1228,29 @@ __global__ __launch_bounds__(1024) void dec1_down_k2d_kernel(DecArgs a, const fl
                                                           : kPast));
     }
   };
-  // shared unit: half a K-chunk (4 k-blocks); lanes m == 0 take their four
-  // 8-column pieces of hs
-  u32x4 sraw[4], shv[4];
+  // shared unit: half a K-chunk (4 k-blocks).  BF16: lanes m == 0 take
+  // their four 8-column pieces of hs (A row 0 for every k-block); Q8: lanes
+  // m < 4 take the piece of k-block kb0 + m (A row m for k-block kb0 + m).
+  constexpr int kSTile = shared_tile_bytes<SF>();
+  constexpr int kShv = SF == MOE_FMT_Q8 ? 1 : 4;
+  ShQuarter sraw;
+  u32x4 shv[kShv];
   int s_kc = -1, s_kb0 = 0;
   auto issue_shared = [&](int su) {
     const bool valid = su < n_sunits;
     s_kc = valid ? su >> 1 : -1;
     s_kb0 = 4 * (su & 1);
-    const uint8_t* tile = valid ? a.sdown + ((size_t)rt * n_cks + s_kc) * kBf16Tile : a.down;
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kBf16Tile : 0);
-    for (int q = 0; q < 4; ++q) sraw[q] = bload16(rs, 1024 * (s_kb0 + q) + 16 * lane);
-    for (int q = 0; q < 4; ++q) {
-      const int col = s_kc * 256 + (s_kb0 + q) * 32 + g4 * 8;
-      shv[q] = bload16(hrs, (valid && m == 0 && col < Is) ? off_hs + col * 2 : kPast);
+    const uint8_t* tile = valid ? a.sdown + ((size_t)rt * n_cks + s_kc) * kSTile : a.down;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, valid ? kSTile : 0);
+    sh_dn_load<SF>(sraw, [&](int off) { return bload16(rs, off); }, s_kb0, lane);
+    if constexpr (SF == MOE_FMT_Q8) {
+      const int col = s_kc * 256 + (s_kb0 + (m & 3)) * 32 + g4 * 8;
+      shv[0] = bload16(hrs, (valid && m < 4 && col < Is) ? off_hs + col * 2 : kPast);
+    } else {
+      for (int q = 0; q < 4; ++q) {
+        const int col = s_kc * 256 + (s_kb0 + q) * 32 + g4 * 8;
+        shv[q] = bload16(hrs, (valid && m == 0 && col < Is) ? off_hs + col * 2 : kPast);
+      }
     }
   };
   issue_shared(wave);
@@ -1157,8 +1292,11 @@ __global__ __launch_bounds__(1024) void dec1_down_k2d_kernel(DecArgs a, const fl
   for (int su = wave; su < n_sunits; su += NW) {
     if (su != wave) issue_shared(su);
     float4v c = zero;
-    for (int q = 0; q < 4; ++q) c = mfma_f16(as_half8(m == 0 ? shv[q] : z4), bf16x8_to_half8(sraw[q]), c);
-    acc += c[0];
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 av = SF == MOE_FMT_Q8 ? (m == q ? shv[0] : z4) : (m == 0 ? shv[q % kShv] : z4);
+      c = mfma_f16(as_half8(av), sh_dn_b<SF>(sraw, q), c);
+    }
+    acc += sh_dn_sum<SF>(sraw, c, s_kb0);
   }
   // sum the 4 lanes of each output row, then the waves in order
   acc += __shfl_xor(acc, 16);
@@ -1192,8 +1330,9 @@ size_t dec1_cb2_upgate_lds(int nw, bool route) {
          (size_t)nw * 4 + (route ? 16 * 4 + sizeof(qmoe_route::TopkLds) : 0);
 }
 
-hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,
-                       int cus, hipStream_t s) {
+template <int SF>
+static hipError_t launch_dec1_sf(const DecArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,
+                                 int cus, hipStream_t s) {
   hipError_t err;
   const int n_chunks = a.H / 256;
   if (fmt_ug == MOE_FMT_K4) {
@@ -1201,11 +1340,11 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* to
     const int U_s = 2 * (a.Is / 16), U_r = a.k * (a.I / 16);
     const int most = U_s > U_r ? U_s : U_r;
     const int grid = most < cus ? most : cus;
-    err = ensure_dyn_lds((const void*)dec1_k4_upgate_kernel);
+    err = ensure_dyn_lds((const void*)dec1_k4_upgate_kernel<SF>);
     if (err != hipSuccess) return err;
     const size_t lds = dec1_k4_upgate_lds(a.H, nw);
     err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
-      hipExtLaunchKernelGGL(dec1_k4_upgate_kernel, dim3(grid), dim3(64 * nw), lds, s, ev0_, ev1_, 0, a);
+      hipExtLaunchKernelGGL(dec1_k4_upgate_kernel<SF>, dim3(grid), dim3(64 * nw), lds, s, ev0_, ev1_, 0, a);
     });
   } else if (fmt_ug == MOE_FMT_CB2 && n_chunks <= 16) {
     const int nw = n_chunks < 4 ? 4 : n_chunks;
@@ -1213,7 +1352,7 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* to
     const int most = U_s > U_r ? U_s : U_r;
     const int grid = most < cus ? most : cus;
     const bool route = a.logits != nullptr;
-    void (*fk)(DecArgs) = route ? dec1_cb2_upgate_kernel<true> : dec1_cb2_upgate_kernel<false>;
+    void (*fk)(DecArgs) = route ? dec1_cb2_upgate_kernel<true, SF> : dec1_cb2_upgate_kernel<false, SF>;
     err = ensure_dyn_lds((const void*)fk);
     if (err != hipSuccess) return err;
     const size_t lds = dec1_cb2_upgate_lds(nw, route);
@@ -1226,11 +1365,11 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* to
     const int nw_ug = (n_chunks + kCpw - 1) / kCpw;
     const int64_t items = (int64_t)a.k * (a.I / 16) + a.Is / 16;
     const int grid_ug = (int)(items < cus ? items : cus);
-    err = ensure_dyn_lds((const void*)dec1_cb2_wide_upgate_kernel);
+    err = ensure_dyn_lds((const void*)dec1_cb2_wide_upgate_kernel<SF>);
     if (err != hipSuccess) return err;
     const size_t lds_ug = dec1_cb2_wide_upgate_lds(nw_ug);
     err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
-      hipExtLaunchKernelGGL(dec1_cb2_wide_upgate_kernel, dim3(grid_ug), dim3(64 * nw_ug), lds_ug, s, ev0_, ev1_, 0, a);
+      hipExtLaunchKernelGGL(dec1_cb2_wide_upgate_kernel<SF>, dim3(grid_ug), dim3(64 * nw_ug), lds_ug, s, ev0_, ev1_, 0, a);
     });
   }
   if (err != hipSuccess) return err;
@@ -1238,13 +1377,19 @@ hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* to
   // compute units in one round, else 8 so that two workgroups share a CU and
   // the tiles run in a single round (H = 7168: 26.6 us instead of 33.3 us)
   const int nw_dn = a.H / 16 > cus ? 8 : 16;
-  void (*fd)(DecArgs, const float*, float*) = fmt_dn == MOE_FMT_K2 ? dec1_down_k2d_kernel : dec1_k4_down_kernel;
+  void (*fd)(DecArgs, const float*, float*) = fmt_dn == MOE_FMT_K2 ? dec1_down_k2d_kernel<SF> : dec1_k4_down_kernel<SF>;
   err = ensure_dyn_lds((const void*)fd);
   if (err != hipSuccess) return err;
   const size_t lds_dn = dec1_down_lds(a, fmt_dn, nw_dn);
   return launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
     hipExtLaunchKernelGGL(fd, dim3(a.H / 16), dim3(64 * nw_dn), lds_dn, s, ev0_, ev1_, 0, a, topk_w, y);
   });
+}
+
+hipError_t launch_dec1(const DecArgs& a, int fmt_ug, int fmt_dn, const float* topk_w, float* y,
+                       int cus, hipStream_t s) {
+  return a.fmt_s == MOE_FMT_Q8 ? launch_dec1_sf<MOE_FMT_Q8>(a, fmt_ug, fmt_dn, topk_w, y, cus, s)
+                               : launch_dec1_sf<MOE_FMT_BF16>(a, fmt_ug, fmt_dn, topk_w, y, cus, s);
 }
 
 }  // namespace qmoe

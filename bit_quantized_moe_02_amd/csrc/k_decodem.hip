@@ -97,6 +97,7 @@ struct UgPayM {
   bool ok;
 };
 
+template <int SF>
 __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* tab = smem;                                                      // CB2 table, LDS offset 0
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
 
   build_expert_list(a.topk_idx, T * k, k, a.E, L);
   const int64_t n_r = (int64_t)L->n * n_rt;
-  const int64_t w_r = (int64_t)2 * kCb2Tile * n_chunks, w_s = (int64_t)2 * kBf16Tile * n_chunks;
+  const int64_t w_r = (int64_t)2 * kCb2Tile * n_chunks, w_s = (int64_t)2 * a.tb_s * n_chunks;
   const int64_t lo = item_start(blockIdx.x, gridDim.x, n_rts, w_s, n_r, w_r);
   const int64_t hi = item_start(blockIdx.x + 1, gridDim.x, n_rts, w_s, n_r, w_r);
 
@@ -198,8 +199,8 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
         g += red[(((b * NW + w) * 2 + 1) * 64 + cl) * 4 + ci];
       }
       const int64_t item = first + b;
-      // (shared items took raw bf16 x, routed ones x 2^-e)
-      const _Float16 h16 = h_of(g, u, item < n_rts ? 0 : xe16[mm], xe16[mm]);
+      // (BF16 shared items took raw bf16 x; Q8 shared and routed ones x 2^-e)
+      const _Float16 h16 = h_of(g, u, (SF == MOE_FMT_BF16 && item < n_rts) ? 0 : xe16[mm], xe16[mm]);
       if (mm < T) {
         if (item < n_rts) {
           a.hs[(size_t)mm * a.Is + item * 16 + nn] = h16;
@@ -230,22 +231,40 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
     }
   };
 
-  // shared row tiles: x (bf16) x bf16 weights on bf16 matrix cores, one
-  // matrix at a time
+  half8 A[8];
+  auto make_a = [&]() {
+    for (int kb = 0; kb < 8; ++kb) A[kb] = active ? bf16x8_to_half8_exp(xr[kb], xe) : as_half8(u32x4{0u, 0u, 0u, 0u});
+  };
+  if constexpr (SF == MOE_FMT_Q8) make_a();
+  // shared row tiles, one matrix at a time.  BF16: x (bf16) x bf16 weights
+  // on bf16 matrix cores.  Q8: x 2^-e (fp16) x the exact codes, each
+  // k-block's dots times row n's scale in fp32.
   const int64_t s_hi = min(hi, (int64_t)n_rts);
   for (int64_t item = lo; item < s_hi; ++item) {
     float4v c[2] = {zero, zero};
     for (int mat = 0; mat < 2; ++mat) {
-      const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)item * n_chunks + chunk) * kBf16Tile;
-      u32x4 raw[8];
-      for (int kb = 0; kb < 8; ++kb) raw[kb] = load16(tile + 1024 * kb + 16 * lane);
-      for (int kb = 0; kb < 8; ++kb) c[mat] = mfma_bf16(active ? xr[kb] : u32x4{0u, 0u, 0u, 0u}, raw[kb], c[mat]);
+      if constexpr (SF == MOE_FMT_Q8) {
+        const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)item * n_chunks + chunk) * kQ8Tile;
+        u32x4 raw[4];
+        for (int i = 0; i < 4; ++i) raw[i] = load16(tile + 1024 * i + 16 * lane);
+        const u32x4 scl = load16(tile + q8_scale_off(n));
+        for (int kb = 0; kb < 8; ++kb) {
+          const u32x4 pc = raw[2 * (kb & 1) + (kb >> 2)];
+          const half8 b = ((kb >> 1) & 1) ? q8_codes(pc.z, pc.w) : q8_codes(pc.x, pc.y);
+          const float4v ct = mfma_f16(A[kb], b, zero);
+          c[mat] += h2f((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu) * ct;
+        }
+      } else {
+        const uint8_t* tile = (mat ? a.sgate : a.sup) + ((size_t)item * n_chunks + chunk) * kBf16Tile;
+        u32x4 raw[8];
+        for (int kb = 0; kb < 8; ++kb) raw[kb] = load16(tile + 1024 * kb + 16 * lane);
+        for (int kb = 0; kb < 8; ++kb) c[mat] = mfma_bf16(active ? xr[kb] : u32x4{0u, 0u, 0u, 0u}, raw[kb], c[mat]);
+      }
     }
     done_item(item, c[0], c[1]);
   }
   // routed items, the next two items' weights in flight
-  half8 A[8];
-  for (int kb = 0; kb < 8; ++kb) A[kb] = active ? bf16x8_to_half8_exp(xr[kb], xe) : as_half8(u32x4{0u, 0u, 0u, 0u});
+  if constexpr (SF != MOE_FMT_Q8) make_a();
   auto compute = [&](const UgPayM& P, int64_t item) {
     float4v cu = zero, cg = zero;
     if (P.ok) {
@@ -288,6 +307,7 @@ struct DnRound {
   uint32_t dd[kDnR];
 };
 
+template <int SF>
 __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
@@ -308,7 +328,7 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
   const int m = lane & 15, qq = lane >> 4, n = lane & 15;
   build_expert_list(a.topk_idx, T * k, k, a.E, L);
   const int64_t n_r = (int64_t)L->n * n_rt;
-  const int64_t w_r = (int64_t)kK2Tile * n_ck, w_s = (int64_t)kBf16Tile * n_cks;
+  const int64_t w_r = (int64_t)kK2Tile * n_ck, w_s = (int64_t)a.tb_s * n_cks;
   const int64_t lo = item_start(blockIdx.x, gridDim.x, n_rts, w_s, n_r, w_r);
   const int64_t hi = item_start(blockIdx.x + 1, gridDim.x, n_rts, w_s, n_r, w_r);
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -388,19 +408,33 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
     __syncthreads();
   };
 
-  // shared row tiles: h_s (fp16) x bf16 weights converted to fp16
+  // shared row tiles: h_s (fp16) x bf16 weights converted to fp16, or x the
+  // exact Q8 codes with each k-block's dots times row n's scale in fp32
   const int64_t s_hi = min(hi, (int64_t)n_rts);
   if (lo < s_hi) stage(-1);
   const bool s_active = wave < n_cks;
   for (int64_t item = lo; item < s_hi; ++item) {
     float4v acc[1] = {zero};
     if (s_active) {
-      const uint8_t* tile = a.sdown + ((size_t)item * n_cks + wave) * kBf16Tile;
-      u32x4 raw[8];
-      for (int kb = 0; kb < 8; ++kb) raw[kb] = load16(tile + 1024 * kb + 16 * lane);
-      for (int kb = 0; kb < 8; ++kb) {
-        const half8 av = as_half8(*reinterpret_cast<const u32x4*>(hA + (size_t)m * kmax + wave * 256 + kb * 32 + qq * 8));
-        acc[0] = mfma_f16(av, bf16x8_to_half8(raw[kb]), acc[0]);
+      if constexpr (SF == MOE_FMT_Q8) {
+        const uint8_t* tile = a.sdown + ((size_t)item * n_cks + wave) * kQ8Tile;
+        u32x4 raw[4];
+        for (int i = 0; i < 4; ++i) raw[i] = load16(tile + 1024 * i + 16 * lane);
+        const u32x4 scl = load16(tile + q8_scale_off(n));
+        for (int kb = 0; kb < 8; ++kb) {
+          const half8 av = as_half8(*reinterpret_cast<const u32x4*>(hA + (size_t)m * kmax + wave * 256 + kb * 32 + qq * 8));
+          const u32x4 pc = raw[2 * (kb & 1) + (kb >> 2)];
+          const half8 b = ((kb >> 1) & 1) ? q8_codes(pc.z, pc.w) : q8_codes(pc.x, pc.y);
+          acc[0] += h2f((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu) * mfma_f16(av, b, zero);
+        }
+      } else {
+        const uint8_t* tile = a.sdown + ((size_t)item * n_cks + wave) * kBf16Tile;
+        u32x4 raw[8];
+        for (int kb = 0; kb < 8; ++kb) raw[kb] = load16(tile + 1024 * kb + 16 * lane);
+        for (int kb = 0; kb < 8; ++kb) {
+          const half8 av = as_half8(*reinterpret_cast<const u32x4*>(hA + (size_t)m * kmax + wave * 256 + kb * 32 + qq * 8));
+          acc[0] = mfma_f16(av, bf16x8_to_half8(raw[kb]), acc[0]);
+        }
       }
     }
     finish(acc, 1, item, n_cks, -1);
@@ -528,16 +562,19 @@ hipError_t launch_decm(const DecArgs& a, const float* topk_w, float* y, int cus,
   int nw_dn = n_ck > n_cks ? n_ck : n_cks;
   if (nw_dn < 4) nw_dn = 4;
   if (nw_ug > 16 || nw_dn > 8) return hipErrorInvalidValue;   // H <= 4096, I and I_s <= 2048
-  hipError_t err = ensure_dyn_lds((const void*)decm_upgate_kernel);
+  const bool q8 = a.fmt_s == MOE_FMT_Q8;
+  void (*fu)(DecArgs) = q8 ? decm_upgate_kernel<MOE_FMT_Q8> : decm_upgate_kernel<MOE_FMT_BF16>;
+  void (*fd)(DecArgs) = q8 ? decm_down_kernel<MOE_FMT_Q8> : decm_down_kernel<MOE_FMT_BF16>;
+  hipError_t err = ensure_dyn_lds((const void*)fu);
   if (err != hipSuccess) return err;
   err = launch_timed(MOE_KERNEL_DECODE_UPGATE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
-    hipExtLaunchKernelGGL(decm_upgate_kernel, dim3(cus), dim3(64 * nw_ug), decm_upgate_lds(nw_ug), s, ev0_, ev1_, 0, a);
+    hipExtLaunchKernelGGL(fu, dim3(cus), dim3(64 * nw_ug), decm_upgate_lds(nw_ug), s, ev0_, ev1_, 0, a);
   });
   if (err != hipSuccess) return err;
-  err = ensure_dyn_lds((const void*)decm_down_kernel);
+  err = ensure_dyn_lds((const void*)fd);
   if (err != hipSuccess) return err;
   err = launch_timed(MOE_KERNEL_DECODE_DOWN, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {
-    hipExtLaunchKernelGGL(decm_down_kernel, dim3(cus), dim3(64 * nw_dn), decm_down_lds(a, nw_dn), s, ev0_, ev1_, 0, a);
+    hipExtLaunchKernelGGL(fd, dim3(cus), dim3(64 * nw_dn), decm_down_lds(a, nw_dn), s, ev0_, ev1_, 0, a);
   });
   if (err != hipSuccess) return err;
   return launch_timed(MOE_KERNEL_DECODE_COMBINE, s, [&](hipEvent_t ev0_, hipEvent_t ev1_) {

@@ -75,6 +75,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* packed, int
         const float mn = (float)k4_scale_value(s0, s1, s2, 8 + kb);
         for (int j = 0; j < 8; ++j) orow[kb * 32 + j] = fmaf(-dmin, mn, dsc * ((float)v[j] - 1024.0f));
       }
+    } else if (FMT == MOE_FMT_Q8) {
+      const uint8_t* tile = packed + tile_i * kQ8Tile;
+      const u32x4 scl = load16(tile + q8_scale_off(n));
+      for (int kb = 0; kb < 8; ++kb) {
+        const uint32_t* cp = reinterpret_cast<const uint32_t*>(tile + q8_code_off(kb, lane));
+        const half8 v = q8_codes(cp[0], cp[1]);
+        const float d = h2f((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu);
+        for (int j = 0; j < 8; ++j) orow[kb * 32 + j] = d * (float)v[j];
+      }
     } else {
       const uint8_t* tile = packed + tile_i * kBf16Tile;
       for (int kb = 0; kb < 8; ++kb) {
@@ -250,6 +259,7 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, int64_t rows, int64_t 
     case MOE_FMT_CB2: fn = dequant_kernel<MOE_FMT_CB2>; break;
     case MOE_FMT_K2: fn = dequant_kernel<MOE_FMT_K2>; break;
     case MOE_FMT_K4: fn = dequant_kernel<MOE_FMT_K4>; break;
+    case MOE_FMT_Q8: fn = dequant_kernel<MOE_FMT_Q8>; break;
     default: fn = dequant_kernel<MOE_FMT_BF16>; break;
   }
   if (lds > 0) {

@@ -18,9 +18,10 @@ struct PfArgs {
   const uint8_t* gate;
   const uint8_t* down;
   size_t expert_bytes, expert_bytes_down;
-  const uint8_t* sup;
+  const uint8_t* sup;             // shared expert, BF16 or Q8 tiles (fmt_s)
   const uint8_t* sgate;
   const uint8_t* sdown;
+  int fmt_s, tb_s;
   const int8_t* codebook;
   // workspace
   _Float16* h;                    // [T*k][I]  fp16, grouped (position) order

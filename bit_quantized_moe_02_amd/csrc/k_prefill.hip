@@ -284,6 +284,25 @@ __device__ __forceinline__ u32x4 bf16_piece(const uint8_t* tile, int kk, int lan
   return load16(tile + 1024 * kb + 16 * (16 * qq + n));
 }
 
+// Q8 tiles: the same lane's 8 codes for step kk and their fp16 scale, as
+// {codes 0-3, codes 4-7, scale bits, 0}; q8_piece_b turns them into the
+// B operand fp16(d q), the fp16 value of each dequantized weight.
+__device__ __forceinline__ u32x4 q8_piece(const uint8_t* tile, int kk, int lane) {
+  const int n = lane & 15, hl = lane >> 5, kb = kk >> 1, qq = 2 * (kk & 1) + hl;
+  const uint32_t* cp = reinterpret_cast<const uint32_t*>(tile + q8_code_off(kb, 16 * qq + n));
+  const uint16_t d = *reinterpret_cast<const uint16_t*>(tile + q8_scale_off(n) + 2 * kb);
+  return u32x4{cp[0], cp[1], (uint32_t)d, 0u};
+}
+__device__ __forceinline__ half8 q8_piece_b(const u32x4& p) { return q8_fold(p.x, p.y, p.z); }
+
+template <int SF>
+__device__ __forceinline__ u32x4 shared_piece(const uint8_t* tile, int kk, int lane) {
+  if constexpr (SF == MOE_FMT_Q8) return q8_piece(tile, kk, lane);
+  else return bf16_piece(tile, kk, lane);
+}
+template <int SF>
+constexpr int shared_tile_bytes() { return SF == MOE_FMT_Q8 ? kQ8Tile : kBf16Tile; }
+
 __device__ __forceinline__ float16v zero16v() {
   float16v z;
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
@@ -471,25 +490,39 @@ __device__ __forceinline__ void ug_routed(const PfArgs& a, uint8_t* smem, int e,
   }
 }
 
-// Up/gate, shared expert (bf16 x bf16 on bf16 matrix cores): one (96-token
-// chunk, 256-row N-tile of I_s) per workgroup.  Weights stream two steps at
-// a time, the next two steps' loads in flight.
-template <int MTA>
+// Up/gate, shared expert: one (96-token chunk, 256-row N-tile of I_s) per
+// workgroup.  BF16: raw bf16 x times bf16 weights on bf16 matrix cores.  Q8:
+// the fp16 copy of x (x 2^-e) times fp16(d q).  Weights stream two steps at a
+// time, the next two steps' loads in flight.
+template <int MTA, int SF>
 __device__ __forceinline__ void ug_shared_steps(float16v (&acc)[2][kUgTiles][kMT], const u32x4 (&cu)[kUgTiles][2],
                                                 const u32x4 (&cg)[kUgTiles][2], const uint8_t* buf, int k0, int lane) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < 2; ++q) {
+    half8 bu[kUgTiles], bg[kUgTiles];
+    if constexpr (SF == MOE_FMT_Q8)
+      for (int b = 0; b < kUgTiles; ++b) {
+        bu[b] = q8_piece_b(cu[b][q]);
+        bg[b] = q8_piece_b(cg[b][q]);
+      }
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt) {
-      const u32x4 av = as_u32x4(a_read(buf, mt, k0 + q, lane));
+      const half8 av = a_read(buf, mt, k0 + q, lane);
 #pragma unroll
       for (int b = 0; b < kUgTiles; ++b) {
-        acc[0][b][mt] = mfma32_bf(av, cu[b][q], acc[0][b][mt]);
-        acc[1][b][mt] = mfma32_bf(av, cg[b][q], acc[1][b][mt]);
+        if constexpr (SF == MOE_FMT_Q8) {
+          acc[0][b][mt] = mfma32(av, bu[b], acc[0][b][mt]);
+          acc[1][b][mt] = mfma32(av, bg[b], acc[1][b][mt]);
+        } else {
+          acc[0][b][mt] = mfma32_bf(as_u32x4(av), cu[b][q], acc[0][b][mt]);
+          acc[1][b][mt] = mfma32_bf(as_u32x4(av), cg[b][q], acc[1][b][mt]);
+        }
       }
     }
+  }
 }
 
+template <int SF>
 __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc, int nt) {
   const int64_t p_begin = (int64_t)mc * kMRows, p_end = min((int64_t)a.T, p_begin + kMRows);
   if (p_begin >= p_end) return;
@@ -502,8 +535,8 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
   const uint8_t* tg[kUgTiles];
   for (int b = 0; b < kUgTiles; ++b) {
     const int rt_l = min((row0 + 32 * b) / 16 + ((lane & 31) >> 4), n_rt - 1);
-    tu[b] = a.sup + (size_t)rt_l * n_chunks * kBf16Tile;
-    tg[b] = a.sgate + (size_t)rt_l * n_chunks * kBf16Tile;
+    tu[b] = a.sup + (size_t)rt_l * n_chunks * shared_tile_bytes<SF>();
+    tg[b] = a.sgate + (size_t)rt_l * n_chunks * shared_tile_bytes<SF>();
   }
   const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
   int rows[dma_per_wave<kUgWaves>()];
@@ -513,11 +546,12 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
     for (int mt = 0; mt < kMT; ++mt) acc[0][b][mt] = acc[1][b][mt] = zero16v();
   u32x4 cu[kUgTiles][2], cg[kUgTiles][2], nu[kUgTiles][2], ng[kUgTiles][2];
   __syncthreads();
-  a_dma<kUgWaves>(stage, a.x, a.H, rows, 0, a.H);
+  const uint16_t* xsrc = SF == MOE_FMT_Q8 ? a.x16 : a.x;
+  a_dma<kUgWaves>(stage, xsrc, a.H, rows, 0, a.H);
   for (int b = 0; b < kUgTiles; ++b)
     for (int q = 0; q < 2; ++q) {
-      cu[b][q] = bf16_piece(tu[b], q, lane);
-      cg[b][q] = bf16_piece(tg[b], q, lane);
+      cu[b][q] = shared_piece<SF>(tu[b], q, lane);
+      cg[b][q] = shared_piece<SF>(tg[b], q, lane);
     }
   const int n_pairs = 8 * n_chunks;
   for (int gp = 0; gp < n_pairs; ++gp) {
@@ -525,20 +559,20 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
     const uint8_t* buf = stage + (chunk & 1) * kChunkBytes;
     if ((gp & 7) == 0) {
       chunk_sync();
-      if (chunk + 1 < n_chunks) a_dma<kUgWaves>(stage + ((chunk + 1) & 1) * kChunkBytes, a.x, a.H, rows, (chunk + 1) * 256, a.H);
+      if (chunk + 1 < n_chunks) a_dma<kUgWaves>(stage + ((chunk + 1) & 1) * kChunkBytes, xsrc, a.H, rows, (chunk + 1) * 256, a.H);
     }
     if (gp + 1 < n_pairs) {
       const int c1 = (gp + 1) >> 3, k1 = 2 * ((gp + 1) & 7);
       for (int b = 0; b < kUgTiles; ++b)
         for (int q = 0; q < 2; ++q) {
-          nu[b][q] = bf16_piece(tu[b] + (size_t)c1 * kBf16Tile, k1 + q, lane);
-          ng[b][q] = bf16_piece(tg[b] + (size_t)c1 * kBf16Tile, k1 + q, lane);
+          nu[b][q] = shared_piece<SF>(tu[b] + (size_t)c1 * shared_tile_bytes<SF>(), k1 + q, lane);
+          ng[b][q] = shared_piece<SF>(tg[b] + (size_t)c1 * shared_tile_bytes<SF>(), k1 + q, lane);
         }
     }
     if (active) {
-      if (mta >= 3) ug_shared_steps<3>(acc, cu, cg, buf, k0, lane);
-      else if (mta == 2) ug_shared_steps<2>(acc, cu, cg, buf, k0, lane);
-      else ug_shared_steps<1>(acc, cu, cg, buf, k0, lane);
+      if (mta >= 3) ug_shared_steps<3, SF>(acc, cu, cg, buf, k0, lane);
+      else if (mta == 2) ug_shared_steps<2, SF>(acc, cu, cg, buf, k0, lane);
+      else ug_shared_steps<1, SF>(acc, cu, cg, buf, k0, lane);
     }
     for (int b = 0; b < kUgTiles; ++b)
       for (int q = 0; q < 2; ++q) {
@@ -552,7 +586,11 @@ __device__ __forceinline__ void ug_shared(const PfArgs& a, uint8_t* smem, int mc
     for (int mt = 0; mt < kMT; ++mt)
       for (int i = 0; i < 16; ++i) {
         const int64_t p = p_begin + 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (p < p_end) a.hs[p * a.Is + row] = h_of(acc[1][b][mt][i], acc[0][b][mt][i], 0, a.xexp[p]);   // raw bf16 x
+        if (p < p_end) {
+          // BF16 took raw bf16 x, Q8 x 2^-e
+          const int e = a.xexp[p];
+          a.hs[p * a.Is + row] = h_of(acc[1][b][mt][i], acc[0][b][mt][i], SF == MOE_FMT_Q8 ? e : 0, e);
+        }
       }
   }
 }
@@ -584,7 +622,8 @@ __global__ __launch_bounds__(64 * kUgWaves) void pf_upgate_kernel(PfArgs a) {
     ug_routed<FMT>(a, smem, g - n_sh, nt);
   } else {
     if (nt * kUgRowsPerWg >= a.Is) return;
-    ug_shared(a, smem, g, nt);
+    if (a.fmt_s == MOE_FMT_Q8) ug_shared<MOE_FMT_Q8>(a, smem, g, nt);
+    else ug_shared<MOE_FMT_BF16>(a, smem, g, nt);
   }
 }
 
@@ -714,15 +753,16 @@ __device__ __forceinline__ void dn_routed(const PfArgs& a, uint8_t* smem, int e,
   }
 }
 
-// Shared expert down: hs (fp16) x bf16 weights converted to fp16 in
-// registers, weights streamed a quarter chunk at a time.
-template <int MTA>
+// Shared expert down: hs (fp16) x bf16 weights converted to fp16, or
+// fp16(d q) of Q8 weights, in registers, weights streamed a quarter chunk at
+// a time.
+template <int MTA, int SF>
 __device__ __forceinline__ void dn_shared_steps(float16v (&acc)[kDnTiles][kMT], const u32x4 (&cw)[kDnTiles][4],
                                                 const uint8_t* buf, int q0, int lane) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     half8 bw[kDnTiles];
-    for (int b = 0; b < kDnTiles; ++b) bw[b] = bf16x8_to_half8(cw[b][q]);
+    for (int b = 0; b < kDnTiles; ++b) bw[b] = SF == MOE_FMT_Q8 ? q8_piece_b(cw[b][q]) : bf16x8_to_half8(cw[b][q]);
 #pragma unroll
     for (int mt = 0; mt < MTA; ++mt) {
       const half8 av = a_read(buf, mt, q0 + q, lane);
@@ -731,6 +771,7 @@ __device__ __forceinline__ void dn_shared_steps(float16v (&acc)[kDnTiles][kMT], 
   }
 }
 
+template <int SF>
 __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc, int nt) {
   const int64_t p_begin = (int64_t)mc * kMRows, p_end = min((int64_t)a.T, p_begin + kMRows);
   if (p_begin >= p_end) return;
@@ -742,7 +783,7 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
   for (int b = 0; b < kDnTiles; ++b) {
     rt0[b] = (nt * kDnRowsPerWg + wave * 32 * kDnTiles + 32 * b) / 16;
     const int rt_l = min(rt0[b] + ((lane & 31) >> 4), n_rt - 1);
-    tp[b] = a.sdown + (size_t)rt_l * n_chunks * kBf16Tile;
+    tp[b] = a.sdown + (size_t)rt_l * n_chunks * shared_tile_bytes<SF>();
   }
   const uint16_t* hsrc = reinterpret_cast<const uint16_t*>(a.hs);
   const int mta = (int)min((int64_t)kMT, (p_end - p_begin + 31) / 32);
@@ -754,7 +795,7 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
   a_dma<kDnWaves>(stage, hsrc, a.Is, rows, 0, a.Is);
   u32x4 cw[kDnTiles][4], nw[kDnTiles][4];
   for (int b = 0; b < kDnTiles; ++b)
-    for (int q = 0; q < 4; ++q) cw[b][q] = bf16_piece(tp[b], q, lane);
+    for (int q = 0; q < 4; ++q) cw[b][q] = shared_piece<SF>(tp[b], q, lane);
   const int n_quarters = 4 * n_chunks;
   for (int gq = 0; gq < n_quarters; ++gq) {
     const int chunk = gq >> 2, q0 = 4 * (gq & 3);
@@ -766,11 +807,11 @@ __device__ __forceinline__ void dn_shared(const PfArgs& a, uint8_t* smem, int mc
     if (gq + 1 < n_quarters) {
       const int c1 = (gq + 1) >> 2, k1 = 4 * ((gq + 1) & 3);
       for (int b = 0; b < kDnTiles; ++b)
-        for (int q = 0; q < 4; ++q) nw[b][q] = bf16_piece(tp[b] + (size_t)c1 * kBf16Tile, k1 + q, lane);
+        for (int q = 0; q < 4; ++q) nw[b][q] = shared_piece<SF>(tp[b] + (size_t)c1 * shared_tile_bytes<SF>(), k1 + q, lane);
     }
-    if (mta >= 3) dn_shared_steps<3>(acc, cw, buf, q0, lane);
-    else if (mta == 2) dn_shared_steps<2>(acc, cw, buf, q0, lane);
-    else dn_shared_steps<1>(acc, cw, buf, q0, lane);
+    if (mta >= 3) dn_shared_steps<3, SF>(acc, cw, buf, q0, lane);
+    else if (mta == 2) dn_shared_steps<2, SF>(acc, cw, buf, q0, lane);
+    else dn_shared_steps<1, SF>(acc, cw, buf, q0, lane);
     for (int b = 0; b < kDnTiles; ++b)
       for (int q = 0; q < 4; ++q) cw[b][q] = nw[b][q];
   }
@@ -793,7 +834,8 @@ __global__ __launch_bounds__(64 * kDnWaves) void pf_down_kernel(PfArgs a) {
   int nt, g;
   if (!pf_tile(n_nt, a.E + n_sh, nt, g)) return;
   if (g >= n_sh) dn_routed<FMT>(a, smem, g - n_sh, nt);
-  else dn_shared(a, smem, g, nt);
+  else if (a.fmt_s == MOE_FMT_Q8) dn_shared<MOE_FMT_Q8>(a, smem, g, nt);
+  else dn_shared<MOE_FMT_BF16>(a, smem, g, nt);
 }
 
 // y[t][h] = sum_j w[t][j] * yslot[slot_pos[t*k + j]][h] + ysh[t][h], summed in

@@ -29,7 +29,8 @@ MOE_FMT_BF16 = 0
 MOE_FMT_CB2 = 1
 MOE_FMT_K2 = 2
 MOE_FMT_K4 = 3
-FMT = {"bf16": MOE_FMT_BF16, "cb2": MOE_FMT_CB2, "k2": MOE_FMT_K2, "k4": MOE_FMT_K4}
+MOE_FMT_Q8 = 4
+FMT = {"bf16": MOE_FMT_BF16, "cb2": MOE_FMT_CB2, "k2": MOE_FMT_K2, "k4": MOE_FMT_K4, "q8": MOE_FMT_Q8}
 
 EXPORTED = [
     "moe_codebook_generate", "moe_packed_bytes", "moe_quantize_pack",
@@ -58,7 +59,7 @@ class MoeWeights(ctypes.Structure):
         ("n_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
         ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
         ("fmt_up", ctypes.c_int32), ("fmt_gate", ctypes.c_int32),
-        ("fmt_down", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("fmt_down", ctypes.c_int32), ("fmt_shared", ctypes.c_int32),
         ("up", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("down", ctypes.c_void_p),
         ("codebook", ctypes.c_void_p),
         ("shared_up", ctypes.c_void_p), ("shared_gate", ctypes.c_void_p),
@@ -278,11 +279,13 @@ class DeviceLayer:
     """Device copies of one layer's packed weights plus the MoeWeights view.
 
     up / gate / down: uint8 device tensors holding E packed matrices back to
-    back; shared_*: BF16-format packed matrices or None; codebook: int8 device
-    tensor [256*8] or None; router: fp32 device tensor [E, H]."""
+    back; shared_*: packed matrices in format `shared_fmt` ("bf16" or "q8")
+    or None; codebook: int8 device tensor [256*8] or None; router: fp32
+    device tensor [E, H]."""
 
     def __init__(self, n_experts, hidden, inter, shared_inter, fmts, up, gate, down, codebook=None,
-                 shared_up=None, shared_gate=None, shared_down=None, router=None, bias=None):
+                 shared_up=None, shared_gate=None, shared_down=None, router=None, bias=None,
+                 shared_fmt="bf16"):
         self.tensors = dict(up=up, gate=gate, down=down, codebook=codebook, shared_up=shared_up,
                             shared_gate=shared_gate, shared_down=shared_down, router=router, bias=bias)
         self.router = router
@@ -292,15 +295,16 @@ class DeviceLayer:
         nb_up, nb_dn = moe_packed_bytes(fmts[0], I, H), moe_packed_bytes(fmts[2], H, I)
         u8 = torch.uint8
         shared = Is > 0
-        self.w = MoeWeights(E, H, I, Is, FMT[fmts[0]], FMT[fmts[1]], FMT[fmts[2]], 0,
+        sf = FMT[shared_fmt]
+        self.w = MoeWeights(E, H, I, Is, FMT[fmts[0]], FMT[fmts[1]], FMT[fmts[2]], sf,
                             _dev(up, "up", u8, E * nb_up), _dev(gate, "gate", u8, E * nb_up),
                             _dev(down, "down", u8, E * nb_dn),
                             _dev(codebook, "codebook", torch.int8, 256 * 8, optional=True),
-                            _dev(shared_up, "shared_up", u8, moe_packed_bytes("bf16", Is, H) if shared else 0,
+                            _dev(shared_up, "shared_up", u8, moe_packed_bytes(sf, Is, H) if shared else 0,
                                  optional=not shared),
-                            _dev(shared_gate, "shared_gate", u8, moe_packed_bytes("bf16", Is, H) if shared else 0,
+                            _dev(shared_gate, "shared_gate", u8, moe_packed_bytes(sf, Is, H) if shared else 0,
                                  optional=not shared),
-                            _dev(shared_down, "shared_down", u8, moe_packed_bytes("bf16", H, Is) if shared else 0,
+                            _dev(shared_down, "shared_down", u8, moe_packed_bytes(sf, H, Is) if shared else 0,
                                  optional=not shared))
         _dev(router, "router", torch.float32, E * H, optional=True)
         _dev(bias, "bias", torch.float32, E, optional=True)

@@ -112,11 +112,24 @@ extern "C" {
  *
  * MOE_FMT_BF16 (unquantized shared expert).  Tile (8192 bytes): element
  *   (n, kb, qq, j) at byte 1024*kb + 16*c + 2*j (c = 16*qq + n), bf16.
+ *
+ * MOE_FMT_Q8 (8-bit shared expert, 8.5 bits/weight; [upppp] "asymmetric
+ *   2-bit quantization": shared experts stay at Q8_0 or F16; [osrepos] the
+ *   "Q8Shared" model file name).  Every 32 weights (n, kb) share one fp16
+ *   scale d; weight = d * q with q a signed 8-bit code in -127..127.
+ *   Tile (4352 bytes):
+ *     [0, 4096)    piece i = 0..3 at 1024*i: lane c at 1024*i + 16*c holds
+ *                  the 8 codes (j = 0..7) of k-block a = 4*(i%2) + i/2, then
+ *                  the 8 codes of k-block a + 2 (int8 each); so k-block kb
+ *                  sits in piece 2*(kb%2) + kb/4, second half when
+ *                  (kb/2) % 2 == 1.
+ *     [4096, 4352) row n at 4096 + 16*n: 8 fp16 scales, kb at byte 2*kb.
  */
 #define MOE_FMT_BF16 0
 #define MOE_FMT_CB2 1
 #define MOE_FMT_K2 2
 #define MOE_FMT_K4 3
+#define MOE_FMT_Q8 4
 
 /* ---------------------------------------------------------------------------
  * Host-only calls (no GPU needed).
@@ -136,8 +149,8 @@ size_t moe_packed_bytes(int fmt, int64_t rows, int64_t k);
 /* Quantizes and packs a host fp32 matrix w [rows, k] (row-major) into
  * out (host, out_bytes >= moe_packed_bytes(fmt, rows, k)): the quantized
  * expert matrices of [digest] "Model weights" (CB2 for up/gate, K2 for down)
- * and [osrepos] "Q4KExperts" (K4), and the unquantized shared expert (BF16,
- * [upppp] "asymmetric 2-bit quantization").  Columns beyond k up to the next
+ * and [osrepos] "Q4KExperts" (K4), and the shared expert (BF16 or Q8,
+ * [upppp] "asymmetric 2-bit quantization"; [osrepos] "Q8Shared").  Columns beyond k up to the next
  * multiple of 256 are taken as zero.
  *   CB2: per 32 weights s = fp16(max|w| / 0.75) (fp64 quotient, one rounding
  *        to fp16); per group the lowest index e minimizing
@@ -148,10 +161,13 @@ size_t moe_packed_bytes(int fmt, int64_t rows, int64_t k);
  *        sc = min(S, floor(a/d + 1/2)), m = min(S, floor(b/dmin + 1/2))
  *        (0 when d or dmin is 0); q = clamp(floor((w + dmin*m)/(d*sc) + 1/2),
  *        0, Q) (0 when d*sc is 0).  K2: Q=3, S=15; K4: Q=15, S=63.
+ *   Q8:  per 32 weights d = fp16(max|w| / 127) (fp64 quotient, one
+ *        rounding); q = sign(w) * min(127, floor(|w|/d + 1/2)) (fp64; 0
+ *        when d is 0).
  *   BF16: each value rounded to bf16 (nearest, ties to even).
  * n_threads <= 0 uses all hardware threads.  Errors: MOE_ERR_INVALID_ARG for
  * NULL pointers, bad shapes, non-finite weights, |w| too large for an fp16
- * scale (CB2 s, K-quant d or dmin would round to infinity), a missing or
+ * scale (CB2 s, Q8 d, K-quant d or dmin would round to infinity), a missing or
  * malformed codebook (CB2) or out_bytes too small; every check runs before
  * the first byte of out is written. */
 int moe_quantize_pack(int fmt, const float* w, int64_t rows, int64_t k,
@@ -166,8 +182,11 @@ int moe_quantize_pack(int fmt, const float* w, int64_t rows, int64_t k,
  *   up, gate: n_experts packed matrices [inter, hidden] back to back, each
  *             moe_packed_bytes(fmt_up, inter, hidden) bytes.
  *   down:     n_experts packed matrices [hidden, inter].
- *   shared_*: MOE_FMT_BF16 packed [shared_inter, hidden] (up, gate) and
- *             [hidden, shared_inter] (down); NULL when shared_inter == 0.
+ *   shared_*: packed [shared_inter, hidden] (up, gate) and
+ *             [hidden, shared_inter] (down) in format fmt_shared; NULL when
+ *             shared_inter == 0.
+ *   fmt_shared: MOE_FMT_BF16 (0, so a zero-initialized field keeps the
+ *             unquantized shared expert) or MOE_FMT_Q8.
  *   codebook: device copy of the 256x8 CB2 table (int8), or NULL if no CB2.
  * Supported: hidden a multiple of 256; inter and shared_inter multiples of
  * 16; (fmt_up, fmt_gate, fmt_down) = (CB2, CB2, K2) or (K4, K4, K4). */
@@ -177,7 +196,7 @@ typedef struct moe_weights {
   int32_t inter;
   int32_t shared_inter;
   int32_t fmt_up, fmt_gate, fmt_down;
-  int32_t reserved;
+  int32_t fmt_shared;
   const void* up;
   const void* gate;
   const void* down;

@@ -24,6 +24,10 @@ blog, server log excerpts):
   prefill_2048      same layer, 2048 tokens, router std 1/64 (logits ~N(0,1))
   k4_h7168          H=7168 I=2048 E=256 k=8, 4-bit K-quant experts,
                     8192-token prefill and 1000 single-token decode steps
+  *_q8              decode_b1, prefill_2048 and the 4-bit decode with the
+                    shared expert in the 8-bit Q8 format (upppp.jp article,
+                    "asymmetric 2-bit quantization": shared experts at Q8_0;
+                    osrepos summary, the "Q8Shared" model file name)
 """
 from __future__ import annotations
 
@@ -66,6 +70,7 @@ class Workload:
     hot_experts: int = 0     # size of the hot set (skewed routing), 0 = none
     hot_bias: float = 0.0    # logit bias added to the hot set
     x_tag: int = TAG_X
+    fmt_shared: str = "bf16"  # shared-expert storage: "bf16" or "q8"
 
     @property
     def fmts(self):
@@ -102,6 +107,16 @@ WORKLOADS = {
     "draft_verify_t3": Workload("draft_verify_t3", 4096, 2048, 256, 8, 2048,
                                 "cb2", "cb2", "k2", seed=1, tokens=3, steps=1000,
                                 x_tag=TAG_X_DRAFT),
+    # the same layers with the shared expert stored in the 8-bit Q8 format
+    # (its fp32 draw quantized directly, no bf16 rounding first)
+    "decode_b1_q8": Workload("decode_b1_q8", 4096, 2048, 256, 8, 2048,
+                             "cb2", "cb2", "k2", seed=1, tokens=1, steps=1000, fmt_shared="q8"),
+    "prefill_2048_q8": Workload("prefill_2048_q8", 4096, 2048, 256, 8, 2048,
+                                "cb2", "cb2", "k2", seed=3, tokens=2048,
+                                router_std=1.0 / 64.0, fmt_shared="q8"),
+    "k4_h7168_decode_q8": Workload("k4_h7168_decode_q8", 7168, 2048, 256, 8, 2048,
+                                   "k4", "k4", "k4", seed=4, tokens=1,
+                                   steps=1000, x_tag=TAG_X_DECODE, fmt_shared="q8"),
 }
 
 
@@ -147,6 +162,16 @@ def expert_weight(w: Workload, which: str, e: int) -> np.ndarray:
     tag = {"up": TAG_UP, "gate": TAG_GATE, "down": TAG_DOWN}[which]
     shape = (w.inter, w.hidden) if which != "down" else (w.hidden, w.inter)
     return normal_f32(w.seed, tag, e, shape, WEIGHT_STD)
+
+
+def shared_weight_f32(w: Workload, which: str) -> np.ndarray:
+    """fp32 draw of the shared expert: up/gate [I_s, H], down [H, I_s] (the
+    "q8" storage quantizes it directly, "bf16" rounds it: shared_weight_bits)."""
+    if w.shared_inter == 0:
+        raise ValueError(f"{w.name} has no shared expert")
+    tag = {"up": TAG_SHARED_UP, "gate": TAG_SHARED_GATE, "down": TAG_SHARED_DOWN}[which]
+    shape = (w.shared_inter, w.hidden) if which != "down" else (w.hidden, w.shared_inter)
+    return normal_f32(w.seed, tag, 0, shape, WEIGHT_STD)
 
 
 def shared_weight_bits(w: Workload, which: str) -> np.ndarray:

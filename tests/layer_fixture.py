@@ -66,11 +66,27 @@ def register(wl: synth.Workload):
     return wl
 
 
-def oracle_shared(wl: synth.Workload):
+def oracle_shared(wl: synth.Workload, fold: bool = False):
+    """fp64 (up, gate, down) of the shared expert: bf16 values, or the Q8
+    format's d*q as the oracle quantizes them; fold=True rounds Q8 weights to
+    fp16 once (the grouped GEMM's fp16(d*q) operands)."""
     if wl.shared_inter == 0:
         return None
+    if wl.fmt_shared == "q8":
+        return _oracle_shared_q8_cached(wl.name, fold)
     return tuple(synth.bf16_bits_to_f32(synth.shared_weight_bits(wl, w)).astype(np.float64)
                  for w in ("up", "gate", "down"))
+
+
+@functools.lru_cache(maxsize=8)
+def _oracle_shared_q8_cached(name: str, fold: bool):
+    wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else _CUSTOM[name]
+    out = []
+    for which in ("up", "gate", "down"):
+        w = synth.shared_weight_f32(wl, which)
+        d = O.dequantize_matrix(O.quantize_matrix("q8", w), k=w.shape[1])
+        out.append(O.f16(d) if fold else d)
+    return tuple(out)
 
 
 def oracle_layer(wl: synth.Workload, x64: np.ndarray, round_h=None):
@@ -106,14 +122,18 @@ def device_layer(wl: synth.Workload, experts=None, device="cuda"):
     sh = [None, None, None]
     if Is > 0:
         for i, which in enumerate(("up", "gate", "down")):
-            wf = synth.bf16_bits_to_f32(synth.shared_weight_bits(wl, which))
-            sh[i] = dev(qmoe.moe_quantize_pack("bf16", wf))
+            if wl.fmt_shared == "q8":
+                sh[i] = dev(qmoe.moe_quantize_pack("q8", synth.shared_weight_f32(wl, which)))
+            else:
+                wf = synth.bf16_bits_to_f32(synth.shared_weight_bits(wl, which))
+                sh[i] = dev(qmoe.moe_quantize_pack("bf16", wf))
     router = dev(synth.router_weight(wl))
     bias = synth.logit_bias(wl)
     bias = dev(bias) if bias is not None else None
     cbd = dev(cb.reshape(-1).copy()) if "cb2" in wl.fmts else None
     return qmoe.DeviceLayer(E, H, I, Is, wl.fmts, dev(up), dev(gate), dev(down), codebook=cbd,
-                            shared_up=sh[0], shared_gate=sh[1], shared_down=sh[2], router=router, bias=bias)
+                            shared_up=sh[0], shared_gate=sh[1], shared_down=sh[2], router=router, bias=bias,
+                            shared_fmt=wl.fmt_shared)
 
 
 def x_bits(wl: synth.Workload, n: int, step: int = 0):

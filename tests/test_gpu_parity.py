@@ -280,10 +280,11 @@ def _check_layer(y, wl, x64, expect_idx=None, mirror_tol=None, round_w=(), prefi
         if round_w:
             # routed weights (matrices round_w: 0 up, 1 gate, 2 down) rounded
             # to fp16 as the kernels hold them; the shared expert's bf16
-            # weights are exact in either form
+            # weights are exact in either form, its Q8 weights enter the
+            # grouped GEMMs as fp16(d q) and the decode kernels exactly
             y_m, _, _ = O.moe_layer(x64, synth.router_weight(wl), synth.logit_bias(wl), wl.top_k,
                                     lambda e: _mirror_expert(wl, e, round_w, prefill),
-                                    shared=oracle_shared(wl), round_h=_mirror_h)
+                                    shared=oracle_shared(wl, fold=prefill), round_h=_mirror_h)
         else:
             y_m, _, _ = oracle_layer(wl, x64, round_h=_mirror_h)
         em = rel_err(y, y_m)

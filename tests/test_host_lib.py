@@ -46,6 +46,7 @@ def test_packed_bytes(q):
     assert q.moe_packed_bytes("k2", 4096, 2048) == 2752512
     assert q.moe_packed_bytes("k4", 2048, 7168) == 8257536
     assert q.moe_packed_bytes("bf16", 16, 100) == 8192
+    assert q.moe_packed_bytes("q8", 2048, 4096) == 128 * 16 * 4352
     assert q.moe_packed_bytes("k2", 256, 128) == 16 * 1 * 1344
     assert q.moe_packed_bytes("cb2", 15, 256) == 0
     assert q.moe_packed_bytes("cb2", 0, 256) == 0
@@ -60,7 +61,7 @@ def _both(q, fmt, w):
     return lib, ora
 
 
-@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4", "bf16"])
+@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4", "bf16", "q8"])
 @pytest.mark.parametrize("rows,k,std", [(16, 256, 0.02), (32, 96, 0.02), (48, 1000, 1.5),
                                         (16, 512, 1e-4), (64, 768, 0.02)])
 def test_pack_bytes_equal_oracle(q, fmt, rows, k, std):
@@ -72,7 +73,7 @@ def test_pack_bytes_equal_oracle(q, fmt, rows, k, std):
     assert np.array_equal(lib, ora), f"{np.sum(lib != ora)} bytes differ"
 
 
-@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4", "bf16"])
+@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4", "bf16", "q8"])
 def test_pack_bytes_independent_of_threads(q, fmt):
     """The host packer splits rows over threads: any thread count (0 = all
     cores) gives the same bytes."""
@@ -84,7 +85,7 @@ def test_pack_bytes_independent_of_threads(q, fmt):
         assert np.array_equal(q.moe_quantize_pack(fmt, w, cb, n_threads=n), ref), n
 
 
-@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4"])
+@pytest.mark.parametrize("fmt", ["cb2", "k2", "k4", "q8"])
 def test_pack_edge_blocks_equal_oracle(q, fmt):
     rng = np.random.default_rng(3)
     w = (rng.standard_normal((32, 512)) * 0.02).astype(np.float32)
@@ -104,6 +105,11 @@ def test_pack_edge_blocks_equal_oracle(q, fmt):
     w[10, ::2] = 1e-3
     w[10, 1::2] = -1e-3                           # alternating signs
     w[11] = rng.choice([-0.03, 0.0, 0.03], 512).astype(np.float32)   # ties in the search
+    # Q8: codes exactly halfway between two grid points (ties away from zero)
+    d = float(np.float16(0.5 / 127))
+    w[12, :32] = [0.5] + [d * (i + 0.5) * (-1) ** i for i in range(31)]
+    w[13, :32] = 178 * 2.0 ** -24                 # fp16-subnormal d whose largest code is clamped
+    w[13, 1] = -63.5 * 2.0 ** -24
     lib, ora = _both(q, fmt, w)
     assert np.array_equal(lib, ora), f"{np.sum(lib != ora)} bytes differ"
 
@@ -141,21 +147,22 @@ def test_quantize_pack_errors(q):
     big[0, 0] = 60000.0
     assert lib.moe_quantize_pack(1, big.ctypes.data, 16, 256, cb.ctypes.data, out.ctypes.data, out.nbytes, 1) == 1
     assert "fp16 scale" in q.moe_last_error()
-    for fmt, val in ((1, 60000.0), (2, 5e6), (3, 7e7), (2, -2e6), (3, -5e6)):
-        # an fp16 scale (CB2 s, K-quant d or dmin) out of range: refused
-        # before any output byte is written
+    names = {1: "cb2", 2: "k2", 3: "k4", 4: "q8"}
+    for fmt, val in ((1, 60000.0), (2, 5e6), (3, 7e7), (2, -2e6), (3, -5e6), (4, 8.4e6), (4, -8.4e6)):
+        # an fp16 scale (CB2 s, Q8 d, K-quant d or dmin) out of range:
+        # refused before any output byte is written
         big = w.copy()
         big[5, 100] = val
-        out_big = np.full(q.moe_packed_bytes({1: "cb2", 2: "k2", 3: "k4"}[fmt], 16, 256), 0xA5, np.uint8)
+        out_big = np.full(q.moe_packed_bytes(names[fmt], 16, 256), 0xA5, np.uint8)
         assert lib.moe_quantize_pack(fmt, big.ctypes.data, 16, 256, cb.ctypes.data, out_big.ctypes.data,
                                      out_big.nbytes, 2) == 1, (fmt, val)
         assert "fp16 scale" in q.moe_last_error()
         assert np.all(out_big == 0xA5), (fmt, val)
     # the largest values whose scales still fit are accepted
-    for fmt, val in ((1, 49000.0), (2, 2.9e6), (3, 4e6)):
+    for fmt, val in ((1, 49000.0), (2, 2.9e6), (3, 4e6), (4, 8.3e6)):
         ok = w.copy()
         ok[5, 100] = val
-        out_ok = np.zeros(q.moe_packed_bytes({1: "cb2", 2: "k2", 3: "k4"}[fmt], 16, 256), np.uint8)
+        out_ok = np.zeros(q.moe_packed_bytes(names[fmt], 16, 256), np.uint8)
         assert lib.moe_quantize_pack(fmt, ok.ctypes.data, 16, 256, cb.ctypes.data, out_ok.ctypes.data,
                                      out_ok.nbytes, 2) == 0, (fmt, val, q.moe_last_error())
     badcb = cb.copy()
@@ -172,7 +179,7 @@ def _fake_weights(q, **kw):
     fails its host-side checks first)."""
     p = 0x10000
     d = dict(n_experts=256, hidden=4096, inter=2048, shared_inter=2048, fmt_up=1, fmt_gate=1, fmt_down=2,
-             reserved=0, up=p, gate=p, down=p, codebook=p, shared_up=p, shared_gate=p, shared_down=p)
+             fmt_shared=0, up=p, gate=p, down=p, codebook=p, shared_up=p, shared_gate=p, shared_down=p)
     d.update(kw)
     return q.MoeWeights(**d)
 
@@ -202,6 +209,9 @@ def test_device_call_argument_errors(q):
     assert dec(ctypes.byref(w), None, 1, 8, P, P, P, P, ws, None) == 1
     w2 = _fake_weights(q, fmt_down=3)
     assert dec(ctypes.byref(w2), P, 1, 8, P, P, P, P, ws, None) == 2               # mixed formats
+    wq = _fake_weights(q, fmt_shared=3)
+    assert dec(ctypes.byref(wq), P, 1, 8, P, P, P, P, ws, None) == 2               # shared format
+    assert "fmt_shared" in q.moe_last_error()
     # whole decode step
     lws = q.moe_layer_decode_workspace_bytes(w, 1, 8)
     assert lws > ws
