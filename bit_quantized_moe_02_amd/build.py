@@ -71,6 +71,45 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-code sanitizer build: AddressSanitizer and UndefinedBehaviorSanitizer
+# on the host side of every translation unit (the packer, and the argument
+# checks, workspace layout and launch code of the C ABI); device code is
+# built as usual.  Every sanitizer flag of a hipcc line carries -Xarch_host.
+# The library needs clang's shared ASan runtime preloaded into the process
+# (sanitizer_runtime() names it); CPU tests only, no GPU.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    clang = os.path.join(os.path.dirname(HIPCC), "..", "lib", "llvm", "bin", "clang++")
+    if not os.path.exists(clang):
+        clang = shutil.which("amdclang++") or "/opt/rocm/llvm/bin/clang++"
+    return subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                          text=True, check=True).stdout.strip()
+
+
+def build_sanitized(out: str) -> str:
+    """Builds the library with host-side ASan + UBSan into `out`."""
+    obj_dir = os.path.join(BUILD, "san")
+    os.makedirs(obj_dir, exist_ok=True)
+    jobs, objs = [], []
+    for src in HOST_SOURCES + DEVICE_SOURCES:
+        obj = os.path.join(obj_dir, src + ".o")
+        flags = HIP_FLAGS + ["-g", "-O1"] + SAN_FLAGS
+        if src in HOST_SOURCES:
+            flags = flags + ["-ffp-contract=off", "-x", "c++"]
+        jobs.append([HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    n = min(len(jobs), int(os.environ.get("MAX_JOBS", "8")))
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(_run, jobs))
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-shared-libasan"] + SAN_FLAGS +
+         ["-o", out + ".tmp"] + objs + ["-lpthread"])
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build_oracle() -> str:
     """Compiles the oracle's plain C search loop (test infrastructure)."""
     src = os.path.join(ROOT, "oracle", "cb2_search.c")

@@ -17,7 +17,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+# QMOE_LIB names another build of the same library (the host-sanitizer build
+# the CPU tests load); by default the one built in this directory.
+LIB_PATH = os.environ.get("QMOE_LIB") or os.path.join(_HERE, "libqmoe.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = 1
