@@ -466,33 +466,59 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   int* ids = reinterpret_cast<int*>(xef + NW);                            // [16] (Route)
   qmoe_route::TopkLds* tk = reinterpret_cast<qmoe_route::TopkLds*>(ids + 16);   // (Route)
 
+  // ---- prologue.  Loads are issued oldest-first in the order they are
+  // needed (the router's logits, codebook and x, then the shared tile, then
+  // a routed tile).  A wave's loads complete in issue order and a wait is a
+  // count of loads still in flight, so these loads are unconditional (lanes
+  // that need none load a copy and ignore it): a load inside a divergent
+  // branch makes the compiler wait for every earlier load at the join.
+  // Route, E <= 256 (a multiple of 4): wave 0 loads all logits, four per
+  // lane, and ranks them alone; otherwise thread tid loads the logit of
+  // expert tid for the workgroup-wide ranking.  Buffer loads: a lane past E
+  // (or a load whose descriptor has no bytes) reads zero, with no branch.
+  const bool wave_rank = Route && a.E <= 256 && (a.E & 3) == 0;
+  float mylogit = 0.f;
+  u32x4 lg4 = {0u, 0u, 0u, 0u};
+  if constexpr (Route) {
+    const float* lrow = a.logits + (size_t)a.t_route * a.E;
+    lg4 = bload16(tile_rsrc(lrow, wave_rank && wave == 0 ? 4 * a.E : 0), 16 * lane);
+    mylogit = __builtin_bit_cast(float, bload4(tile_rsrc(lrow, wave_rank ? 0 : 4 * a.E), 4 * tid));
+  }
   const int k = a.k, n_chunks = a.H / 256, n_rt = a.I / 16, n_rts = a.Is / 16;
-  const int G = gridDim.x, gi = blockIdx.x;
-  const int U_s = 2 * n_rts, U_r = k * n_rt;
-  const int s_lo = (int)((int64_t)gi * U_s / G), s_hi = (int)((int64_t)(gi + 1) * U_s / G);
-  const int r_lo = (int)((int64_t)gi * U_r / G), r_hi = (int)((int64_t)(gi + 1) * U_r / G);
+  // (32-bit products: gi * U_r <= 255 * 16 * 1024)
+  const unsigned G = gridDim.x, gi = blockIdx.x;
+  const unsigned U_s = 2 * n_rts, U_r = k * n_rt;
+  const int s_lo = (int)(gi * U_s / G), s_hi = (int)((gi + 1) * U_s / G);
+  const int r_lo = (int)(gi * U_r / G), r_hi = (int)((gi + 1) * U_r / G);
   const bool active = wave < n_chunks;       // idle waves (H < 1024) load chunk 0 and discard it
   const int chunk = active ? wave : 0;
   const int n = lane & 15, g = lane >> 4, m = lane & 15, qq = lane >> 4;
 
-  // ---- prologue.  Loads are issued oldest-first in the order they are
-  // needed (expert ids, codebook and x, then the shared tile, then a routed
-  // tile), so the table can be built while the weights are still in flight.
-  // A wave's loads complete in issue order and a wait is a count of loads
-  // still in flight, so these loads are unconditional (lanes that need none
-  // load a copy and ignore it): a load inside a divergent branch makes the
-  // compiler wait for every earlier load at the join.
-  // Route: the logit of expert e = tid, through the scalar cache (a vector
-  // load issued beside the weight tiles would wait as long as they do):
-  // wave w reads experts 64w .. 64w+63 and lane l keeps expert 64w + l's.
-  // (read after the vector loads below are issued: a scalar wait counts
-  // every scalar load, and the vector loads' addresses need some)
   int8_t cbv[4];
   {
     const int8_t* cbp = a.codebook + ((tid & 511) >> 1) * 8 + 4 * (tid & 1);
     for (int i = 0; i < 4; ++i) cbv[i] = cbp[i];
   }
   const u32x4 xr = load16(a.x + chunk * 256 + (m & 7) * 32 + qq * 8);    // used by lanes m < 8
+
+  // wave ranking: the route keys of experts 4 lane .. 4 lane + 3 (0 past E).
+  // Every wave waits here until wave 0 has its logits, so that no weight
+  // tile is requested before them: the logits are then among the first
+  // requests the memory system serves, not queued behind the weight stream
+  // (which a compute unit drains in request order).
+  uint64_t key[4] = {0, 0, 0, 0};
+  if constexpr (Route) {
+    const float4v lf = __builtin_bit_cast(float4v, lg4);     // (whole-vector cast)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      key[i] = wave_rank && e < a.E ? qmoe_route::route_key(lf[i], e) : 0;
+    }
+    if (wave_rank) {
+      __builtin_amdgcn_s_waitcnt(0);      // this wave's loads are in (wave 0: the logits)
+      __syncthreads();
+    }
+  }
 
   // shared half tile loads of both matrices (zeros when the workgroup has
   // no shared item)
@@ -511,24 +537,6 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   issue_shared(s_lo, s_lo < s_hi);
 
   if constexpr (Route) {
-    float mylogit = 0.f;
-    typedef const __attribute__((address_space(4))) float* cfp;
-    const int e0 = 64 * wave;
-    if (e0 + 64 <= a.E) {
-      const cfp lp = (cfp)(a.logits + (size_t)a.t_route * a.E + e0);
-      float lv[64];
-#pragma unroll
-      for (int i = 0; i < 64; ++i) lv[i] = lp[i];
-#pragma unroll
-      for (int i = 0; i < 64; ++i) mylogit = lane == i ? lv[i] : mylogit;
-    } else if (e0 < a.E) {
-      const cfp lp = (cfp)(a.logits + (size_t)a.t_route * a.E + e0);
-      for (int i = 0; i < a.E - e0; ++i) {
-        const float v = lp[i];
-        mylogit = lane == i ? v : mylogit;
-      }
-    }
-    auto logit_of = [&](int) { return mylogit; };        // called for e = tid only
     auto out = [&](int j, int e, float w) {
       ids[j] = e;
       if (blockIdx.x == 0) {
@@ -536,9 +544,32 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
         a.topk_w_out[j] = w;
       }
     };
-    if (blockDim.x >= 1024) qmoe_route::rank_topk<1024>(*tk, a.E, k, logit_of, out);
-    else if (blockDim.x >= 512) qmoe_route::rank_topk<512>(*tk, a.E, k, logit_of, out);
-    else qmoe_route::rank_topk<256>(*tk, a.E, k, logit_of, out);
+    if (wave_rank) {
+      // wave 0: k rounds of wave-wide maxima over its registers (no LDS
+      // passes, no barrier until the result)
+      if (wave == 0) {
+        qmoe_route::wave_topk4(key, k, [&](int j, uint64_t mk) {
+          if (lane == 0) {
+            tk->kv[j] = qmoe_route::key_logit(mk);
+            tk->ki[j] = ids[j] = (int)(0xFFFFFFFFu - (uint32_t)mk);
+          }
+        });
+        // w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), the sum in rank order
+        // as in the workgroup ranking (workgroup 0 writes them out)
+        if (blockIdx.x == 0 && lane < k) {
+          const float top = tk->kv[0];
+          float z = 0.f;
+          for (int j = 0; j < k; ++j) z += expf(tk->kv[j] - top);
+          a.topk_idx_out[lane] = tk->ki[lane];
+          a.topk_w_out[lane] = expf(tk->kv[lane] - top) / z;
+        }
+      }
+    } else {
+      auto logit_of = [&](int) { return mylogit; };        // called for e = tid only
+      if (blockDim.x >= 1024) qmoe_route::rank_topk<1024>(*tk, a.E, k, logit_of, out);
+      else if (blockDim.x >= 512) qmoe_route::rank_topk<512>(*tk, a.E, k, logit_of, out);
+      else qmoe_route::rank_topk<256>(*tk, a.E, k, logit_of, out);
+    }
     __syncthreads();
   }
 
@@ -771,10 +802,11 @@ __global__ __launch_bounds__(1024) void dec1_k4_upgate_kernel(DecArgs a) {
   float* red_s = red_r + kRedBatch * 2 * NW * 32;                          // [NW][2][8]
   uint32_t* xef = reinterpret_cast<uint32_t*>(red_s + NW * 2 * 8);         // [NW] largest x exponent field per wave
 
-  const int G = gridDim.x, gi = blockIdx.x;
-  const int U_s = 2 * n_rts, U_r = k * n_rt;
-  const int s_lo = (int)((int64_t)gi * U_s / G), s_hi = (int)((int64_t)(gi + 1) * U_s / G);
-  const int r_lo = (int)((int64_t)gi * U_r / G), r_hi = (int)((int64_t)(gi + 1) * U_r / G);
+  // (32-bit products: gi * U_r <= 255 * 16 * 1024)
+  const unsigned G = gridDim.x, gi = blockIdx.x;
+  const unsigned U_s = 2 * n_rts, U_r = k * n_rt;
+  const int s_lo = (int)(gi * U_s / G), s_hi = (int)((gi + 1) * U_s / G);
+  const int r_lo = (int)(gi * U_r / G), r_hi = (int)((gi + 1) * U_r / G);
   const int n = lane & 15, g = lane >> 4, m = lane & 15, qq = lane >> 4;
 
   // routed units u = item * n_kp + kp, loaded kPrefetch3 ahead

@@ -101,6 +101,46 @@ __device__ __forceinline__ void rank_topk(TopkLds& sm, int E, int k, LogitOf log
 }
 
 
+// Wave-wide maximum of an unsigned value by DPP, with no LDS traffic: row
+// shifts leave each row's maximum in its lane 15, two row broadcasts carry
+// the rows' maxima to lane 63, which every lane reads.  Lanes whose DPP
+// source lies outside the row, and lanes a mask leaves out, take 0, which
+// does not change an unsigned maximum.
+template <int Ctrl, int RowMask, int BankMask>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, Ctrl, RowMask, BankMask, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  v = max(v, dpp_u32<0x111, 0xF, 0xF>(v));   // row_shr:1
+  v = max(v, dpp_u32<0x112, 0xF, 0xF>(v));   // row_shr:2
+  v = max(v, dpp_u32<0x113, 0xF, 0xF>(v));   // row_shr:3
+  v = max(v, dpp_u32<0x114, 0xF, 0xE>(v));   // row_shr:4, lanes 4-15 of each row
+  v = max(v, dpp_u32<0x118, 0xF, 0xC>(v));   // row_shr:8, lanes 8-15 of each row
+  v = max(v, dpp_u32<0x142, 0xA, 0xF>(v));   // row_bcast:15 into rows 1 and 3
+  v = max(v, dpp_u32<0x143, 0xC, 0xF>(v));   // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top k (k <= 16, wave-uniform) of up to 256 route keys held four per lane
+// by one wave: k rounds, each finding the wave's largest key (the logit
+// part first, then the index part among the lanes that hold that logit)
+// and clearing it; out(j, key) receives the j-th largest (wave-uniform).
+// Keys are distinct and real keys exceed the padding key 0.
+template <typename Out>
+__device__ __forceinline__ void wave_topk4(uint64_t (&key)[4], int k, Out out) {
+  for (int j = 0; j < k; ++j) {
+    const uint64_t a = key[0] > key[1] ? key[0] : key[1];
+    const uint64_t b = key[2] > key[3] ? key[2] : key[3];
+    const uint64_t lm = a > b ? a : b;
+    const uint32_t mh = wave_max_u32_dpp((uint32_t)(lm >> 32));
+    const uint32_t ml = wave_max_u32_dpp((uint32_t)(lm >> 32) == mh ? (uint32_t)lm : 0u);
+    const uint64_t mk = ((uint64_t)mh << 32) | ml;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = key[i] == mk ? 0 : key[i];
+    out(j, mk);
+  }
+}
+
 // Wave-wide maximum of a 64-bit key (every lane gets it).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
