@@ -104,6 +104,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-prefill", action="store_true", help="headline: decode parts only")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--stream-slots", type=int, default=0, metavar="N",
+                   help="decode workloads: also time the step with the routed experts streamed from host "
+                        "memory through an HBM cache of N experts (moe_layer_decode_streamed)")
+    p.add_argument("--stream-keep", type=int, default=1, help="cache steps kept from eviction (with --stream-slots)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="also run one elementwise pass (torch.neg) over MIB MiB: a kernel of known "
                         "traffic that the hardware byte counters are scaled by")
@@ -306,6 +310,51 @@ def time_decode(wl, layers, steps, warmup, label):
     del graph
     return {"seconds": t1 - t0, "durs": {kn: ev.seconds(kn) for kn in kernels},
             "idx": idx_all[warmup:].cpu().numpy(), "eager_tps": steps * T / (te1 - te0)}
+
+
+def time_streamed(wl, layer, n_slots, keep, steps, warmup):
+    """Decode steps with the routed experts in page-locked host memory and an
+    HBM cache of n_slots experts: each step is one moe_layer_decode_streamed
+    call (route, choices to the host, plan, copies of the misses on a copy
+    stream, expert FFN over the cache), launched eagerly (the call waits for
+    the routing on the host, so it cannot be captured in a graph)."""
+    import torch
+    from bit_quantized_moe_02_amd import qmoe
+    E, H, k, T = wl.n_experts, wl.hidden, wl.top_k, wl.tokens
+    t = layer.tensors
+    host = []
+    for n in ("up", "gate", "down"):
+        h = torch.empty(t[n].numel(), dtype=torch.uint8, pin_memory=True)
+        h.copy_(t[n])
+        host.append(h)
+    cache = qmoe.ExpertCache(E, H, wl.inter, wl.fmts, *host, n_slots=n_slots, keep=keep, shared_from=layer)
+    n_x = min(steps + warmup, wl.steps)
+    xs = torch.stack([torch.from_numpy(synth.activations_bits(wl, T, step=s).view(np.int16)).view(torch.bfloat16)
+                      for s in range(n_x)]).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(cache.decode_workspace_bytes(T, k), dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    for s in range(warmup):
+        cache.decode(layer.router, layer.bias, xs[s % n_x], T, k, idx, w, y, ws, copy_stream=cs)
+    torch.cuda.synchronize()
+    _, h0, m0 = cache.state()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        cache.decode(layer.router, layer.bias, xs[(warmup + i) % n_x], T, k, idx, w, y, ws, copy_stream=cs)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _, h1, m1 = cache.state()
+    nb = 2 * qmoe.moe_packed_bytes(wl.fmt_up, wl.inter, H) + qmoe.moe_packed_bytes(wl.fmt_down, H, wl.inter)
+    hits, misses = h1 - h0, m1 - m0
+    cache.close()
+    return {"n_slots": n_slots, "keep": keep, "cache_bytes": n_slots * nb, "steps": steps,
+            "tokens_per_s": round(steps * T / (t1 - t0), 1), "ms_per_step": round((t1 - t0) / steps * 1e3, 4),
+            "hit_rate": round(hits / max(1, hits + misses), 4),
+            "copied_bytes_per_token": round(misses * nb / (steps * T), 1),
+            "host_to_device_GBs": round(misses * nb / (t1 - t0) / 1e9, 2),
+            "entry": "moe_layer_decode_streamed", "host_memory": "page-locked", "launch": "eager"}
 
 
 def shared_bytes(wl):
@@ -530,6 +579,10 @@ def main():
                 "quantized_bytes_per_token": float(qb / steps),
                 "frac_hbm_expert_kernels": round(float(qb / qs / 1e9 / HBM_PEAK_GBS), 4),
                 "kernels": q}
+        if args.stream_slots > 0 and not head:
+            log(f"[bench] streaming through {args.stream_slots} cache slots ...")
+            out["expert_streaming"] = time_streamed(wl, layers[0], args.stream_slots, args.stream_keep,
+                                                    min(steps, 200), min(warmup, 20))
         if not args.no_cpu_baseline:
             log("[bench] timing the CPU oracle (decode) ...")
             out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -27,7 +27,8 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX_HOST", shutil.which("g++") or "c++")
 
 HOST_SOURCES = ["host_quant.cpp"]
-DEVICE_SOURCES = ["abi.hip", "k_route.hip", "k_decode.hip", "k_decode1.hip", "k_decodem.hip", "k_prefill.hip", "k_misc.hip"]
+DEVICE_SOURCES = ["abi.hip", "k_route.hip", "k_decode.hip", "k_decode1.hip", "k_decodem.hip", "k_prefill.hip", "k_misc.hip",
+                  "expert_cache.hip"]
 
 HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -87,6 +87,17 @@ int check_weights(const moe_weights* w, Geometry* g, const char* fn) {
   return MOE_OK;
 }
 
+}  // namespace
+
+// The weight checks of the decode and prefill calls, for other translation
+// units (the expert cache validates its host layer with them).
+int qmoe::validate_weights(const moe_weights* w, const char* fn) {
+  Geometry g;
+  return check_weights(w, &g, fn);
+}
+
+namespace {
+
 // Up to this many tokens the decode call runs the single-token kernels once
 // per token; beyond, the batched kernels that read each distinct expert once.
 constexpr int kDecPerTokenMax = 3;

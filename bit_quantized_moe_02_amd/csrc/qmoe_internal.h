@@ -22,6 +22,16 @@ inline int64_t pad256(int64_t k) { return (k + 255) / 256 * 256; }
 // Bytes of one tile of each format; 0 for an unknown format.
 int tile_bytes(int fmt);
 
+}  // namespace qmoe
+
+struct moe_weights;
+
+namespace qmoe {
+
+// Shape, format and pointer checks of a weight set (those of the decode and
+// prefill calls); MOE_OK or the failing code with its message recorded.
+int validate_weights(const moe_weights* w, const char* fn);
+
 // Measurement hook (moe_profile_next_launch): pending (kernel id, start
 // event, stop event) entries of this thread; each is consumed by the next
 // launch of its kernel.

@@ -40,7 +40,9 @@ EXPORTED = [
     "moe_group_tokens", "moe_ffn_workspace_bytes", "moe_expert_ffn_decode",
     "moe_expert_ffn_prefill", "moe_layer_decode_workspace_bytes", "moe_layer_decode",
     "moe_debug_dequant", "moe_profile_next_launch", "moe_last_error", "moe_layer_decode_noalloc",
-    "moe_measure_read",
+    "moe_measure_read", "moe_expert_cache_slot_bytes", "moe_expert_cache_create", "moe_expert_cache_destroy",
+    "moe_expert_cache_weights", "moe_expert_cache_plan", "moe_expert_cache_fetch", "moe_expert_cache_state",
+    "moe_layer_decode_streamed_workspace_bytes", "moe_layer_decode_streamed",
 ]
 MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
@@ -96,6 +98,16 @@ def _load():
         "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int, vp, vp]),
         "moe_measure_read": (ctypes.c_int, [vp, sz, vp, ctypes.c_int, vp]),
         "moe_last_error": (ctypes.c_char_p, []),
+        "moe_expert_cache_slot_bytes": (sz, [ctypes.POINTER(MoeWeights), i32]),
+        "moe_expert_cache_create": (ctypes.c_int, [ctypes.POINTER(MoeWeights), i32, i32, vp, sz,
+                                                   ctypes.POINTER(vp)]),
+        "moe_expert_cache_destroy": (ctypes.c_int, [vp]),
+        "moe_expert_cache_weights": (ctypes.c_int, [vp, ctypes.POINTER(MoeWeights)]),
+        "moe_expert_cache_plan": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, ctypes.POINTER(i32)]),
+        "moe_expert_cache_fetch": (ctypes.c_int, [vp, vp, vp, i32, vp]),
+        "moe_expert_cache_state": (ctypes.c_int, [vp, vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "moe_layer_decode_streamed_workspace_bytes": (sz, [vp, i32, i32]),
+        "moe_layer_decode_streamed": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -310,3 +322,102 @@ class DeviceLayer:
                                  optional=not shared))
         _dev(router, "router", torch.float32, E * H, optional=True)
         _dev(bias, "bias", torch.float32, E, optional=True)
+
+
+# ---------------------------------------------------------------------------
+# Expert streaming: an HBM cache of n_slots experts over a layer whose routed
+# experts stay in host memory.
+
+
+def _host(a, name, nbytes):
+    """Address of a host buffer (numpy array or CPU tensor, page-locked for
+    asynchronous copies) of at least `nbytes` bytes."""
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous host tensor")
+        if a.numel() * a.element_size() < nbytes:
+            raise ValueError(f"{name} holds fewer than {nbytes} bytes")
+        return a.data_ptr()
+    a = np.asarray(a)
+    if not a.flags.c_contiguous or a.nbytes < nbytes:
+        raise ValueError(f"{name} must be a contiguous host array of at least {nbytes} bytes")
+    return a.ctypes.data
+
+
+class ExpertCache:
+    """moe_expert_cache over a layer whose up/gate/down are host buffers
+    (`host_up`, `host_gate`, `host_down`: E packed experts each) and whose
+    shared expert and codebook come from the device layer `shared_from`
+    (a DeviceLayer, or None).  `slot_mem`: uint8 device tensor of at least
+    moe_expert_cache_slot_bytes bytes (allocated here when None)."""
+
+    def __init__(self, n_experts, hidden, inter, fmts, host_up, host_gate, host_down, n_slots, keep=0,
+                 shared_from=None, slot_mem=None):
+        E, H, I = n_experts, hidden, inter
+        nb_up, nb_dn = moe_packed_bytes(fmts[0], I, H), moe_packed_bytes(fmts[2], H, I)
+        self._keep_alive = [host_up, host_gate, host_down, shared_from]
+        sw = shared_from.w if shared_from is not None else None
+        self.host_w = MoeWeights(E, H, I, sw.shared_inter if sw else 0, FMT[fmts[0]], FMT[fmts[1]], FMT[fmts[2]],
+                                 sw.fmt_shared if sw else 0,
+                                 _host(host_up, "host_up", E * nb_up), _host(host_gate, "host_gate", E * nb_up),
+                                 _host(host_down, "host_down", E * nb_dn),
+                                 sw.codebook if sw else None, sw.shared_up if sw else None,
+                                 sw.shared_gate if sw else None, sw.shared_down if sw else None)
+        need = int(lib.moe_expert_cache_slot_bytes(ctypes.byref(self.host_w), n_slots))
+        if need == 0:
+            raise QmoeError(MOE_ERR_INVALID_ARG, "bad layer or n_slots")
+        if slot_mem is None:
+            slot_mem = torch.empty(need, dtype=torch.uint8, device="cuda")
+        self.slot_mem = slot_mem
+        self.ptr = ctypes.c_void_p()
+        _check(lib.moe_expert_cache_create(ctypes.byref(self.host_w), n_slots, keep,
+                                           _dev(slot_mem, "slot_mem", torch.uint8, need), slot_mem.numel(),
+                                           ctypes.byref(self.ptr)))
+        self.n_slots, self.n_experts, self.hidden = n_slots, E, H
+        self.w = MoeWeights()
+        _check(lib.moe_expert_cache_weights(self.ptr, ctypes.byref(self.w)))
+
+    def plan(self, ids):
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+        slots = np.empty(ids.size, np.int32)
+        me = np.empty(max(ids.size, 1), np.int32)
+        ms = np.empty(max(ids.size, 1), np.int32)
+        nm = ctypes.c_int32(0)
+        _check(lib.moe_expert_cache_plan(self.ptr, ids.ctypes.data, ids.size, slots.ctypes.data, me.ctypes.data,
+                                         ms.ctypes.data, ctypes.byref(nm)))
+        return slots, me[:nm.value].copy(), ms[:nm.value].copy()
+
+    def fetch(self, miss_experts, miss_slots, stream=None):
+        me = np.ascontiguousarray(miss_experts, dtype=np.int32)
+        ms = np.ascontiguousarray(miss_slots, dtype=np.int32)
+        _check(lib.moe_expert_cache_fetch(self.ptr, me.ctypes.data, ms.ctypes.data, me.size, _stream(stream)))
+
+    def state(self):
+        eos = np.empty(self.n_slots, np.int32)
+        h, m = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(lib.moe_expert_cache_state(self.ptr, eos.ctypes.data, ctypes.byref(h), ctypes.byref(m)))
+        return eos, h.value, m.value
+
+    def decode_workspace_bytes(self, T, k):
+        return int(lib.moe_layer_decode_streamed_workspace_bytes(self.ptr, T, k))
+
+    def decode(self, w_router, logit_bias, x_bf16, T, k, topk_idx, topk_w, y, ws, stream=None, copy_stream=None):
+        H = self.hidden
+        _check(lib.moe_layer_decode_streamed(
+            self.ptr, _dev(w_router, "w_router", torch.float32, self.n_experts * H),
+            _dev(logit_bias, "logit_bias", torch.float32, self.n_experts, optional=True),
+            _dev(x_bf16, "x_bf16", torch.bfloat16, T * H), T, k,
+            _dev(topk_idx, "topk_idx", torch.int32, T * k), _dev(topk_w, "topk_w", torch.float32, T * k),
+            _dev(y, "y", torch.float32, T * H), *_ws(ws), _stream(stream),
+            None if copy_stream is None else _stream(copy_stream)))
+
+    def close(self):
+        if self.ptr:
+            lib.moe_expert_cache_destroy(self.ptr)
+            self.ptr = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -356,6 +356,89 @@ int moe_profile_next_launch(int kernel_id, void* start_event, void* stop_event);
  * of 16; MOE_ERR_INVALID_ARG otherwise. */
 int moe_measure_read(const void* src, size_t bytes, uint32_t* out, int blocks, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Expert streaming ([osrepos] "SSD Streaming for Large Models": for models
+ * larger than GPU memory the routed MoE experts are loaded from storage as
+ * they are needed, into an expert cache whose size the user sets).  Here the
+ * routed experts stay in host memory and an HBM cache of n_slots experts
+ * holds the ones in use.  A step maps its top-k expert ids to cache slots
+ * (moe_expert_cache_plan), copies the experts it misses into their slots
+ * (moe_expert_cache_fetch), and runs the expert FFN over the cache, which is
+ * a weight set of n_slots experts (moe_expert_cache_weights), with the slot
+ * ids in place of the expert ids.  Routing weights, the shared expert and
+ * the order of every sum are those of the resident layer, so the output is
+ * the same to the bit.
+ *
+ * Replacement (the pages name none; least recently used over steps): a step
+ * needs the distinct ids of its [T, k] choices in order of first appearance
+ * (ids outside [0, n_experts) are skipped); resident ones are hits; each miss
+ * takes the lowest free slot, else evicts the least recently used resident
+ * expert that this step does not need and that was not used in the last
+ * `keep` steps; after the step its experts count as used now, later-appearing
+ * ones more recently.  A cache is used by one thread at a time. */
+typedef struct moe_expert_cache moe_expert_cache;
+
+/* Device bytes of the slot storage for n_slots experts of layer w (three
+ * slot arrays: up, gate, down; each 256-byte aligned); 0 on bad arguments. */
+size_t moe_expert_cache_slot_bytes(const moe_weights* w, int32_t n_slots);
+
+/* Creates a cache.  host_layer: the layer as in moe_weights, except that up,
+ * gate and down point to HOST memory holding all n_experts packed experts
+ * (page-locked memory makes the copies asynchronous; the caller keeps it
+ * alive and unchanged while the cache exists); shared_* and codebook are
+ * device pointers, used as they are.  slot_mem: device memory of at least
+ * moe_expert_cache_slot_bytes(host_layer, n_slots) bytes, 256-byte aligned,
+ * owned by the caller.  1 <= n_slots <= n_experts; keep >= 0 (1 when a step
+ * may be planned while the previous one still runs on the GPU).  Runs on the
+ * host only.  Returns MOE_OK and *out, or MOE_ERR_INVALID_ARG /
+ * MOE_ERR_UNSUPPORTED (as moe_expert_ffn_decode's weight checks). */
+int moe_expert_cache_create(const moe_weights* host_layer, int32_t n_slots, int32_t keep, void* slot_mem,
+                            size_t slot_mem_bytes, moe_expert_cache** out);
+
+/* Frees the cache's host state (and its page-locked staging buffers). */
+int moe_expert_cache_destroy(moe_expert_cache* cache);
+
+/* The cache as a weight set: n_experts = n_slots, up/gate/down = the slot
+ * arrays, the other fields as host_layer. */
+int moe_expert_cache_weights(const moe_expert_cache* cache, moe_weights* out);
+
+/* Host only.  Maps one step's n expert ids (host, e.g. [T, k] top-k choices)
+ * to slots: slots_out[i] (host, n entries) is the slot of ids[i] (-1 for an
+ * id outside [0, n_experts)).  The misses (experts now assigned a slot whose
+ * bytes must be copied) go to miss_experts[0 .. *n_miss) and miss_slots
+ * (host, at least n entries each), in order of first appearance.  If the
+ * step needs more experts than the slots that are free or evictable it
+ * returns MOE_ERR_INVALID_ARG and changes nothing. */
+int moe_expert_cache_plan(moe_expert_cache* cache, const int32_t* ids, int32_t n, int32_t* slots_out,
+                          int32_t* miss_experts, int32_t* miss_slots, int32_t* n_miss);
+
+/* Enqueues on `stream` the host-to-device copies of n_miss experts (up,
+ * gate and down of miss_experts[i] into slot miss_slots[i]; host arrays as
+ * moe_expert_cache_plan wrote them).  The FFN that reads those slots must
+ * run after them (the same stream, or an event). */
+int moe_expert_cache_fetch(moe_expert_cache* cache, const int32_t* miss_experts, const int32_t* miss_slots,
+                           int32_t n_miss, void* stream);
+
+/* Host only: the expert held by each slot (expert_of_slot[n_slots], -1 when
+ * free) and the hit and miss counts since creation. */
+int moe_expert_cache_state(const moe_expert_cache* cache, int32_t* expert_of_slot, int64_t* hits,
+                           int64_t* misses);
+
+/* Workspace bytes of moe_layer_decode_streamed for T tokens, k choices. */
+size_t moe_layer_decode_streamed_workspace_bytes(const moe_expert_cache* cache, int32_t T, int32_t k);
+
+/* One decode step with the routed experts streamed through the cache:
+ * moe_route of x, a copy of the choices to the host (the host waits for
+ * `stream` here, so the call cannot be captured in a graph), plan, the
+ * misses' copies on copy_stream (NULL: on stream; `stream` waits for them),
+ * then moe_expert_ffn_decode over the cache with the slot ids.  topk_idx,
+ * topk_w and y as in moe_layer_decode (expert ids, not slots).  T <= 16.
+ * Errors as the calls it makes, plus MOE_ERR_INVALID_ARG when the step needs
+ * more experts than the cache can hold. */
+int moe_layer_decode_streamed(moe_expert_cache* cache, const float* w_router, const float* logit_bias,
+                              const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx, float* topk_w,
+                              float* y, void* ws, size_t ws_bytes, void* stream, void* copy_stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* moe_last_error(void);
 

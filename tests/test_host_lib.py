@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(q):
     names = _declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 26, names
     lib = ctypes.CDLL(q.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

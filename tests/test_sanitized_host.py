@@ -27,7 +27,8 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-m", "not gpu", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_host_lib.py")],
+                        os.path.join(ROOT, "tests", "test_host_lib.py"),
+                        os.path.join(ROOT, "tests", "test_expert_cache.py")],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=900)
     print(r.stdout[-3000:])
     assert r.returncode == 0, r.stdout[-3000:]
