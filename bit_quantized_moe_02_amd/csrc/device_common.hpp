@@ -205,25 +205,45 @@ __device__ __forceinline__ half8 cb2_group(uint32_t code, const uint8_t* val_lan
   return as_half8(v ^ m);
 }
 
-// CB2 combined table (REP x 64 KB, the kernels place it at LDS offset 0):
-// entry (idx, half, nib) holds the 4 fp16 values T[idx][4*half+i]/4, negated
-// where bit i of nib is set, so a group of 8 weights is two 8-byte reads
-// addressed straight from its 16-bit code (idx | flip << 8): half 0 takes flip
-// bits 0..3, half 1 bits 4..7.  Copy r of the entry sits at byte
-//   ((idx*2 + half)*16 + nib)*8*REP + 8*r,
-// and lane l reads copy l % REP: with REP = 2 even and odd lanes read
-// disjoint halves of the LDS banks, so random codes collide less.
+// CB2 combined table (64 KB, the kernels place it at LDS offset 0): entry
+// (idx, half, nib) holds the 4 fp16 values T[idx][4*half+i]/4, negated where
+// bit i of nib is set, so a group of 8 weights is two 8-byte reads addressed
+// straight from its 16-bit code (idx | flip << 8): half 0 takes flip bits
+// 0..3, half 1 bits 4..7.  The entry sits at byte
+//   half*32768 + idx*128 + nib*8.
+// The sign nibbles are uniform over their 16 values, the indices are not
+// (on Gaussian weights a handful of codebook rows take most codes), so the
+// bank pair a read lands on is chosen by nib and the low bit of idx: 32 bank
+// pairs, a lane's two reads at the same 8-byte position of the 256-byte bank
+// row as far as idx goes.  Both offsets come from the code with a shift, a
+// mask and a bit-field insert each, the idx part shared.
 constexpr int kCb2CombBytes = 256 * 2 * 16 * 8;
 
-template <int REP>
-__device__ __forceinline__ half8 cb2_comb(uint32_t w, int odd, const uint8_t* tab_lane) {
-  static_assert(REP == 1 || REP == 2, "replication 1 or 2");
-  const uint32_t c = odd ? (w >> 16) : (w & 0xFFFFu);
-  const uint32_t base = (c & 0xFFu) << (REP == 1 ? 8 : 9);
-  const uint32_t a0 = base | (REP == 1 ? ((c >> 5) & 0x78u) : ((c >> 4) & 0xF0u));   // nib = flip & 15
-  const uint32_t a1 = base | (REP == 1 ? ((c >> 9) & 0x78u) : ((c >> 8) & 0xF0u));   // nib = flip >> 4
-  const uint2 lo = *reinterpret_cast<const uint2*>(tab_lane + a0);
-  const uint2 hi = *reinterpret_cast<const uint2*>(tab_lane + 128 * REP + a1);
+// (x & mask) | (y & ~mask) in one instruction.
+__device__ __forceinline__ uint32_t bfi_b32(uint32_t mask, uint32_t x, uint32_t y) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(x), "v"(y));
+  return r;
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+
+// LDS offset of a workgroup-memory pointer.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// The 8 fp16 table values of the code in the low (odd = 0) or high (odd = 1)
+// half of the 32-bit word w.  tab is the table's LDS offset and must be a
+// multiple of 32 KB (the entry offset is OR-ed into it): the kernels here
+// place the table at offset 0 of their dynamic LDS and declare no static LDS.
+__device__ __forceinline__ half8 cb2_comb(uint32_t w, int odd, uint32_t tab) {
+  const uint32_t i7 = ((odd ? (w >> 9) : (w << 7)) & 0x7F80u) | tab;        // idx*128
+  const uint32_t lo_a = bfi_b32(0x78u, odd ? (w >> 21) : (w >> 5), i7);    // + (flip & 15)*8
+  const uint32_t hi_a = bfi_b32(0x78u, odd ? (w >> 25) : (w >> 9), i7);    // + (flip >> 4)*8
+  const u32x2 lo = *(lds_u32x2*)(size_t)lo_a;
+  const u32x2 hi = *(lds_u32x2*)(size_t)(hi_a + 32768u);
   return as_half8(u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
@@ -238,12 +258,11 @@ __device__ __forceinline__ uint2 cb2_pair_values(const int8_t* v) {
   return make_uint2(w[0], w[1]);
 }
 
-// Slot i (0 .. 8192*REP - 1, in memory order) of the table, from the pair
-// values val4[pr] (cb2_pair_values).
-template <int REP>
+// Slot i (0 .. 8191, in memory order: i = (half*256 + idx)*16 + nib) of the
+// table, from the pair values val4[pr] (cb2_pair_values), pr = 2*idx + half.
 __device__ __forceinline__ void cb2_comb_put(uint8_t* tab, int i, const uint2* val4) {
-  const int pr = i / (16 * REP), nib = (i / REP) & 15;
-  const uint2 val = val4[pr];
+  const int nib = i & 15;
+  const uint2 val = val4[2 * ((i >> 4) & 255) + (i >> 12)];
   const uint32_t m01 = ((uint32_t)(nib & 1) << 15) | ((uint32_t)(nib & 2) << 30);
   const uint32_t m23 = ((uint32_t)(nib & 4) << 13) | ((uint32_t)(nib & 8) << 28);
   *reinterpret_cast<uint2*>(tab + (size_t)i * 8) = make_uint2(val.x ^ m01, val.y ^ m23);
@@ -259,7 +278,7 @@ __device__ __forceinline__ void cb2_comb_fill(const int8_t* codebook, uint8_t* t
     val4[pr] = cb2_pair_values(v);
   }
   __syncthreads();
-  for (int i = tid; i < 512 * 16; i += nthreads) cb2_comb_put<1>(tab, i, val4);
+  for (int i = tid; i < 512 * 16; i += nthreads) cb2_comb_put(tab, i, val4);
   __syncthreads();
 }
 

@@ -417,7 +417,6 @@ __global__ __launch_bounds__(1024) void dec1_cb2_wide_upgate_kernel(DecArgs a) {
 // MFMA covers two k-blocks of 8 rows with all 64 lanes loading useful bytes.
 
 constexpr int kRedBatch = 8;      // routed row tiles per cross-wave reduction
-constexpr int kTabRep = 1;        // copies of the CB2 table (2 measured no faster)
 constexpr int kPrefetch3 = 3;     // routed row tiles in flight per wave
 
 struct Cb2Pay {
@@ -457,10 +456,10 @@ __device__ __forceinline__ float cb2_scaled(const float4v& c, const uint32_t sc[
 template <bool Route, int SF>
 __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* tab = smem;                                                     // [0, kTabRep x 64 KB)
+  uint8_t* tab = smem;                                                     // [0, 64 KB)
   const int tid = threadIdx.x, lane = tid & 63, NW = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float* red_r = reinterpret_cast<float*>(smem + kTabRep * kCb2CombBytes);  // [kRedBatch][2][NW][32]
+  float* red_r = reinterpret_cast<float*>(smem + kCb2CombBytes);  // [kRedBatch][2][NW][32]
   float* red_s = red_r + kRedBatch * 2 * NW * 32;                         // [NW][2][8]
   uint32_t* xef = reinterpret_cast<uint32_t*>(red_s + NW * 2 * 8);        // [NW] largest x exponent field per wave
   int* ids = reinterpret_cast<int*>(xef + NW);                            // [16] (Route)
@@ -625,7 +624,7 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int kb = 0; kb < 8; ++kb) A[kb] = as_half8(m == kb ? xh : z);
   }
-  for (int i = tid; i < 512 * 16 * kTabRep; i += blockDim.x) cb2_comb_put<kTabRep>(tab, i, val4);
+  for (int i = tid; i < 512 * 16; i += blockDim.x) cb2_comb_put(tab, i, val4);
   __syncthreads();
 
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -657,8 +656,6 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
     __syncthreads();
   }
 
-  const uint8_t* tab_lane = tab + 8 * (lane % kTabRep);
-
   // ---- routed row tiles, kPrefetch3 in flight per wave (the second and
   // third are issued only now: their registers held the shared tile)
   issue(P1, r_lo + 1);
@@ -667,8 +664,8 @@ __global__ __launch_bounds__(1024) void dec1_cb2_upgate_kernel(DecArgs a) {
     float4v cu = zero, cg = zero;
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      cu = mfma_f16(A[kb], cb2_comb<kTabRep>(P.code[0][kb >> 1], kb & 1, tab_lane), cu);
-      cg = mfma_f16(A[kb], cb2_comb<kTabRep>(P.code[1][kb >> 1], kb & 1, tab_lane), cg);
+      cu = mfma_f16(A[kb], cb2_comb(P.code[0][kb >> 1], kb & 1, lds_offset(tab)), cu);
+      cg = mfma_f16(A[kb], cb2_comb(P.code[1][kb >> 1], kb & 1, lds_offset(tab)), cg);
     }
     if (lane < 32 && active) {
       red_r[((b * 2 + 0) * NW + wave) * 32 + lane] = cb2_scaled(cu, P.sc[0], P.ok);
@@ -1358,7 +1355,7 @@ size_t dec1_down_lds(const DecArgs& a, int fmt_dn, int nw) {
 }
 
 size_t dec1_cb2_upgate_lds(int nw, bool route) {
-  return (size_t)kTabRep * kCb2CombBytes + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4 +
+  return (size_t)kCb2CombBytes + (size_t)kRedBatch * 2 * nw * 32 * 4 + (size_t)nw * 2 * 8 * 4 +
          (size_t)nw * 4 + (route ? 16 * 4 + sizeof(qmoe_route::TopkLds) : 0);
 }
 

@@ -46,7 +46,7 @@ __device__ __forceinline__ float4v mfma_bf16(const u32x4& a, const u32x4& b, con
 
 // CB2 group for k-block kb with its fp16 scale folded in.
 __device__ __forceinline__ half8 cb2_scaled_b(const u32x4& codes, const u32x4& scl, int kb, const uint8_t* tab) {
-  const half8 v = cb2_comb<1>(codes[kb >> 1], kb & 1, tab);
+  const half8 v = cb2_comb(codes[kb >> 1], kb & 1, lds_offset(tab));
   const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)((scl[kb >> 1] >> (16 * (kb & 1))) & 0xFFFFu));
   return v * s;
 }
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
     val4[pr] = cb2_pair_values(v);
   }
   __syncthreads();
-  for (int i = tid; i < 512 * 16; i += blockDim.x) cb2_comb_put<1>(tab, i, val4);
+  for (int i = tid; i < 512 * 16; i += blockDim.x) cb2_comb_put(tab, i, val4);
   int xe;                                                                   // exponent of this lane's row m
   {
     uint32_t ef = 0;
