@@ -219,11 +219,17 @@ __device__ __forceinline__ half8 cb2_group(uint32_t code, const uint8_t* val_lan
 // mask and a bit-field insert each, the idx part shared.
 constexpr int kCb2CombBytes = 256 * 2 * 16 * 8;
 
-// (x & mask) | (y & ~mask) in one instruction.
-__device__ __forceinline__ uint32_t bfi_b32(uint32_t mask, uint32_t x, uint32_t y) {
-  uint32_t r;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(x), "v"(y));
-  return r;
+// A constant the compiler sees as an unknown scalar (vector) register value:
+// expressions over it then select three-operand instructions (v_bfi_b32,
+// v_and_or_b32) that take no literal constants, instead of a pair of
+// two-operand ones with literals.  The empty asm emits nothing.
+__device__ __forceinline__ uint32_t sreg(uint32_t c) {
+  asm("" : "+s"(c));
+  return c;
+}
+__device__ __forceinline__ uint32_t vreg(uint32_t c) {
+  asm("" : "+v"(c));
+  return c;
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -240,8 +246,9 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // place the table at offset 0 of their dynamic LDS and declare no static LDS.
 __device__ __forceinline__ half8 cb2_comb(uint32_t w, int odd, uint32_t tab) {
   const uint32_t i7 = ((odd ? (w >> 9) : (w << 7)) & 0x7F80u) | tab;        // idx*128
-  const uint32_t lo_a = bfi_b32(0x78u, odd ? (w >> 21) : (w >> 5), i7);    // + (flip & 15)*8
-  const uint32_t hi_a = bfi_b32(0x78u, odd ? (w >> 25) : (w >> 9), i7);    // + (flip >> 4)*8
+  const uint32_t m = sreg(0x78u);
+  const uint32_t lo_a = ((odd ? (w >> 21) : (w >> 5)) & m) | (i7 & ~m);    // + (flip & 15)*8
+  const uint32_t hi_a = ((odd ? (w >> 25) : (w >> 9)) & m) | (i7 & ~m);    // + (flip >> 4)*8
   const u32x2 lo = *(lds_u32x2*)(size_t)lo_a;
   const u32x2 hi = *(lds_u32x2*)(size_t)(hi_a + 32768u);
   return as_half8(u32x4{lo.x, lo.y, hi.x, hi.y});
@@ -292,21 +299,27 @@ __device__ __forceinline__ int k2_slot_t(int kb, int s) {
   return (kb & 1) ? (s == 0 ? 4 : s - 1) : s;
 }
 
+// (a & mask) | c with the mask in a scalar and c in a vector register, one
+// v_and_or_b32.
+__device__ __forceinline__ uint32_t and_or_b32(uint32_t a, uint32_t mask, uint32_t c) {
+  return (a & sreg(mask)) | c;
+}
+
 // 4 words of magic fp16 pairs for k-block kb: value 1024 + 4^t q.
 __device__ __forceinline__ u32x4 k2_magic(const u32x4& words, int kb) {
-  const uint32_t w = words[kb >> 1];
+  const uint32_t w = words[kb >> 1], m = vreg(0x64006400u);
   u32x4 r;
   if ((kb & 1) == 0) {
-    r.x = (w & 0x00030003u) | 0x64006400u;
-    r.y = (w & 0x000C000Cu) | 0x64006400u;
-    r.z = (w & 0x00300030u) | 0x64006400u;
-    r.w = (w & 0x00C000C0u) | 0x64006400u;
+    r.x = and_or_b32(w, 0x00030003u, m);
+    r.y = and_or_b32(w, 0x000C000Cu, m);
+    r.z = and_or_b32(w, 0x00300030u, m);
+    r.w = and_or_b32(w, 0x00C000C0u, m);
   } else {
     const uint32_t w10 = w >> 10;
-    r.x = (w & 0x03000300u) | 0x64006400u;
-    r.y = (w10 & 0x00030003u) | 0x64006400u;
-    r.z = (w10 & 0x000C000Cu) | 0x64006400u;
-    r.w = (w10 & 0x00300030u) | 0x64006400u;
+    r.x = and_or_b32(w, 0x03000300u, m);
+    r.y = and_or_b32(w10, 0x00030003u, m);
+    r.z = and_or_b32(w10, 0x000C000Cu, m);
+    r.w = and_or_b32(w10, 0x00300030u, m);
   }
   return r;
 }
@@ -315,11 +328,12 @@ __device__ __forceinline__ u32x4 k2_magic(const u32x4& words, int kb) {
 // K4: words of half kb/4 (16 bytes per lane), word kb%4 holds kb; slot s
 // (weights 2s, 2s+1) at bits 4s and 4s+16 (t = 0): value 1024 + q.
 __device__ __forceinline__ u32x4 k4_magic(uint32_t w) {
+  const uint32_t m = vreg(0x64006400u);
   u32x4 r;
-  r.x = (w & 0x000F000Fu) | 0x64006400u;
-  r.y = ((w >> 4) & 0x000F000Fu) | 0x64006400u;
-  r.z = ((w >> 8) & 0x000F000Fu) | 0x64006400u;
-  r.w = ((w >> 12) & 0x000F000Fu) | 0x64006400u;
+  r.x = and_or_b32(w, 0x000F000Fu, m);
+  r.y = and_or_b32(w >> 4, 0x000F000Fu, m);
+  r.z = and_or_b32(w >> 8, 0x000F000Fu, m);
+  r.w = and_or_b32(w >> 12, 0x000F000Fu, m);
   return r;
 }
 
