@@ -297,8 +297,8 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
 
 // Down: a round is up to kDnR consecutive row tiles of one expert (or one
 // shared row tile).  Wave w owns K chunk w; its slice of the staged A rows
-// stays in registers for the whole expert, the next round's weights are in
-// flight while the current one computes, and the waves' partial sums are
+// stays in registers for the whole expert, the next two rounds' weights are
+// in flight while the current one computes, and the waves' partial sums are
 // reduced once per round.
 constexpr int kDnR = 4;
 
@@ -498,15 +498,20 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
     }
     finish(acc, cnt, rt0, n_ck, L->expert[d]);
   };
-  DnRound P0, P1;
-  int d0 = 0, rt0 = 0, d1 = 0, rt1 = 0;
-  int c0 = issue(P0, d0, rt0);
-  while (c0 > 0) {
-    const int c1 = issue(P1, d1, rt1);
+  // three rounds rotate through P0, P1, P2: two in flight while one computes
+  DnRound P0, P1, P2;
+  int d0 = 0, rt0 = 0, d1 = 0, rt1 = 0, d2 = 0, rt2 = 0;
+  int c0 = issue(P0, d0, rt0), c1 = issue(P1, d1, rt1), c2 = 0;
+  while (true) {
+    if (c0 == 0) break;
+    c2 = issue(P2, d2, rt2);
     compute(P0, c0, d0, rt0);
     if (c1 == 0) break;
     c0 = issue(P0, d0, rt0);
     compute(P1, c1, d1, rt1);
+    if (c2 == 0) break;
+    c1 = issue(P1, d1, rt1);
+    compute(P2, c2, d2, rt2);
   }
 }
 
