@@ -60,12 +60,12 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # that feeds the kernel: when the sources differ, the figure no longer
 # describes the kernel and "traffic" is reported as null.
 MEASURED_TRAFFIC = {
-    ("decode_b1", "decode_upgate"): ("791fe505d67063a6", 7.635e+07),
-    ("decode_b1", "decode_down"): ("791fe505d67063a6", 3.936e+07),
-    ("prefill_2048", "prefill_upgate"): ("791fe505d67063a6", 1.837e+09),
-    ("prefill_2048", "prefill_down"): ("791fe505d67063a6", 1.318e+09),
-    ("decode_b16_hot", "decode_upgate"): ("791fe505d67063a6", 4.033e+08),
-    ("decode_b16_hot", "decode_down"): ("791fe505d67063a6", 2.154e+08),
+    ("decode_b1", "decode_upgate"): ("d2cd54f6d188088a", 7.632e+07),
+    ("decode_b1", "decode_down"): ("d2cd54f6d188088a", 3.933e+07),
+    ("prefill_2048", "prefill_upgate"): ("d2cd54f6d188088a", 1.839e+09),
+    ("prefill_2048", "prefill_down"): ("d2cd54f6d188088a", 1.317e+09),
+    ("decode_b16_hot", "decode_upgate"): ("d2cd54f6d188088a", 4.033e+08),
+    ("decode_b16_hot", "decode_down"): ("d2cd54f6d188088a", 2.156e+08),
 }
 KERNEL_SOURCES = ["abi.hip", "device_common.hpp", "route_common.hpp", "decode_common.hpp", "launch_util.h",
                   "k_decode.h", "k_prefill.h", "k_decode1.hip", "k_decodem.hip", "k_decode.hip", "k_prefill.hip",
