@@ -23,7 +23,10 @@
  * ---------------------------------------------------------------------------
  * Conventions for every call
  *   Ownership: the caller owns every buffer.  The library never allocates or
- *     frees device memory and keeps no pointer after a call returns.
+ *     frees device memory and keeps no pointer after a call returns, except
+ *     a moe_expert_cache: it keeps the layer's pointers and the slot memory
+ *     given at creation until moe_expert_cache_destroy, and page-locked host
+ *     staging of its own (freed there).
  *   Pointers: "device" pointers are HIP device memory on the current device;
  *     "host" pointers are ordinary process memory.  Device base pointers must
  *     be 16-byte aligned.
@@ -31,7 +34,8 @@
  *     stream).  Device calls enqueue kernels and return without waiting.
  *   Errors: arguments are checked on the host before anything is enqueued.
  *     On failure a call returns a nonzero MOE_ERR_* code, leaves its outputs
- *     untouched and sets a thread-local message readable with
+ *     untouched (one exception: moe_layer_decode_streamed, below) and sets
+ *     a thread-local message readable with
  *     moe_last_error().  A failed kernel launch returns MOE_ERR_HIP.  No call
  *     aborts, exits or lets a C++ exception escape.
  *   Determinism: every result is a fixed-order computation (no atomics in
@@ -382,7 +386,10 @@ typedef struct moe_expert_cache moe_expert_cache;
  * slot arrays: up, gate, down; each 256-byte aligned); 0 on bad arguments. */
 size_t moe_expert_cache_slot_bytes(const moe_weights* w, int32_t n_slots);
 
-/* Creates a cache.  host_layer: the layer as in moe_weights, except that up,
+/* A cache holds host state that its calls read and change: calls on one
+ * cache must not overlap (one thread at a time).
+ *
+ * Creates a cache.  host_layer: the layer as in moe_weights, except that up,
  * gate and down point to HOST memory holding all n_experts packed experts
  * (page-locked memory makes the copies asynchronous; the caller keeps it
  * alive and unchanged while the cache exists); shared_* and codebook are
@@ -434,7 +441,9 @@ size_t moe_layer_decode_streamed_workspace_bytes(const moe_expert_cache* cache, 
  * then moe_expert_ffn_decode over the cache with the slot ids.  topk_idx,
  * topk_w and y as in moe_layer_decode (expert ids, not slots).  T <= 16.
  * Errors as the calls it makes, plus MOE_ERR_INVALID_ARG when the step needs
- * more experts than the cache can hold. */
+ * more experts than the cache can hold: that is known only after routing,
+ * so on this error topk_idx and topk_w hold the step's choices; y, the cache
+ * and its slots are untouched. */
 int moe_layer_decode_streamed(moe_expert_cache* cache, const float* w_router, const float* logit_bias,
                               const void* x_bf16, int32_t T, int32_t k, int32_t* topk_idx, float* topk_w,
                               float* y, void* ws, size_t ws_bytes, void* stream, void* copy_stream);

@@ -142,3 +142,40 @@ def test_plan_fetch_then_expert_ffn(q):
         torch.cuda.synchronize()
         assert torch.equal(y, ry), s
     cache.close()
+
+
+def test_streamed_decode_refuses_overfull_step(q):
+    """A step that needs more experts than the cache has slots is refused
+    after routing: the choices and weights are written (they decide the
+    refusal), y and the cache are untouched, and the next step that fits
+    runs as the resident layer does."""
+    import torch
+    wl = ODD_CB2
+    layer = device_layer(wl)
+    xb = x_bits(wl, 2, step=5)[0]
+    ri, rw, _ = _resident(q, layer, xb, wl.top_k)
+    distinct = len(set(ri.cpu().numpy().reshape(-1).tolist()))
+    assert distinct > wl.top_k                    # the two tokens share fewer than k experts
+    n_slots = distinct - 1
+    print(f"overfull step: {distinct} experts, {n_slots} slots", flush=True)
+    cache = _cache_for(q, wl, layer, n_slots, 0)
+    T, H = xb.shape
+    idx = torch.full((T, wl.top_k), -9, dtype=torch.int32, device="cuda")
+    w = torch.full((T, wl.top_k), -9.0, dtype=torch.float32, device="cuda")
+    y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(cache.decode_workspace_bytes(T, wl.top_k), dtype=torch.uint8, device="cuda")
+    with pytest.raises(q.QmoeError) as ei:
+        cache.decode(layer.router, layer.bias, _bf16(xb), T, wl.top_k, idx, w, y, ws)
+    torch.cuda.synchronize()
+    assert ei.value.code == q.MOE_ERR_INVALID_ARG
+    assert "slots" in q.moe_last_error()
+    assert torch.equal(idx, ri) and torch.equal(w, rw)
+    assert torch.isnan(y).all()
+    eos, hits, misses = cache.state()
+    assert (eos == -1).all() and hits == 0 and misses == 0
+    # one token needs only k experts
+    x1 = x_bits(wl, 1, step=6)[0]
+    r1 = _resident(q, layer, x1, wl.top_k)
+    s1 = _streamed(q, cache, layer, x1, wl.top_k)
+    assert all(torch.equal(a, b) for a, b in zip(s1, r1))
+    cache.close()
