@@ -38,6 +38,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -56,28 +57,52 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # HBM bytes per launch (read + written) of the dominant kernels, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by the counts the same
 # counters gave for an elementwise pass of known size (FETCH x 2.0, WRITE x 1.0);
-# the summaries are under profiles/.  Each entry holds a digest of every source
-# that feeds the kernel: when the sources differ, the figure no longer
-# describes the kernel and "traffic" is reported as null.
+# the summaries are under profiles/.  Each entry names the source file that
+# defines the kernel and holds a digest of that file, of abi.hip (which sets
+# the launch) and of every header the two reach through their #include lines
+# (kernel_digest): when any of them differs, the figure no longer describes
+# the kernel and "traffic" is reported as null.
 MEASURED_TRAFFIC = {
-    ("decode_b1", "decode_upgate"): ("d2cd54f6d188088a", 7.632e+07),
-    ("decode_b1", "decode_down"): ("d2cd54f6d188088a", 3.933e+07),
-    ("prefill_2048", "prefill_upgate"): ("d2cd54f6d188088a", 1.839e+09),
-    ("prefill_2048", "prefill_down"): ("d2cd54f6d188088a", 1.317e+09),
-    ("decode_b16_hot", "decode_upgate"): ("d2cd54f6d188088a", 4.033e+08),
-    ("decode_b16_hot", "decode_down"): ("d2cd54f6d188088a", 2.156e+08),
+    ("decode_b1", "decode_upgate"): ("k_decode1.hip", "e539f4cd3fe18268", 7.632e+07),
+    ("decode_b1", "decode_down"): ("k_decode1.hip", "e539f4cd3fe18268", 3.933e+07),
+    ("prefill_2048", "prefill_upgate"): ("k_prefill.hip", "1d84c2d801ff45c6", 1.839e+09),
+    ("prefill_2048", "prefill_down"): ("k_prefill.hip", "1d84c2d801ff45c6", 1.317e+09),
+    ("decode_b16_hot", "decode_upgate"): ("k_decodem.hip", "b3cfedbb541f5367", 4.033e+08),
+    ("decode_b16_hot", "decode_down"): ("k_decodem.hip", "b3cfedbb541f5367", 2.156e+08),
 }
-KERNEL_SOURCES = ["abi.hip", "device_common.hpp", "route_common.hpp", "decode_common.hpp", "launch_util.h",
-                  "k_decode.h", "k_prefill.h", "k_decode1.hip", "k_decodem.hip", "k_decode.hip", "k_prefill.hip",
-                  "k_route.hip", "k_misc.hip"]
+CSRC = os.path.join(ROOT, "bit_quantized_moe_02_amd", "csrc")
 
 
-def source_digest():
+def kernel_sources(kernel_file):
+    """kernel_file and abi.hip with every file they include ("..." includes,
+    followed transitively), as paths sorted by their name under the
+    repository root."""
+    seen = set()
+
+    def visit(path):
+        path = os.path.normpath(path)
+        if path in seen:
+            return
+        seen.add(path)
+        with open(path) as f:
+            for line in f:
+                m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+                if m:
+                    visit(os.path.join(os.path.dirname(path), m.group(1)))
+
+    for name in ("abi.hip", kernel_file):
+        visit(os.path.join(CSRC, name))
+    return sorted(seen, key=lambda f: os.path.relpath(f, ROOT))
+
+
+def kernel_digest(kernel_file):
     import hashlib
-    d = os.path.join(ROOT, "bit_quantized_moe_02_amd", "csrc")
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(d, f), "rb").read())
+    for f in kernel_sources(kernel_file):
+        h.update(os.path.relpath(f, ROOT).encode())
+        h.update(b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -477,8 +502,8 @@ def time_prefill(wl, layer, steps, warmup):
 
 def traffic_of(workload, kernel):
     rec = MEASURED_TRAFFIC.get((workload, kernel))
-    if rec is not None and rec[0] == source_digest():
-        return rec[1]
+    if rec is not None and rec[1] == kernel_digest(rec[0]):
+        return rec[2]
     return None
 
 
