@@ -63,12 +63,12 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # (kernel_digest): when any of them differs, the figure no longer describes
 # the kernel and "traffic" is reported as null.
 MEASURED_TRAFFIC = {
-    ("decode_b1", "decode_upgate"): ("k_decode1.hip", "e539f4cd3fe18268", 7.632e+07),
-    ("decode_b1", "decode_down"): ("k_decode1.hip", "e539f4cd3fe18268", 3.933e+07),
-    ("prefill_2048", "prefill_upgate"): ("k_prefill.hip", "1d84c2d801ff45c6", 1.839e+09),
-    ("prefill_2048", "prefill_down"): ("k_prefill.hip", "1d84c2d801ff45c6", 1.317e+09),
-    ("decode_b16_hot", "decode_upgate"): ("k_decodem.hip", "b3cfedbb541f5367", 4.033e+08),
-    ("decode_b16_hot", "decode_down"): ("k_decodem.hip", "b3cfedbb541f5367", 2.156e+08),
+    ("decode_b1", "decode_upgate"): ("k_decode1.hip", "b85a1305e51cfb66", 7.632e+07),
+    ("decode_b1", "decode_down"): ("k_decode1.hip", "b85a1305e51cfb66", 3.933e+07),
+    ("prefill_2048", "prefill_upgate"): ("k_prefill.hip", "f22f902d45e073d1", 1.839e+09),
+    ("prefill_2048", "prefill_down"): ("k_prefill.hip", "f22f902d45e073d1", 1.317e+09),
+    ("decode_b16_hot", "decode_upgate"): ("k_decodem.hip", "f9c13c3ed3d26888", 4.033e+08),
+    ("decode_b16_hot", "decode_down"): ("k_decodem.hip", "f9c13c3ed3d26888", 2.156e+08),
 }
 CSRC = os.path.join(ROOT, "bit_quantized_moe_02_amd", "csrc")
 

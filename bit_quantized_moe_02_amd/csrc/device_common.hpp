@@ -212,11 +212,12 @@ __device__ __forceinline__ half8 cb2_group(uint32_t code, const uint8_t* val_lan
 // 0..3, half 1 bits 4..7.  The entry sits at byte
 //   half*32768 + idx*128 + nib*8.
 // The sign nibbles are uniform over their 16 values, the indices are not
-// (on Gaussian weights a handful of codebook rows take most codes), so the
-// bank pair a read lands on is chosen by nib and the low bit of idx: 32 bank
-// pairs, a lane's two reads at the same 8-byte position of the 256-byte bank
-// row as far as idx goes.  Both offsets come from the code with a shift, a
-// mask and a bit-field insert each, the idx part shared.
+// (on Gaussian weights a handful of codebook rows take most codes).  The bank
+// pair a read lands on follows its offset modulo 256, here
+// (idx & 1)*128 + nib*8: 32 bank pairs, set mostly by the uniform nibble
+// (an order keyed on idx crowds lanes with the common indices into the same
+// banks).  Each offset is a shift, a mask and a bit-field insert of the code,
+// the idx*128 term shared by the two.
 constexpr int kCb2CombBytes = 256 * 2 * 16 * 8;
 
 // A constant the compiler sees as an unknown scalar (vector) register value:
