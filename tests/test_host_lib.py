@@ -255,6 +255,26 @@ def test_profile_hook_arguments(q):
     assert q.lib.moe_profile_next_launch(99, 0x10, 0x20) == 1
     assert q.lib.moe_profile_next_launch(2, None, 0x20) == 1
     assert q.lib.moe_profile_next_launch(-1, None, None) == 0
+    # at most 8 pending requests (host state only: nothing is launched)
+    for _ in range(8):
+        assert q.lib.moe_profile_next_launch(9, 0x10, 0x20) == 0
+    assert q.lib.moe_profile_next_launch(9, 0x10, 0x20) == 1
+    assert "pending" in q.moe_last_error()
+    assert q.lib.moe_profile_next_launch(-1, None, None) == 0
+    assert q.lib.moe_profile_next_launch(9, 0x10, 0x20) == 0
+    assert q.lib.moe_profile_next_launch(-1, None, None) == 0
+
+
+def test_measure_read_argument_errors(q):
+    rd = q.lib.moe_measure_read
+    P = 0x20000
+    assert rd(None, 1024, P, 0, None) == 1
+    assert rd(P, 1024, None, 0, None) == 1
+    assert rd(P + 8, 1024, P, 0, None) == 1            # src alignment
+    assert rd(P, 0, P, 0, None) == 1
+    assert rd(P, 1000, P, 0, None) == 1                # not a multiple of 16
+    assert rd(P, 1024, P, -1, None) == 1
+    assert rd(P, 1024, P, (1 << 20) + 1, None) == 1
 
 
 def test_binding_refuses_host_tensors(q):
