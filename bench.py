@@ -67,8 +67,6 @@ MEASURED_TRAFFIC = {
     ("decode_b1", "decode_down"): ("k_decode1.hip", "b85a1305e51cfb66", 3.933e+07),
     ("prefill_2048", "prefill_upgate"): ("k_prefill.hip", "f22f902d45e073d1", 1.839e+09),
     ("prefill_2048", "prefill_down"): ("k_prefill.hip", "f22f902d45e073d1", 1.317e+09),
-    ("decode_b16_hot", "decode_upgate"): ("k_decodem.hip", "f9c13c3ed3d26888", 4.033e+08),
-    ("decode_b16_hot", "decode_down"): ("k_decodem.hip", "f9c13c3ed3d26888", 2.156e+08),
 }
 CSRC = os.path.join(ROOT, "bit_quantized_moe_02_amd", "csrc")
 

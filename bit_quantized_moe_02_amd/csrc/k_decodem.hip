@@ -39,6 +39,23 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMRB = 2;      // items per cross-wave reduction (up/gate)
 
+// Weight loads of the next items are issued on every path, also past a
+// workgroup's last item, so that the compiler can count the loads issued
+// after each payload and wait for that payload alone (a vector wait is a
+// count of loads still in flight, and a load issued on one path only makes
+// every later use wait for all of them).  A payload past the last item reads
+// through a descriptor of 0 bytes: its loads return zeros and touch no
+// memory.  base must be wave-uniform; word 3 is the untyped-dword setting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wt_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 wt_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t wt_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 __device__ __forceinline__ float4v mfma_bf16(const u32x4& a, const u32x4& b, const float4v& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                   0, 0);
@@ -93,8 +110,7 @@ __device__ __forceinline__ half4 k2_min_b(const u32x4& scm, int g) {
 // Up/gate.  Items: shared row tiles [0, n_rts), then (expert d, row tile rt).
 
 struct UgPayM {
-  u32x4 code[2], scl[2];     // up, gate: the lane's group codes, row n's scales
-  bool ok;
+  u32x4 code[2], scl[2];     // up, gate: the lane's group codes, row n's scales (zeros past the last item)
 };
 
 template <int SF>
@@ -133,15 +149,14 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   const int64_t r_end = hi - n_rts;
   auto issue = [&](UgPayM& P) {
     const bool ok = r_ld < r_end && active;
-    const int e = ok ? L->expert[d_ld] : 0;
+    const int e = ok ? __builtin_amdgcn_readfirstlane(L->expert[d_ld]) : 0;
     const int rt = ok ? rt_ld : 0;
     const size_t t_off = (size_t)e * a.expert_bytes + ((size_t)rt * n_chunks + chunk) * kCb2Tile;
     for (int mat = 0; mat < 2; ++mat) {
-      const uint8_t* tile = (mat ? a.gate : a.up) + t_off;
-      P.code[mat] = load16(tile + 16 * lane);
-      P.scl[mat] = load16(tile + 1024 + 16 * n);
+      const __amdgpu_buffer_rsrc_t rs = wt_rsrc((mat ? a.gate : a.up) + t_off, ok ? kCb2Tile : 0);
+      P.code[mat] = wt_load16(rs, 16 * lane);
+      P.scl[mat] = wt_load16(rs, 1024 + 16 * n);
     }
-    P.ok = ok;
     ++r_ld;
     if (++rt_ld == n_rt) {
       rt_ld = 0;
@@ -149,7 +164,7 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
     }
   };
   UgPayM P0, P1, P2;
-  if (hi > n_rts) issue(P0);
+  issue(P0);
   {
     // each token's exponent: the wave's largest field of row m (the 4 lanes
     // qq of row m), combined over the waves after the next barrier (computed
@@ -198,15 +213,18 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
         u += red[(((b * NW + w) * 2 + 0) * 64 + cl) * 4 + ci];
         g += red[(((b * NW + w) * 2 + 1) * 64 + cl) * 4 + ci];
       }
-      const int64_t item = first + b;
+      // (32-bit item arithmetic: fewer registers in this loop, whose
+      // temporaries would otherwise push the weight loads in flight out of
+      // their registers)
+      const int item = (int)first + b;
       // (BF16 shared items took raw bf16 x; Q8 shared and routed ones x 2^-e)
       const _Float16 h16 = h_of(g, u, (SF == MOE_FMT_BF16 && item < n_rts) ? 0 : xe16[mm], xe16[mm]);
       if (mm < T) {
         if (item < n_rts) {
           a.hs[(size_t)mm * a.Is + item * 16 + nn] = h16;
         } else {
-          const int64_t r = item - n_rts;
-          const int dd = (int)(r / n_rt), rt = (int)(r - (int64_t)dd * n_rt);
+          const int r = item - n_rts;
+          const int dd = r / n_rt, rt = r - dd * n_rt;
           const int e = L->expert[dd];
           if ((L->mask[dd] >> mm) & 1u)
             for (int j = 0; j < k; ++j)
@@ -265,27 +283,28 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
   }
   // routed items, the next two items' weights in flight
   if constexpr (SF != MOE_FMT_Q8) make_a();
+  // (every payload is used on every path, also an idle wave's: a payload
+  // whose loads some path never waits for makes the compiler wait for all
+  // loads in flight before its registers are reused)
   auto compute = [&](const UgPayM& P, int64_t item) {
     float4v cu = zero, cg = zero;
-    if (P.ok) {
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        cu = mfma_f16(A[kb], cb2_scaled_b(P.code[0], P.scl[0], kb, tab), cu);
-        cg = mfma_f16(A[kb], cb2_scaled_b(P.code[1], P.scl[1], kb, tab), cg);
-      }
+    for (int kb = 0; kb < 8; ++kb) {
+      cu = mfma_f16(A[kb], cb2_scaled_b(P.code[0], P.scl[0], kb, tab), cu);
+      cg = mfma_f16(A[kb], cb2_scaled_b(P.code[1], P.scl[1], kb, tab), cg);
     }
     done_item(item, cu, cg);
   };
   const int64_t r0 = max(lo, (int64_t)n_rts);
-  if (r0 + 1 < hi) issue(P1);
+  issue(P1);
   for (int64_t item = r0; item < hi; item += 3) {
-    if (item + 2 < hi) issue(P2);
+    issue(P2);
     compute(P0, item);
     if (item + 1 >= hi) break;
-    if (item + 3 < hi) issue(P0);
+    issue(P0);
     compute(P1, item + 1);
     if (item + 2 >= hi) break;
-    if (item + 4 < hi) issue(P1);
+    issue(P1);
     compute(P2, item + 2);
   }
 }
@@ -301,6 +320,7 @@ __global__ __launch_bounds__(1024) void decm_upgate_kernel(DecArgs a) {
 // in flight while the current one computes, and the waves' partial sums are
 // reduced once per round.
 constexpr int kDnR = 4;
+constexpr int kStageLoads = 8;   // h loads per thread in flight while a workgroup stages an expert's rows
 
 struct DnRound {
   u32x4 q[kDnR], scm[kDnR];
@@ -320,8 +340,11 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
   ExpertList* L = reinterpret_cast<ExpertList*>(red + kDnR * NW * 256);
   int* slot_of = reinterpret_cast<int*>(L + 1);                              // [16] slot of token m (or -1)
   uint32_t* slot_bits = reinterpret_cast<uint32_t*>(slot_of + 16);           // [16] choices j of token m
-  _Float16* xsb = reinterpret_cast<_Float16*>((reinterpret_cast<uintptr_t>(slot_bits + 16) + 15) &
-                                               ~(uintptr_t)15);               // [2][16][kmax/16] hi, lo
+  // (an offset from smem, 16-byte aligned: a pointer rounded through an
+  // integer would lose its LDS address space, and its reads would become
+  // flat loads that wait for every weight load in flight)
+  const size_t xsb_off = ((size_t)(reinterpret_cast<uint8_t*>(slot_bits + 16) - smem) + 15) & ~(size_t)15;
+  _Float16* xsb = reinterpret_cast<_Float16*>(smem + xsb_off);               // [2][16][kmax/16] hi, lo
   const int nsb = kmax / 16;                                                  // sub-blocks per staged row
 
   const int n_rt = a.H / 16, n_rts = a.Is > 0 ? a.H / 16 : 0;
@@ -355,14 +378,26 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
       slot_bits[tid] = bits;
     }
     __syncthreads();
+    // rows of h (or h_s) into hA: eight loads per thread in flight before
+    // one wait (a row or column without data reads past the buffer: zeros)
     const _Float16* src = d < 0 ? a.hs : a.h;
-    const int vp = Kp / 8, vk = K / 8;
-    for (int i = tid; i < 16 * vp; i += blockDim.x) {
-      const int mm = i / vp, c = i - mm * vp;
-      const int sl = slot_of[mm];
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (sl >= 0 && c < vk) v = load16(src + (size_t)sl * K + 8 * c);
-      *reinterpret_cast<u32x4*>(hA + (size_t)mm * kmax + 8 * c) = v;
+    const int vp = Kp / 8, vk = K / 8, total = 16 * vp;
+    const int src_bytes = (d < 0 ? T * a.Is : T * k * a.I) * 2;      // <= 1 MiB here
+    const __amdgpu_buffer_rsrc_t hr = wt_rsrc(src, src_bytes);
+    for (int i0 = 0; i0 < total; i0 += kStageLoads * (int)blockDim.x) {
+      u32x4 v[kStageLoads];
+#pragma unroll
+      for (int u = 0; u < kStageLoads; ++u) {
+        const int i = i0 + u * (int)blockDim.x + tid;
+        const int mm = min(i / vp, 15), c = i - (i / vp) * vp;
+        const int sl = slot_of[mm];
+        v[u] = wt_load16(hr, (i < total && sl >= 0 && c < vk) ? (sl * K + 8 * c) * 2 : src_bytes);
+      }
+#pragma unroll
+      for (int u = 0; u < kStageLoads; ++u) {
+        const int i = i0 + u * (int)blockDim.x + tid;
+        if (i < total) *reinterpret_cast<u32x4*>(hA + (size_t)(i / vp) * kmax + 8 * (i % vp)) = v[u];
+      }
     }
     __syncthreads();
     if (d >= 0) {
@@ -445,21 +480,34 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
   const int chunk = r_active ? wave : 0;
   int64_t r_next = max(lo, (int64_t)n_rts) - n_rts;       // next routed item to load
   const int64_t r_end = hi - n_rts;
-  // issue the loads of the round starting at r_next; returns its size (0: none)
+  // (expert, row tile) of r_next, advanced without a division per round (a
+  // round never crosses an expert)
+  int d_nx = (int)(r_next / n_rt), rt_nx = (int)(r_next - (int64_t)d_nx * n_rt);
+  // issue the loads of the round starting at r_next; returns its size (0:
+  // none left, its loads read nothing).  Offsets within one expert's down
+  // matrix fit 32 bits (H <= 4096, I <= 2048 here).
   auto issue = [&](DnRound& P, int& d, int& rt0) {
-    if (r_next >= r_end) return 0;
-    d = (int)(r_next / n_rt);
-    rt0 = (int)(r_next - (int64_t)d * n_rt);
-    const int cnt = (int)min((int64_t)min(kDnR, n_rt - rt0), r_end - r_next);
-    const uint8_t* base = a.down + (size_t)L->expert[d] * a.expert_bytes_down + (size_t)chunk * kK2Tile;
+    const bool any = r_next < r_end;
+    const int cnt = any ? (int)min((int64_t)min(kDnR, n_rt - rt_nx), r_end - r_next) : 0;
+    const int e = any ? __builtin_amdgcn_readfirstlane(L->expert[d_nx]) : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        wt_rsrc(a.down + (size_t)e * a.expert_bytes_down + (size_t)chunk * kK2Tile,
+                any ? (int)(a.expert_bytes_down - (size_t)chunk * kK2Tile) : 0);
 #pragma unroll
     for (int j = 0; j < kDnR; ++j) {
-      const uint8_t* tile = base + (size_t)(rt0 + min(j, cnt - 1)) * n_ck * kK2Tile;
-      P.q[j] = load16(tile + 16 * lane);
-      P.scm[j] = load16(tile + 1024 + 16 * n);
-      P.dd[j] = *reinterpret_cast<const uint32_t*>(tile + 1280 + 4 * n);
+      const int toff = (rt_nx + min(j, max(cnt - 1, 0))) * n_ck * kK2Tile;
+      P.q[j] = wt_load16(rs, toff + 16 * lane);
+      P.scm[j] = wt_load16(rs, toff + 1024 + 16 * n);
+      P.dd[j] = wt_load4(rs, toff + 1280 + 4 * n);
     }
+    d = d_nx;
+    rt0 = rt_nx;
     r_next += cnt;
+    rt_nx += cnt;
+    if (rt_nx == n_rt) {
+      rt_nx = 0;
+      ++d_nx;
+    }
     return cnt;
   };
   half8 A[8];
@@ -474,27 +522,27 @@ __global__ __launch_bounds__(512) void decm_down_kernel(DecArgs a) {
     float4v acc[kDnR];
 #pragma unroll
     for (int j = 0; j < kDnR; ++j) acc[j] = zero;
-    if (r_active) {
-      // sum_k h w = d sum_k h (q sc) - dmin sum_sb m X_sb: the q sc dots on
-      // the f16 matrix cores (exact operands), the min term as one
-      // 16x16x16 product of the sub-block sums (hi + lo) with the mins
+    // sum_k h w = d sum_k h (q sc) - dmin sum_sb m X_sb: the q sc dots on
+    // the f16 matrix cores (exact operands), the min term as one 16x16x16
+    // product of the sub-block sums (hi + lo) with the mins.  Every tile of
+    // the round is computed on every path, also past cnt and on idle waves
+    // (finish reduces the first cnt tiles of the first n_ck waves): a
+    // payload whose loads some path never waits for makes the compiler wait
+    // for all loads in flight before its registers are reused.
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-        for (int j = 0; j < kDnR; ++j)
-          if (j < cnt) acc[j] = mfma_f16(A[kb], k2_qsc_b(P.q[j], P.scm[j], kb, qq), acc[j]);
-      const int g = lane >> 4;
-      const half4 xh = *reinterpret_cast<const half4*>(xsb + (size_t)m * nsb + 16 * chunk + 4 * g);
-      const half4 xl = *reinterpret_cast<const half4*>(xsb + (size_t)(16 + m) * nsb + 16 * chunk + 4 * g);
+      for (int j = 0; j < kDnR; ++j) acc[j] = mfma_f16(A[kb], k2_qsc_b(P.q[j], P.scm[j], kb, qq), acc[j]);
+    const int g = lane >> 4;
+    const half4 xh = *reinterpret_cast<const half4*>(xsb + (size_t)m * nsb + 16 * chunk + 4 * g);
+    const half4 xl = *reinterpret_cast<const half4*>(xsb + (size_t)(16 + m) * nsb + 16 * chunk + 4 * g);
 #pragma unroll
-      for (int j = 0; j < kDnR; ++j)
-        if (j < cnt) {
-          const half4 mb = k2_min_b(P.scm[j], g);
-          float4v cm = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, mb, zero, 0, 0, 0);
-          cm = __builtin_amdgcn_mfma_f32_16x16x16f16(xl, mb, cm, 0, 0, 0);
-          const float dd = h2f(P.dd[j] & 0xFFFFu), dm = h2f(P.dd[j] >> 16);
-          for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(dd, acc[j][i], -dm * cm[i]);
-        }
+    for (int j = 0; j < kDnR; ++j) {
+      const half4 mb = k2_min_b(P.scm[j], g);
+      float4v cm = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, mb, zero, 0, 0, 0);
+      cm = __builtin_amdgcn_mfma_f32_16x16x16f16(xl, mb, cm, 0, 0, 0);
+      const float dd = h2f(P.dd[j] & 0xFFFFu), dm = h2f(P.dd[j] >> 16);
+      for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(dd, acc[j][i], -dm * cm[i]);
     }
     finish(acc, cnt, rt0, n_ck, L->expert[d]);
   };
