@@ -6,6 +6,7 @@ tokens passes the union of their routed experts."""
 from __future__ import annotations
 
 import functools
+import os
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -24,7 +25,9 @@ def oracle_expert(wl: synth.Workload, e: int):
     return _oracle_expert_cached(wl.name, e)
 
 
-@functools.lru_cache(maxsize=64)
+# (96 experts: a 16-token step's ~70 distinct experts stay cached between its
+# fp64 and mirror sums; ~200 MB each at H = 4096, ~350 MB at H = 7168)
+@functools.lru_cache(maxsize=96)
 def _oracle_expert_cached(name: str, e: int):
     wl = synth.WORKLOADS[name] if name in synth.WORKLOADS else _CUSTOM[name]
     out = []
@@ -33,6 +36,17 @@ def _oracle_expert_cached(name: str, e: int):
         f = O.quantize_matrix(fmt, w, codebook())
         out.append(O.dequantize_matrix(f, codebook(), k=w.shape[1]))
     return tuple(out)
+
+
+def prefetch_oracle_experts(wl: synth.Workload, experts) -> None:
+    """Quantizes the given experts in the oracle on a few threads (the C
+    search and numpy's array operations release the GIL), so that the layer
+    sums that follow find them cached; the values are those oracle_expert
+    computes one by one."""
+    todo = sorted(set(int(e) for e in np.asarray(experts).reshape(-1)) - {-1})
+    if len(todo) > 1:
+        with ThreadPoolExecutor(min(8, len(todo), os.cpu_count() or 1)) as ex:
+            list(ex.map(lambda e: oracle_expert(wl, e), todo))
 
 
 def down_k2_as_prefill(wl: synth.Workload, e: int):
@@ -91,6 +105,7 @@ def _oracle_shared_q8_cached(name: str, fold: bool):
 
 def oracle_layer(wl: synth.Workload, x64: np.ndarray, round_h=None):
     """(y, idx, weights) of the fp64 oracle for tokens x64 [T, H]."""
+    prefetch_oracle_experts(wl, O.route(x64, synth.router_weight(wl), synth.logit_bias(wl), wl.top_k)[0])
     return O.moe_layer(x64, synth.router_weight(wl), synth.logit_bias(wl), wl.top_k,
                        lambda e: oracle_expert(wl, e), shared=oracle_shared(wl), round_h=round_h)
 

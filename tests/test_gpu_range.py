@@ -24,7 +24,7 @@ import oracle as O
 import synth
 
 from layer_fixture import (device_layer, down_k2_as_prefill, near_tie_tokens, oracle_expert, oracle_shared,
-                           register, rel_err)
+                           prefetch_oracle_experts, register, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +129,7 @@ def reference(wl, x64, xb, idx, w, mirror=False, round_w=(), prefill=False):
     choices.  mirror: h rounded to fp16 under the per-token scale 2^-2e and
     the routed weights of round_w as the kernels hold them."""
     T = x64.shape[0]
+    prefetch_oracle_experts(wl, [e for e in np.asarray(idx).reshape(-1) if 0 <= e < wl.n_experts])
     ex = x_exponent(xb)
     sh = oracle_shared(wl)
     y = np.zeros((T, wl.hidden))
